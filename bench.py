@@ -1,0 +1,224 @@
+"""SpMM benchmark: effective TFLOP/s of the BCSR / WCSR path on MI355X.
+
+One step = one SpMM C = A*B through the C-ABI on a device-resident synthetic
+input (the tile kernel plus, for WCSR windows that were split, the merge
+kernel).  Throughput follows the AsyncSparse paper's evaluation (Section IV):
+2 * nnz * N / t with nnz the true nonzero count of A; the stored-entry rate
+(2 * stored * N / t) is reported next to it.
+
+Default workload: the WCSR matrix 16384 x 16384 at about 1% density (window 16,
+column padding 8), N = 128, fp16 in, fp32 out.  ``--config`` selects another
+workload (1: small BCSR, 3: one WCSR population member, 4: BCSR at Qwen2.5-7B
+gate_proj shape, 5: block-sparse P*V).  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective SpMM TFLOP/s (2·nnz·N) BCSR & WCSR; % of MFMA/HBM roofline"
+PEAK_MFMA_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+E_C = {"fp32": 4, "bf16": 2, "fp16": 2}
+
+
+def make_problem(cfg: int, args):
+    import synth
+    if cfg == 1:
+        return synth.config1(), "cfg1: BCSR 256x256 fp16, 16x16 blocks, 26/256 kept, N=64, fp32 out"
+    if cfg == 2:
+        return synth.config2(), ("cfg2: WCSR 16384x16384 fp16, lognormal rows (mean ~200), half "
+                                 "+-256 band / half uniform, window 16, b_col 8, N=128, fp32 out")
+    if cfg == 3:
+        p = synth.config3_matrix(args.member, args.n3)
+        return p, "cfg3 member %d: WCSR m=k=%d, N=%d, %s" % (
+            args.member, p.m, p.N, "banded" if p.meta["banded"] else "uniform")
+    if cfg == 4:
+        p = synth.config4(args.which)
+        return p, "cfg4 %s: BCSR %dx%d bf16, 64x64 blocks, 90%% block sparse, N=65536, bf16 out" % (
+            args.which, p.m, p.k)
+    if cfg == 5:
+        p = synth.config5(width=args.width)
+        return p, "cfg5: BCSR P*V 65536x65536 bf16, 64x64 blocks (diag + 4 vertical + 8 slash%s), " \
+                  "N=128, fp32 out" % ("" if args.width == 1 else ", width %d" % args.width)
+    raise SystemExit("unknown config %d" % cfg)
+
+
+def algorithmic(p, A):
+    """Flops and the method's compulsory HBM bytes for one SpMM."""
+    N = p.N
+    stored = A.stored_entries
+    if p.fmt == "bcsr":
+        nblk = int(A.h_ptr[-1])
+        cols = np.unique(A.h_idx)
+        brows = int(np.minimum(cols.astype(np.int64) * p.b_col + p.b_col, p.k).sum()
+                    - np.minimum(cols.astype(np.int64) * p.b_col, p.k).sum())
+        meta = 4 * nblk + 4 * A.h_ptr.size
+    else:
+        P = A.h_idx.size
+        brows = int(np.unique(A.h_idx[A.h_idx >= 0]).size)
+        meta = 4 * P + 4 * A.h_ptr.size
+    bytes_alg = 2 * stored + meta + 2 * N * brows + E_C[p.c_dtype] * p.m * N
+    return {"flops_true": 2.0 * p.nnz * N, "flops_stored": 2.0 * stored * N,
+            "bytes_alg": float(bytes_alg), "b_rows_referenced": brows}
+
+
+def cpu_baseline(p, budget_s: float):
+    """The oracle, as it stands, on all cores of this process, on the same input.
+    Repeats the full product until ``budget_s`` has passed (at least once)."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    rows = p.coo_rows()
+    oracle.spmm(min(p.m, 64), p.k, p.N, rows[rows < 64], p.col_idx[rows < 64], p.vals[rows < 64],
+                p.B, p.ab_dtype, nthreads=cores)            # untimed warm-up
+    # bounded sample: whole rows from the top of A, at most ~2e9 multiply-adds per pass
+    per_row = np.diff(p.row_ptr.astype(np.int64)) * p.N
+    cum = np.cumsum(per_row)
+    n_rows = int(np.searchsorted(cum, 2e9)) + 1 if cum.size and cum[-1] > 2e9 else p.m
+    n_rows = max(1, min(p.m, n_rows))
+    sel = rows < n_rows
+    r, c, v = rows[sel], p.col_idx[sel], p.vals[sel]
+    reps, t_total = 0, 0.0
+    while reps == 0 or t_total < budget_s:
+        t0 = time.perf_counter()
+        oracle.spmm(n_rows, p.k, p.N, r, c, v, p.B, p.ab_dtype, nthreads=cores)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    t = t_total / reps
+    return {"value": 2.0 * r.size * p.N / t / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "rows 0..%d of the same matrix (%d nonzeros, N=%d), fp64, %d repetition(s), "
+                      "%.2f s each" % (n_rows - 1, r.size, p.N, reps, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--which", default="gate", help="config 4 weight: gate, up or down")
+    ap.add_argument("--member", type=int, default=0, help="config 3 matrix index")
+    ap.add_argument("--n3", type=int, default=128, help="config 3 N")
+    ap.add_argument("--width", type=int, default=1, help="config 5 line width in blocks")
+    ap.add_argument("--split", type=int, default=0, help="WCSR sub-task size (0 = plan's choice)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cold", action="store_true", help="also time with caches flushed")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import window_spmm_amd as ws
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    print("bench: generating config %d" % args.config, file=sys.stderr, flush=True)
+    p, workload = make_problem(args.config, args)
+    print("bench: building format and plan", file=sys.stderr, flush=True)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, device=dev, split_cols=args.split)
+    info = A.plan.info()
+    B = torch.from_numpy(p.B.view(np.int16)).to(dev)
+    C = A.new_c(dev)
+    alg = algorithmic(p, A)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        A.run(B, C, stream)
+    torch.cuda.synchronize()
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        A.run(B, C, stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ev_ms = np.array([s.elapsed_time(e) for s, e in ev])
+    t_kernel = float(ev_ms.mean()) / 1e3
+
+    cold = None
+    if args.cold:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        cms = []
+        for _ in range(min(args.steps, 30)):
+            flush.fill_(1.0)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            A.run(B, C, stream)
+            e.record(stream)
+            torch.cuda.synchronize()
+            cms.append(s.elapsed_time(e))
+        cold = float(np.mean(cms)) / 1e3
+        del flush
+
+    t_roof_mfma = alg["flops_stored"] / (PEAK_MFMA_TFLOPS * 1e12)
+    t_roof_hbm = alg["bytes_alg"] / (PEAK_HBM_GBS * 1e9)
+    if t_roof_hbm >= t_roof_mfma:
+        roof = {"bound": "hbm", "achieved": alg["bytes_alg"] / t_kernel / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": alg["flops_stored"] / t_kernel / 1e12,
+                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel_us"] = t_kernel * 1e6
+    roof["kernels"] = "spmm_tile_kernel" + (" + wcsr_merge_kernel" if info["n_merges"] else "")
+
+    value = alg["flops_true"] / (ms_step / 1e3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.ab_dtype,
+        "data": "synthetic (seeded; no dataset)",
+        "config": {"workload": workload, "format": p.fmt, "m": p.m, "k": p.k, "N": p.N,
+                   "b_row": p.b_row, "b_col": p.b_col, "nnz": p.nnz,
+                   "stored_entries": A.stored_entries, "c_dtype": p.c_dtype,
+                   "plan": {k: info[k] for k in ("tile_cols", "waves_n", "waves_k", "cols_per_lane",
+                                                 "split_cols", "n_tasks", "n_merges")}},
+        "tflops_true_event": alg["flops_true"] / t_kernel / 1e12,
+        "tflops_stored_event": alg["flops_stored"] / t_kernel / 1e12,
+        "roofline_fraction": max(t_roof_mfma, t_roof_hbm) / t_kernel,
+        "t_roof_us": max(t_roof_mfma, t_roof_hbm) * 1e6,
+        "bytes_alg": alg["bytes_alg"],
+        "roofline": roof,
+    }
+    if cold is not None:
+        out["cold_us"] = cold * 1e6
+        out["roofline_fraction_cold"] = max(t_roof_mfma, t_roof_hbm) / cold
+    if not args.no_cpu:
+        print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

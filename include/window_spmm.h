@@ -1,0 +1,183 @@
+/*
+ * window_spmm — sparse x dense matrix multiply (SpMM) for AMD Instinct MI355X
+ * (gfx950), in the two sparse formats of the AsyncSparse paper (Liu, Pu,
+ * Zhang, "AsyncSparse: Accelerating Sparse Matrix-Matrix Multiplication on
+ * Asynchronous GPU Architectures").
+ *
+ *   C[m x N] = A[m x k] * B[k x N]      A sparse, B and C dense, row-major.
+ *
+ * The operation is the one set up in the paper's Section II-C ("Sparse
+ * Formats": A in R^{m x k} sparse, B in R^{k x n} dense, C = A x B).
+ *
+ * Conventions for every function below
+ *  - Every function returns spmm_status_t and never throws or aborts.  On an
+ *    error the outputs are unspecified, no plan is created, and
+ *    spmm_last_error() returns a message for the calling thread.
+ *  - Arguments prefixed h_ are host pointers, d_ are device pointers (memory
+ *    of the current HIP device).  The caller owns every buffer it passes; the
+ *    library never frees them.
+ *  - Index arrays are int32; element offsets inside the library are 64-bit.
+ *  - 16-bit values are passed as raw codes (uint16_t): IEEE binary16 or
+ *    bfloat16 according to the dtype argument.  Builders copy codes bit-exactly.
+ *  - Matrices are row-major; leading dimensions (ldb, ldc) count elements.
+ */
+#ifndef WINDOW_SPMM_H
+#define WINDOW_SPMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPMM_OK = 0,
+    SPMM_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad block/window size */
+    SPMM_ERR_BAD_FORMAT = 2,       /* inconsistent sparse arrays (see each function) */
+    SPMM_ERR_UNSUPPORTED = 3,      /* valid input this build has no kernel for */
+    SPMM_ERR_OUT_OF_MEMORY = 4,    /* host or device allocation failed */
+    SPMM_ERR_HIP = 5               /* HIP runtime / launch error, or no usable gfx950 device */
+} spmm_status_t;
+
+typedef enum { SPMM_FP16 = 0, SPMM_BF16 = 1, SPMM_FP32 = 2 } spmm_dtype_t;
+
+typedef struct spmm_plan_s *spmm_plan_t;
+
+/* Read-only description of a plan (for reports and tests). */
+typedef struct {
+    int32_t format;          /* 0 = BCSR, 1 = WCSR */
+    int32_t tile_rows;       /* rows of C per work-group tile (= b_row) */
+    int32_t tile_cols;       /* columns of C per work-group tile (BN) */
+    int32_t waves_n;         /* waves splitting the tile's columns */
+    int32_t waves_k;         /* waves splitting the reduction (packed columns) */
+    int32_t cols_per_lane;   /* adjacent C columns each lane accumulates (V) */
+    int64_t split_cols;      /* WCSR sub-task size T (0 for BCSR) */
+    int64_t n_tasks;         /* WCSR tasks (= work-groups per column tile) */
+    int64_t n_merges;        /* WCSR windows split into more than one task */
+    int64_t n_slots;         /* WCSR partial-result slots in the workspace */
+    int64_t stored_entries;  /* b_row*b_col*nnz_blocks (BCSR) or b_row*P (WCSR) */
+    size_t workspace_bytes;  /* bytes of d_workspace spmm_*_run needs */
+} spmm_plan_info_t;
+
+/* ---------------------------------------------------------------------------
+ * Host-side format builders (CPU only; no device needed).
+ *
+ * Input A is CSR: h_row_ptr[m+1] (non-decreasing, row_ptr[0] = 0), column
+ * indices sorted strictly increasing inside each row and in [0, k), values as
+ * 16-bit codes.  Every CSR entry is structural, whatever its value.
+ * BAD_FORMAT: row_ptr not monotone / not starting at 0, a column out of range,
+ * unsorted or duplicate columns in a row.  INVALID_ARGUMENT: m < 0, k < 0,
+ * b_row or b_col outside [1, 1024], a required pointer null.
+ * Each builder has a _count call that sizes the outputs, then a fill call.
+ * ------------------------------------------------------------------------- */
+
+/* BCSR (Section II-C "Block Compressed Sparse Row", Fig. 2): A is tiled into
+ * b_row x b_col blocks; every block holding at least one entry is kept.
+ * Outputs: block_row_ptr[ceil(m/b_row)+1], block_col_idx[nnz_blocks] (increasing
+ * inside a block row), blocks[nnz_blocks*b_row*b_col]: each block a dense
+ * row-major b_row x b_col tile, absent entries +0 (code 0x0000). */
+spmm_status_t spmm_csr_to_bcsr_count(int64_t m, int64_t k, const int32_t *h_row_ptr,
+                                     const int32_t *h_col_idx, int32_t b_row, int32_t b_col,
+                                     int64_t *nnz_blocks);
+spmm_status_t spmm_csr_to_bcsr(int64_t m, int64_t k, const int32_t *h_row_ptr,
+                               const int32_t *h_col_idx, const uint16_t *h_values, int32_t b_row,
+                               int32_t b_col, int32_t *h_block_row_ptr, int32_t *h_block_col_idx,
+                               uint16_t *h_blocks);
+
+/* WCSR (Section II-C "Window Compressed Sparse Row", Fig. 2): rows are grouped
+ * into windows of b_row rows; window w keeps the sorted union of its rows'
+ * column indices, padded with -1 up to the next multiple of b_col (W_w columns,
+ * no extra group when the count divides evenly).  Outputs:
+ * window_row_ptr[ceil(m/b_row)+1] (prefix sum of W_w; P = last entry),
+ * window_col_idx[P], values[b_row*P]: window w's b_row x W_w tile is row-major
+ * and starts at element b_row*window_row_ptr[w]; rows past m and pad columns
+ * hold +0.  UNSUPPORTED if P >= 2^31. */
+spmm_status_t spmm_csr_to_wcsr_count(int64_t m, int64_t k, const int32_t *h_row_ptr,
+                                     const int32_t *h_col_idx, int32_t b_row, int32_t b_col,
+                                     int64_t *padded_cols);
+spmm_status_t spmm_csr_to_wcsr(int64_t m, int64_t k, const int32_t *h_row_ptr,
+                               const int32_t *h_col_idx, const uint16_t *h_values, int32_t b_row,
+                               int32_t b_col, int32_t *h_window_row_ptr, int32_t *h_window_col_idx,
+                               uint16_t *h_values_out);
+
+/* Window splitting (Section III-C: long windows become fixed-size sub-tasks and
+ * each work-group takes one task descriptor).  A window of W <= split_cols
+ * packed columns is one task (window, begin, end, -1) writing C directly; a
+ * longer window becomes ceil(W/split_cols) tasks of split_cols columns (the last
+ * one shorter) with consecutive partial slots, plus one merge record
+ * (window, first_slot, n_slots).  Empty windows are one empty task.
+ * tasks[n_tasks*4], merges[n_merges*3]; split_cols must be a positive multiple
+ * of 32.  BAD_FORMAT if window_row_ptr is not monotone. */
+spmm_status_t spmm_wcsr_split_count(int64_t n_windows, const int32_t *h_window_row_ptr,
+                                    int64_t split_cols, int64_t *n_tasks, int64_t *n_merges);
+spmm_status_t spmm_wcsr_split(int64_t n_windows, const int32_t *h_window_row_ptr,
+                              int64_t split_cols, int32_t *h_tasks, int32_t *h_merges);
+
+/* ---------------------------------------------------------------------------
+ * Plans.  A plan validates the format's host row pointer, picks the kernel
+ * configuration for (format, b_row, b_col, N, dtypes), copies the small
+ * metadata it needs to plan-owned device memory (block/window row pointer,
+ * WCSR task and merge tables) and records the device pointers it is given.
+ * Those device arrays (column indices, values) are read by every run and must
+ * stay valid and unchanged until spmm_plan_destroy.  A plan is immutable, so
+ * runs on different streams may overlap if each has its own workspace and C.
+ *
+ * Supported: b_row in {16, 32, 64}; b_col a multiple of 8 (BCSR: at most 256);
+ * ab_dtype FP16 or BF16 (A and B alike); c_dtype FP32, BF16 or FP16; N a
+ * multiple of 8 (m = 0 or N = 0 gives a plan whose runs do nothing); device
+ * index and value arrays 16-byte aligned.  Otherwise UNSUPPORTED.
+ * Accumulation is fp32; 16-bit C is rounded once (nearest-even).
+ * The plan needs a gfx950 device (SPMM_ERR_HIP otherwise).
+ * *workspace_bytes receives the size of the workspace every run needs (0 if
+ * none).
+ * ------------------------------------------------------------------------- */
+
+/* BCSR plan.  h_block_row_ptr[ceil(m/b_row)+1] (host, read during the call);
+ * d_block_col_idx[nnz_blocks], d_blocks[nnz_blocks*b_row*b_col] (device).
+ * Block-column indices are not read on the host; an index whose block lies
+ * outside [0, k) contributes nothing (its B rows read as zero). */
+spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
+                             int32_t b_col, const int32_t *h_block_row_ptr,
+                             const int32_t *d_block_col_idx, const void *d_blocks,
+                             spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype, size_t *workspace_bytes);
+
+/* WCSR plan.  h_window_row_ptr[ceil(m/b_row)+1] (host; every window width a
+ * multiple of b_col, else BAD_FORMAT); d_window_col_idx[P], d_values[b_row*P]
+ * (device).  A column index outside [0, k) (the -1 pads included) reads B as
+ * zero.  split_cols: sub-task size T (positive multiple of 32), or 0 to let the
+ * plan choose. */
+spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
+                             int32_t b_col, const int32_t *h_window_row_ptr,
+                             const int32_t *d_window_col_idx, const void *d_values,
+                             spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype, int64_t split_cols,
+                             size_t *workspace_bytes);
+
+/* Run: C = A * B, enqueued on `stream` (a hipStream_t; NULL = the null stream),
+ * no host synchronisation.  d_B: k x N codes with leading dimension ldb; d_C:
+ * m x N of c_dtype with leading dimension ldc.  Rows < m and columns < N of C
+ * are overwritten (C is never read); rows without entries become 0.
+ * Requirements (else UNSUPPORTED): d_B and d_C 16-byte aligned, ldb >= N and
+ * ldc >= N, both multiples of 8.  d_workspace: at least workspace_bytes of
+ * device memory (16-byte aligned) when workspace_bytes > 0, else ignored.
+ * Device-side faults surface at the caller's next synchronisation. */
+spmm_status_t spmm_bcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void *d_C, int64_t ldc,
+                            void *d_workspace, void *stream);
+spmm_status_t spmm_wcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void *d_C, int64_t ldc,
+                            void *d_workspace, void *stream);
+
+spmm_status_t spmm_plan_info(spmm_plan_t plan, spmm_plan_info_t *info);
+
+/* Frees the plan's host and device memory.  NULL is accepted.  The caller must
+ * make sure no run using the plan is still executing. */
+spmm_status_t spmm_plan_destroy(spmm_plan_t plan);
+
+const char *spmm_status_string(spmm_status_t status);
+/* Message describing the calling thread's last error ("" if none). */
+const char *spmm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WINDOW_SPMM_H */

@@ -35,3 +35,9 @@ def load_fig2():
 @pytest.fixture(scope="session")
 def fig2():
     return load_fig2()
+
+
+@pytest.fixture(scope="session")
+def cfg2():
+    import synth
+    return synth.config2()

@@ -1,0 +1,78 @@
+"""The C-ABI library: it loads, exports every function include/window_spmm.h
+declares, and its argument checks and error codes work without a GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import window_spmm_amd as ws
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"^\s*(?:spmm_status_t|const char \*)\s*(spmm_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 14
+    lib = ctypes.CDLL(ws.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert names == set(ws.EXPORTED)
+
+
+def test_status_strings():
+    for code in range(6):
+        s = ws._lib.spmm_status_string(code).decode()
+        assert s.startswith("SPMM_")
+    assert ws._lib.spmm_status_string(99).decode() == "SPMM_ERR_UNKNOWN"
+
+
+def _code(fn):
+    with pytest.raises(ws.SpmmError) as e:
+        fn()
+    return e.value.code
+
+
+def test_plan_argument_checks_before_device():
+    ptr = np.array([0, 1], np.int32)
+    # b_row not supported by any kernel
+    assert _code(lambda: ws.bcsr_plan(8, 64, 64, 8, 8, ptr, 256, 256)) == ws.ERR_UNSUPPORTED
+    # N not a multiple of 8
+    assert _code(lambda: ws.bcsr_plan(16, 64, 60, 16, 16, ptr, 256, 256)) == ws.ERR_UNSUPPORTED
+    # misaligned device arrays
+    assert _code(lambda: ws.bcsr_plan(16, 64, 64, 16, 16, ptr, 258, 256)) == ws.ERR_UNSUPPORTED
+    # row pointer going backwards
+    assert _code(lambda: ws.bcsr_plan(32, 64, 64, 16, 16, np.array([0, 2, 1], np.int32), 256, 256)) \
+        == ws.ERR_BAD_FORMAT
+    # window width not a multiple of b_col
+    assert _code(lambda: ws.wcsr_plan(16, 64, 64, 16, 8, np.array([0, 12], np.int32), 256, 256)) \
+        == ws.ERR_BAD_FORMAT
+    # split size not a multiple of 32
+    assert _code(lambda: ws.wcsr_plan(16, 64, 64, 16, 8, np.array([0, 16], np.int32), 256, 256,
+                                      split_cols=40)) == ws.ERR_INVALID_ARGUMENT
+
+
+def test_run_with_null_plan_is_an_error():
+    code = ws._lib.spmm_bcsr_run(None, None, 0, None, 0, None, None)
+    assert code == ws.ERR_INVALID_ARGUMENT
+    assert "null plan" in ws._lib.spmm_last_error().decode()
+    assert ws._lib.spmm_plan_destroy(None) == ws.OK
+
+
+def test_plan_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    ptr = np.array([0, 1], np.int32)
+    assert _code(lambda: ws.bcsr_plan(16, 64, 64, 16, 16, ptr, 256, 256)) == ws.ERR_HIP

@@ -1,0 +1,259 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle.
+
+Acceptance: |C_gpu - C_ref| <= 2e-3 * sum_k |a_ik||b_kj| elementwise (fp16/bf16
+inputs, fp32 accumulation); exact equality where the data make every partial
+sum exact (small integers).  C is pre-filled with NaN so an unwritten element
+fails."""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def ws():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import window_spmm_amd
+    return window_spmm_amd
+
+
+def _device_b(p):
+    return torch.from_numpy(p.B.view(np.int16)).cuda()
+
+
+def run_gpu(ws, p, split_cols=0, A=None, repeats=1):
+    _say("gpu case:", p.name, p.fmt, p.m, p.k, p.N, p.b_row, p.b_col, p.ab_dtype, p.c_dtype,
+         "split", split_cols)
+    if A is None:
+        A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                            p.ab_dtype, p.c_dtype, split_cols=split_cols)
+    B = _device_b(p)
+    outs = []
+    for _ in range(repeats):
+        C = A.new_c()
+        C.fill_(float("nan"))
+        A.run(B, C)
+        torch.cuda.synchronize()
+        outs.append(C.float().cpu().numpy().astype(np.float64))
+    return outs if repeats > 1 else outs[0]
+
+
+def check(p, got, rows=None):
+    ref, bound = oracle.spmm(p.m, p.k, p.N, p.coo_rows(), p.col_idx, p.vals, p.B, p.ab_dtype,
+                             out_rows=rows)
+    if rows is not None:
+        got = got[rows]
+    ok, worst, at = oracle.within_tolerance(got, ref, bound, TOL)
+    _say("   worst |dC|/Bound = %.3g at %s" % (worst, at))
+    assert ok, "parity failed at %s: got %r ref %r bound %r" % (
+        at, got[at] if at else None, ref[at] if at else None, bound[at] if at else None)
+    return ref
+
+
+# --------------------------------------------------------------------------
+# small cases spanning several tiles and ragged tails
+# --------------------------------------------------------------------------
+
+BCSR_CASES = [
+    # m, k, N, b_row, b_col, ab, c
+    (200, 150, 72, 64, 64, "bf16", "fp32"),
+    (256, 256, 64, 16, 16, "fp16", "fp32"),
+    (130, 270, 200, 32, 16, "fp16", "bf16"),
+    (64, 64, 8, 64, 64, "bf16", "fp16"),
+    (1000, 700, 136, 64, 32, "bf16", "bf16"),
+    (77, 93, 24, 16, 8, "fp16", "fp32"),
+    (300, 500, 520, 64, 64, "bf16", "bf16"),
+    (96, 4000, 40, 32, 64, "fp16", "fp32"),
+]
+
+
+@pytest.mark.parametrize("case", BCSR_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bcsr_small(ws, case):
+    m, k, N, br, bc, ab, ct = case
+    p = synth.block_problem(m, k, N, br, bc, 0.3, seed=m + k, ab_dtype=ab, c_dtype=ct,
+                            entry_density=0.7)
+    check(p, run_gpu(ws, p))
+
+
+WCSR_CASES = [
+    # m, k, N, b_row, b_col, ab, c, density, split
+    (90, 300, 40, 16, 8, "fp16", "fp32", 0.05, 0),
+    (1000, 800, 128, 16, 8, "fp16", "fp32", 0.03, 64),
+    (517, 1200, 256, 16, 8, "fp16", "fp32", 0.02, 0),
+    (300, 300, 32, 16, 8, "bf16", "bf16", 0.05, 32),
+    (64, 4000, 128, 32, 16, "fp16", "fp32", 0.05, 96),
+    (128, 128, 8, 64, 8, "fp16", "fp16", 0.2, 0),
+    (333, 2000, 264, 16, 8, "bf16", "fp32", 0.02, 128),
+]
+
+
+@pytest.mark.parametrize("case", WCSR_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_wcsr_small(ws, case):
+    m, k, N, br, bc, ab, ct, dens, T = case
+    p = synth.random_problem(m, k, N, dens, seed=m + N, ab_dtype=ab, c_dtype=ct, fmt="wcsr",
+                             b_row=br, b_col=bc, empty_row_frac=0.1)
+    check(p, run_gpu(ws, p, split_cols=T))
+
+
+# --------------------------------------------------------------------------
+# exactness, special matrices, edge cases
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,br,bc", [("bcsr", 64, 64), ("bcsr", 16, 16), ("wcsr", 16, 8)])
+def test_integer_data_is_bit_exact(ws, fmt, br, bc):
+    if fmt == "bcsr":
+        p = synth.block_problem(320, 300, 136, br, bc, 0.25, seed=7, ab_dtype="fp16",
+                                c_dtype="fp32", kind="int", entry_density=0.5)
+    else:
+        p = synth.random_problem(320, 900, 136, 0.04, seed=7, ab_dtype="fp16", c_dtype="fp32",
+                                 kind="int", fmt="wcsr", b_row=br, b_col=bc)
+    got = run_gpu(ws, p, split_cols=64 if fmt == "wcsr" else 0)
+    ref, _ = oracle.spmm(p.m, p.k, p.N, p.coo_rows(), p.col_idx, p.vals, p.B, "fp16")
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("fmt", ["bcsr", "wcsr"])
+def test_identity_gives_b(ws, fmt):
+    n, N = 256, 136
+    ptr = np.arange(n + 1, dtype=np.int32)
+    cols = np.arange(n, dtype=np.int32)
+    vals = synth.bf16_bits(np.ones(n))
+    B = synth.make_dense_b(np.random.default_rng(3), n, N, "bf16")
+    br, bc = (64, 64) if fmt == "bcsr" else (16, 8)
+    p = synth.Problem("identity", n, n, N, ptr, cols, vals, B, "bf16", "fp32", fmt, br, bc)
+    got = run_gpu(ws, p)
+    assert np.array_equal(got, oracle.decode16(B, "bf16").reshape(n, N))
+
+
+@pytest.mark.parametrize("fmt", ["bcsr", "wcsr"])
+def test_empty_matrix_gives_zero(ws, fmt):
+    m, k, N = 100, 70, 24
+    p = synth.Problem("empty", m, k, N, np.zeros(m + 1, np.int32), np.zeros(0, np.int32),
+                      np.zeros(0, np.uint16), synth.make_dense_b(np.random.default_rng(0), k, N, "fp16"),
+                      "fp16", "fp32", fmt, 16, 16 if fmt == "bcsr" else 8)
+    got = run_gpu(ws, p)
+    assert np.array_equal(got, np.zeros((m, N)))
+
+
+def test_single_entry(ws):
+    m, k, N = 64, 64, 128
+    ptr = np.zeros(m + 1, np.int32)
+    ptr[38:] = 1
+    p = synth.Problem("single", m, k, N, ptr, np.array([45], np.int32), synth.fp16_bits(np.array([-1.5])),
+                      synth.make_dense_b(np.random.default_rng(1), k, N, "fp16"), "fp16", "fp32",
+                      "bcsr", 64, 64)
+    got = run_gpu(ws, p)
+    b = oracle.decode16(p.B, "fp16").reshape(k, N)
+    assert np.array_equal(got[37], -1.5 * b[45])
+    assert not np.delete(got, 37, axis=0).any()
+
+
+def test_empty_rows_and_ragged_m_n(ws):
+    # m not a multiple of 64, N with a partial last tile, a third of the rows empty
+    p = synth.random_problem(201, 333, 520, 0.05, seed=12, ab_dtype="bf16", c_dtype="bf16",
+                             fmt="bcsr", b_row=64, b_col=16, empty_row_frac=0.33)
+    got = run_gpu(ws, p)
+    ref = check(p, got)
+    empty = np.diff(p.row_ptr) == 0
+    assert not got[empty].any() and not ref[empty].any()
+
+
+def test_wcsr_split_invariance_and_determinism(ws):
+    p = synth.random_problem(400, 3000, 128, 0.06, seed=5, ab_dtype="fp16", c_dtype="fp32",
+                             kind="int", fmt="wcsr", b_row=16, b_col=8)
+    ref, _ = oracle.spmm(p.m, p.k, p.N, p.coo_rows(), p.col_idx, p.vals, p.B, "fp16")
+    for T in (32, 64, 160, 1 << 20):
+        assert np.array_equal(run_gpu(ws, p, split_cols=T), ref), T
+    q = synth.random_problem(400, 3000, 128, 0.06, seed=6, ab_dtype="fp16", c_dtype="fp32",
+                             fmt="wcsr", b_row=16, b_col=8)
+    outs = run_gpu(ws, q, split_cols=64, repeats=20)
+    assert all(np.array_equal(o, outs[0]) for o in outs[1:])
+    check(q, outs[0])
+
+
+def test_bcsr_deterministic(ws):
+    p = synth.block_problem(640, 640, 256, 64, 64, 0.3, seed=9, ab_dtype="bf16", c_dtype="fp32")
+    outs = run_gpu(ws, p, repeats=10)
+    assert all(np.array_equal(o, outs[0]) for o in outs[1:])
+
+
+def test_ld_larger_than_n(ws):
+    p = synth.block_problem(128, 128, 64, 64, 64, 0.5, seed=3, ab_dtype="bf16", c_dtype="fp32")
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    Bbig = torch.zeros((p.k, 96), dtype=torch.int16, device="cuda")
+    Bbig[:, :64] = _device_b(p)
+    Cbig = torch.full((p.m, 80), float("nan"), device="cuda")
+    A.run(Bbig[:, :64], Cbig[:, :64])
+    torch.cuda.synchronize()
+    got = Cbig.cpu().numpy().astype(np.float64)
+    assert np.isnan(got[:, 64:]).all()
+    check(p, got[:, :64])
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+
+def test_config1_full(ws):
+    p = synth.config1()
+    check(p, run_gpu(ws, p))
+
+
+def test_config2_full(ws, cfg2):
+    check(cfg2, run_gpu(ws, cfg2))
+
+
+@pytest.mark.parametrize("N", [32, 128, 256])
+def test_config3_members(ws, N):
+    specs = synth.config3_specs()
+    small = sorted(range(32), key=lambda j: specs[j][0] * specs[j][1])[:3]
+    for j in small:
+        p = synth.config3_matrix(j, N)
+        check(p, run_gpu(ws, p))
+    # the largest member, on sampled rows
+    j = max(range(32), key=lambda j: specs[j][0] * specs[j][1])
+    if N == 128:
+        p = synth.config3_matrix(j, N)
+        got = run_gpu(ws, p)
+        rows = np.random.default_rng(0).choice(p.m, 512, replace=False)
+        check(p, got, rows=rows)
+
+
+def test_config4_gate_sampled(ws):
+    p = synth.config4("gate")
+    got = run_gpu(ws, p)
+    assert np.isfinite(got).all()
+    rows = np.random.default_rng(1).choice(p.m, 48, replace=False)
+    check(p, got, rows=rows)
+
+
+def test_config4_down_sampled(ws):
+    p = synth.config4("down", N=8192)
+    got = run_gpu(ws, p)
+    rows = np.random.default_rng(2).choice(p.m, 48, replace=False)
+    check(p, got, rows=rows)
+
+
+def test_config5_sampled(ws):
+    p = synth.config5()
+    got = run_gpu(ws, p)
+    assert np.isfinite(got).all()
+    rows = np.random.default_rng(3).choice(p.m, 2048, replace=False)
+    check(p, got, rows=rows)

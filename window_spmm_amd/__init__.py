@@ -1,0 +1,289 @@
+"""Python binding of libwindow_spmm (BCSR / WCSR SpMM for MI355X, gfx950).
+
+Argument marshalling only: every step of the SpMM runs in the native library
+(host-side format builders in C++, the product in HIP kernels).  Device
+buffers are torch tensors (or raw integer device addresses); torch provides
+memory and streams, nothing else.  There is no fallback: if the native
+library is missing, importing this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwindow_spmm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("window_spmm_amd: native library %s is missing; build it with "
+                      "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, ERR_INVALID_ARGUMENT, ERR_BAD_FORMAT, ERR_UNSUPPORTED, ERR_OUT_OF_MEMORY, ERR_HIP = range(6)
+DTYPES = {"fp16": 0, "bf16": 1, "fp32": 2}
+EXPORTED = [
+    "spmm_csr_to_bcsr_count", "spmm_csr_to_bcsr", "spmm_csr_to_wcsr_count", "spmm_csr_to_wcsr",
+    "spmm_wcsr_split_count", "spmm_wcsr_split", "spmm_bcsr_plan", "spmm_wcsr_plan",
+    "spmm_bcsr_run", "spmm_wcsr_run", "spmm_plan_info", "spmm_plan_destroy",
+    "spmm_status_string", "spmm_last_error",
+]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
+                ("tile_cols", ctypes.c_int32), ("waves_n", ctypes.c_int32),
+                ("waves_k", ctypes.c_int32), ("cols_per_lane", ctypes.c_int32),
+                ("split_cols", ctypes.c_int64), ("n_tasks", ctypes.c_int64),
+                ("n_merges", ctypes.c_int64), ("n_slots", ctypes.c_int64),
+                ("stored_entries", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+_P64 = ctypes.POINTER(ctypes.c_int64)
+_Psz = ctypes.POINTER(ctypes.c_size_t)
+_sigs = {
+    "spmm_csr_to_bcsr_count": [_i64, _i64, _vp, _vp, _i32, _i32, _P64],
+    "spmm_csr_to_bcsr": [_i64, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp],
+    "spmm_csr_to_wcsr_count": [_i64, _i64, _vp, _vp, _i32, _i32, _P64],
+    "spmm_csr_to_wcsr": [_i64, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp],
+    "spmm_wcsr_split_count": [_i64, _vp, _i64, _P64, _P64],
+    "spmm_wcsr_split": [_i64, _vp, _i64, _vp, _vp],
+    "spmm_bcsr_plan": [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                       ctypes.c_int, ctypes.c_int, _Psz],
+    "spmm_wcsr_plan": [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                       ctypes.c_int, ctypes.c_int, _i64, _Psz],
+    "spmm_bcsr_run": [_vp, _vp, _i64, _vp, _i64, _vp, _vp],
+    "spmm_wcsr_run": [_vp, _vp, _i64, _vp, _i64, _vp, _vp],
+    "spmm_plan_info": [_vp, ctypes.POINTER(PlanInfo)],
+    "spmm_plan_destroy": [_vp],
+}
+for _name, _args in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = ctypes.c_int
+_lib.spmm_status_string.argtypes = [ctypes.c_int]
+_lib.spmm_status_string.restype = ctypes.c_char_p
+_lib.spmm_last_error.argtypes = []
+_lib.spmm_last_error.restype = ctypes.c_char_p
+
+
+class SpmmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        name = _lib.spmm_status_string(code).decode()
+        msg = _lib.spmm_last_error().decode()
+        super().__init__("%s: %s (%s)" % (where, name, msg))
+
+
+def _check(code: int, where: str):
+    if code != OK:
+        raise SpmmError(code, where)
+
+
+def _host(a, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _hp(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data) if a.size else ctypes.c_void_p(0)
+
+
+def _dp(x) -> ctypes.c_void_p:
+    """Device address of a torch tensor (or an integer address, or None)."""
+    if x is None:
+        return ctypes.c_void_p(0)
+    if isinstance(x, int):
+        return ctypes.c_void_p(x)
+    return ctypes.c_void_p(x.data_ptr())
+
+
+# --------------------------------------------------------------------------
+# host-side builders
+# --------------------------------------------------------------------------
+
+def csr_to_bcsr(m: int, k: int, row_ptr, col_idx, values, b_row: int, b_col: int):
+    """CSR -> BCSR ``(block_row_ptr, block_col_idx, blocks)`` (numpy)."""
+    rp, ci, v = _host(row_ptr, np.int32), _host(col_idx, np.int32), _host(values, np.uint16)
+    n = ctypes.c_int64(0)
+    _check(_lib.spmm_csr_to_bcsr_count(m, k, _hp(rp), _hp(ci), b_row, b_col, ctypes.byref(n)),
+           "spmm_csr_to_bcsr_count")
+    brp = np.empty(-(-m // b_row) + 1, np.int32)
+    bci = np.empty(n.value, np.int32)
+    blk = np.empty(n.value * b_row * b_col, np.uint16)
+    _check(_lib.spmm_csr_to_bcsr(m, k, _hp(rp), _hp(ci), _hp(v), b_row, b_col, _hp(brp), _hp(bci),
+                                 _hp(blk)), "spmm_csr_to_bcsr")
+    return brp, bci, blk
+
+
+def csr_to_wcsr(m: int, k: int, row_ptr, col_idx, values, b_row: int, b_col: int):
+    """CSR -> WCSR ``(window_row_ptr, window_col_idx, values)`` (numpy)."""
+    rp, ci, v = _host(row_ptr, np.int32), _host(col_idx, np.int32), _host(values, np.uint16)
+    P = ctypes.c_int64(0)
+    _check(_lib.spmm_csr_to_wcsr_count(m, k, _hp(rp), _hp(ci), b_row, b_col, ctypes.byref(P)),
+           "spmm_csr_to_wcsr_count")
+    wrp = np.empty(-(-m // b_row) + 1, np.int32)
+    wci = np.empty(P.value, np.int32)
+    wv = np.empty(P.value * b_row, np.uint16)
+    _check(_lib.spmm_csr_to_wcsr(m, k, _hp(rp), _hp(ci), _hp(v), b_row, b_col, _hp(wrp), _hp(wci),
+                                 _hp(wv)), "spmm_csr_to_wcsr")
+    return wrp, wci, wv
+
+
+def wcsr_split(window_row_ptr, split_cols: int):
+    """Task list ``(tasks int32[n,4], merges int32[s,3])`` for sub-task size T."""
+    wrp = _host(window_row_ptr, np.int32)
+    nw = wrp.size - 1
+    nt, nm = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib.spmm_wcsr_split_count(nw, _hp(wrp), split_cols, ctypes.byref(nt), ctypes.byref(nm)),
+           "spmm_wcsr_split_count")
+    tasks = np.empty((nt.value, 4), np.int32)
+    merges = np.empty((nm.value, 3), np.int32)
+    _check(_lib.spmm_wcsr_split(nw, _hp(wrp), split_cols, _hp(tasks), _hp(merges)), "spmm_wcsr_split")
+    return tasks, merges
+
+
+# --------------------------------------------------------------------------
+# plans and runs
+# --------------------------------------------------------------------------
+
+class Plan:
+    """Owns a spmm_plan_t; keeps the device arrays it refers to alive."""
+
+    def __init__(self, handle, fmt: str, workspace_bytes: int, keep=()):
+        self._h = handle
+        self.fmt = fmt
+        self.workspace_bytes = int(workspace_bytes)
+        self._keep = keep
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("plan destroyed")
+        return self._h
+
+    def info(self) -> dict:
+        pi = PlanInfo()
+        _check(_lib.spmm_plan_info(self.handle, ctypes.byref(pi)), "spmm_plan_info")
+        return pi.as_dict()
+
+    def destroy(self):
+        if self._h is not None:
+            _lib.spmm_plan_destroy(self._h)
+            self._h = None
+            self._keep = ()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def bcsr_plan(m, k, N, b_row, b_col, h_block_row_ptr, d_block_col_idx, d_blocks,
+              ab_dtype="bf16", c_dtype="fp32") -> Plan:
+    rp = _host(h_block_row_ptr, np.int32)
+    h = ctypes.c_void_p(0)
+    ws = ctypes.c_size_t(0)
+    _check(_lib.spmm_bcsr_plan(ctypes.byref(h), m, k, N, b_row, b_col, _hp(rp), _dp(d_block_col_idx),
+                               _dp(d_blocks), DTYPES[ab_dtype], DTYPES[c_dtype], ctypes.byref(ws)),
+           "spmm_bcsr_plan")
+    return Plan(h, "bcsr", ws.value, (d_block_col_idx, d_blocks))
+
+
+def wcsr_plan(m, k, N, b_row, b_col, h_window_row_ptr, d_window_col_idx, d_values,
+              ab_dtype="fp16", c_dtype="fp32", split_cols=0) -> Plan:
+    rp = _host(h_window_row_ptr, np.int32)
+    h = ctypes.c_void_p(0)
+    ws = ctypes.c_size_t(0)
+    _check(_lib.spmm_wcsr_plan(ctypes.byref(h), m, k, N, b_row, b_col, _hp(rp), _dp(d_window_col_idx),
+                               _dp(d_values), DTYPES[ab_dtype], DTYPES[c_dtype], int(split_cols),
+                               ctypes.byref(ws)), "spmm_wcsr_plan")
+    return Plan(h, "wcsr", ws.value, (d_window_col_idx, d_values))
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ld(t) -> int:
+    if t is None:
+        return 0
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("B and C must be 2-D with unit column stride")
+    return int(t.stride(0))
+
+
+def bcsr_run(plan: Plan, B, C, workspace=None, stream=None):
+    _check(_lib.spmm_bcsr_run(plan.handle, _dp(B), _ld(B), _dp(C), _ld(C), _dp(workspace),
+                              _stream_handle(stream)), "spmm_bcsr_run")
+
+
+def wcsr_run(plan: Plan, B, C, workspace=None, stream=None):
+    _check(_lib.spmm_wcsr_run(plan.handle, _dp(B), _ld(B), _dp(C), _ld(C), _dp(workspace),
+                              _stream_handle(stream)), "spmm_wcsr_run")
+
+
+# --------------------------------------------------------------------------
+# convenience: a device-resident sparse matrix with its plan
+# --------------------------------------------------------------------------
+
+_TORCH_C = {"fp32": "float32", "bf16": "bfloat16", "fp16": "float16"}
+
+
+class DeviceSparse:
+    """Builds BCSR or WCSR on the host (native builders), copies the arrays to
+    the device, makes the plan and a workspace.  ``run(B, C)`` enqueues C = A*B."""
+
+    def __init__(self, fmt: str, m: int, k: int, N: int, row_ptr, col_idx, values, b_row: int,
+                 b_col: int, ab_dtype: str, c_dtype: str, device="cuda", split_cols: int = 0):
+        import torch
+        self.fmt, self.m, self.k, self.N = fmt, int(m), int(k), int(N)
+        self.ab_dtype, self.c_dtype = ab_dtype, c_dtype
+        self.b_row, self.b_col = int(b_row), int(b_col)
+        if fmt == "bcsr":
+            ptr, idx, vals = csr_to_bcsr(m, k, row_ptr, col_idx, values, b_row, b_col)
+        elif fmt == "wcsr":
+            ptr, idx, vals = csr_to_wcsr(m, k, row_ptr, col_idx, values, b_row, b_col)
+        else:
+            raise ValueError(fmt)
+        self.h_ptr, self.h_idx, self.h_vals = ptr, idx, vals
+        self.d_idx = torch.from_numpy(idx.copy()).to(device) if idx.size else \
+            torch.empty(4, dtype=torch.int32, device=device)
+        self.d_vals = torch.from_numpy(vals.view(np.int16).copy()).to(device) if vals.size else \
+            torch.empty(8, dtype=torch.int16, device=device)
+        if fmt == "bcsr":
+            self.plan = bcsr_plan(m, k, N, b_row, b_col, ptr, self.d_idx, self.d_vals, ab_dtype,
+                                  c_dtype)
+        else:
+            self.plan = wcsr_plan(m, k, N, b_row, b_col, ptr, self.d_idx, self.d_vals, ab_dtype,
+                                  c_dtype, split_cols)
+        nbytes = self.plan.workspace_bytes
+        self.workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32,
+                                     device=device) if nbytes else None
+
+    @property
+    def stored_entries(self) -> int:
+        return int(self.h_vals.size)
+
+    def new_c(self, device="cuda"):
+        import torch
+        return torch.empty((self.m, self.N), dtype=getattr(torch, _TORCH_C[self.c_dtype]),
+                           device=device)
+
+    def run(self, B, C, stream=None):
+        (bcsr_run if self.fmt == "bcsr" else wcsr_run)(self.plan, B, C, self.workspace, stream)
+        return C

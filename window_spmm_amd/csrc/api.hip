@@ -1,0 +1,409 @@
+// C-ABI entry points: plans and runs for BCSR and WCSR SpMM on gfx950.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+struct spmm_plan_s {
+    int fmt;                    // 0 = BCSR, 1 = WCSR
+    int64_t m, k, N;
+    int32_t b_row, b_col;
+    int ab, ct;
+    const uint16_t *A;
+    const int32_t *col_idx;
+    int32_t *d_row_ptr;         // plan-owned copy of the block / window row pointer
+    int32_t *d_tasks;           // WCSR (window, begin, end, slot)
+    int32_t *d_merges;          // WCSR (window, first_slot, n_slots)
+    int64_t n_items;            // block rows (BCSR) or tasks (WCSR)
+    int64_t n_merges, n_slots, split_cols;
+    int64_t stored_entries;
+    int V, waves_n, waves_k;
+    int64_t tile_cols, n_col_tiles;
+    size_t workspace;
+    int device;
+};
+
+namespace wspmm {
+namespace {
+
+int env_int(const char *name, int dflt)
+{
+    const char *s = std::getenv(name);
+    return (s && *s) ? std::atoi(s) : dflt;
+}
+
+spmm_status_t hip_fail(hipError_t e, const char *what)
+{
+    return fail(SPMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The library only runs on gfx950; find out whether the current device is one.
+spmm_status_t current_device(int *dev, int *n_cu)
+{
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count == 0)
+        return fail(SPMM_ERR_HIP, "no HIP device available");
+    if ((e = hipGetDevice(dev)) != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    hipDeviceProp_t prop;
+    if ((e = hipGetDeviceProperties(&prop, *dev)) != hipSuccess)
+        return hip_fail(e, "hipGetDeviceProperties");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(SPMM_ERR_HIP, "device %d is %s, this library is built for gfx950", *dev,
+                    prop.gcnArchName);
+    *n_cu = prop.multiProcessorCount;
+    return SPMM_OK;
+}
+
+spmm_status_t check_common(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
+                           int32_t b_col, const int32_t *h_ptr, const void *d_idx,
+                           const void *d_vals, spmm_dtype_t ab, spmm_dtype_t ct,
+                           size_t *workspace_bytes, bool bcsr)
+{
+    if (!plan || !workspace_bytes || !h_ptr)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "null plan, workspace_bytes or row pointer");
+    if (m < 0 || k < 0 || N < 0)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "negative size");
+    if (b_row < 1 || b_col < 1)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "block/window size must be positive");
+    if (b_row != 16 && b_row != 32 && b_row != 64)
+        return fail(SPMM_ERR_UNSUPPORTED, "b_row = %d: supported 16, 32, 64", b_row);
+    if (b_col % 8 != 0 || (bcsr && b_col > 256))
+        return fail(SPMM_ERR_UNSUPPORTED, "b_col = %d: must be a multiple of 8%s", b_col,
+                    bcsr ? " and at most 256" : "");
+    if (ab != SPMM_FP16 && ab != SPMM_BF16)
+        return fail(SPMM_ERR_UNSUPPORTED, "A/B dtype must be FP16 or BF16");
+    if (ct != SPMM_FP32 && ct != SPMM_BF16 && ct != SPMM_FP16)
+        return fail(SPMM_ERR_UNSUPPORTED, "C dtype must be FP32, BF16 or FP16");
+    if (N % 8 != 0)
+        return fail(SPMM_ERR_UNSUPPORTED, "N = %lld must be a multiple of 8", (long long)N);
+    if (N > (int64_t(1) << 28) || m >= (int64_t(1) << 31) || k >= (int64_t(1) << 31))
+        return fail(SPMM_ERR_UNSUPPORTED, "matrix dimension too large");
+    if (((uintptr_t)d_idx | (uintptr_t)d_vals) & 15)
+        return fail(SPMM_ERR_UNSUPPORTED, "device index/value arrays must be 16-byte aligned");
+    const int64_t nrow = ceil_div(m, b_row);
+    if (h_ptr[0] != 0)
+        return fail(SPMM_ERR_BAD_FORMAT, "row pointer must start at 0");
+    for (int64_t i = 0; i < nrow; ++i) {
+        if (h_ptr[i + 1] < h_ptr[i])
+            return fail(SPMM_ERR_BAD_FORMAT, "row pointer decreases at %lld", (long long)i);
+        if (!bcsr && (h_ptr[i + 1] - h_ptr[i]) % b_col != 0)
+            return fail(SPMM_ERR_BAD_FORMAT, "window %lld width is not a multiple of b_col",
+                        (long long)i);
+    }
+    if (h_ptr[nrow] > 0 && (!d_idx || !d_vals))
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "null device index or value array");
+    return SPMM_OK;
+}
+
+// Tile shape: V columns per lane (wave width 16V), waves along N, waves along k'.
+void choose_config(spmm_plan_s *pl, double mean_kprime, int n_cu)
+{
+    int V = pl->N >= 128 ? 8 : (pl->N >= 64 ? 4 : 2);
+    V = env_int("SPMM_FORCE_V", V);
+    if (V != 2 && V != 4 && V != 8)
+        V = 8;
+    const int64_t wave_cols = 16 * V;
+    const int64_t col_waves = ceil_div(pl->N, wave_cols);
+    int wn = (pl->b_row == 64 && col_waves >= 2) ? 2 : 1;
+    wn = std::max(1, std::min(8, env_int("SPMM_FORCE_WAVES_N", wn)));
+    const int64_t col_tiles = std::max<int64_t>(1, ceil_div(pl->N, wave_cols * wn));
+    // add reduction waves while the grid is small and the items are long
+    const int64_t waves = std::max<int64_t>(1, pl->n_items * col_tiles * wn);
+    int wk = 1;
+    while (wn * wk * 2 <= 8 && waves * wk < int64_t(16) * n_cu && mean_kprime >= 64.0 * wk * 2)
+        wk *= 2;
+    wk = std::max(1, std::min(8 / wn, env_int("SPMM_FORCE_WAVES_K", wk)));
+    pl->V = V;
+    pl->waves_n = wn;
+    pl->waves_k = wk;
+    pl->tile_cols = wave_cols * wn;
+    pl->n_col_tiles = pl->N > 0 ? ceil_div(pl->N, pl->tile_cols) : 0;
+}
+
+template <typename T>
+spmm_status_t upload(const T *h, int64_t n, T **d)
+{
+    *d = nullptr;
+    if (n == 0)
+        return SPMM_OK;
+    hipError_t e = hipMalloc(reinterpret_cast<void **>(d), sizeof(T) * (size_t)n);
+    if (e != hipSuccess) {
+        *d = nullptr;
+        return fail(SPMM_ERR_OUT_OF_MEMORY, "hipMalloc of %lld bytes failed: %s",
+                    (long long)(sizeof(T) * n), hipGetErrorString(e));
+    }
+    e = hipMemcpy(*d, h, sizeof(T) * (size_t)n, hipMemcpyHostToDevice);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipMemcpy");
+    return SPMM_OK;
+}
+
+void free_plan(spmm_plan_s *pl)
+{
+    if (!pl)
+        return;
+    if (pl->d_row_ptr) (void)hipFree(pl->d_row_ptr);
+    if (pl->d_tasks) (void)hipFree(pl->d_tasks);
+    if (pl->d_merges) (void)hipFree(pl->d_merges);
+    delete pl;
+}
+
+spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int64_t ldc,
+                        void *ws)
+{
+    if (!pl)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "null plan");
+    if (pl->m == 0 || pl->N == 0)
+        return SPMM_OK;
+    if (!C || (pl->k > 0 && !B))
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "null B or C");
+    if (((uintptr_t)B | (uintptr_t)C) & 15)
+        return fail(SPMM_ERR_UNSUPPORTED, "B and C must be 16-byte aligned");
+    if (ldb < pl->N || ldc < pl->N || ldb % 8 || ldc % 8)
+        return fail(SPMM_ERR_UNSUPPORTED, "ldb/ldc must be >= N and multiples of 8");
+    if (pl->workspace > 0 && (!ws || ((uintptr_t)ws & 15)))
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "plan needs a 16-byte aligned workspace of %zu bytes",
+                    pl->workspace);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != pl->device)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "plan was made on device %d, current is %d",
+                    pl->device, dev);
+    return SPMM_OK;
+}
+
+spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void *C, int64_t ldc,
+                       void *ws, void *stream)
+{
+    spmm_status_t s = check_run(pl, B, ldb, C, ldc, ws);
+    if (s != SPMM_OK)
+        return s;
+    if (pl->fmt != fmt)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "plan format does not match the run call");
+    if (pl->m == 0 || pl->N == 0 || pl->n_items == 0)
+        return ok();
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    TileParams p;
+    p.A = pl->A;
+    p.col_idx = pl->col_idx;
+    p.row_ptr = pl->d_row_ptr;
+    p.tasks = reinterpret_cast<const int4 *>(pl->d_tasks);
+    p.B = reinterpret_cast<const uint16_t *>(B);
+    p.ldb = ldb;
+    p.C = C;
+    p.ldc = ldc;
+    p.partial = reinterpret_cast<float *>(ws);
+    p.m = pl->m;
+    p.k = pl->k;
+    p.N = pl->N;
+    p.b_col = pl->b_col;
+    p.tile_cols = (int32_t)pl->tile_cols;
+    p.waves_n = pl->waves_n;
+    p.waves_k = pl->waves_k;
+    p.c_dtype = pl->ct;
+    hipError_t e = launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, pl->n_items, pl->n_col_tiles, st);
+    if (e != hipSuccess)
+        return hip_fail(e, "tile kernel launch");
+    if (pl->n_merges > 0) {
+        MergeParams mp;
+        mp.merges = reinterpret_cast<const int3 *>(pl->d_merges);
+        mp.partial = reinterpret_cast<const float *>(ws);
+        mp.C = C;
+        mp.ldc = ldc;
+        mp.m = pl->m;
+        mp.N = pl->N;
+        mp.R = pl->b_row;
+        mp.c_dtype = pl->ct;
+        e = launch_merge(mp, pl->n_merges, st);
+        if (e != hipSuccess)
+            return hip_fail(e, "merge kernel launch");
+    }
+    return ok();
+}
+
+}  // namespace
+}  // namespace wspmm
+
+using namespace wspmm;
+
+extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
+                                        int32_t b_row, int32_t b_col,
+                                        const int32_t *h_block_row_ptr,
+                                        const int32_t *d_block_col_idx, const void *d_blocks,
+                                        spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
+                                        size_t *workspace_bytes)
+{
+    spmm_status_t s = check_common(plan, m, k, N, b_row, b_col, h_block_row_ptr, d_block_col_idx,
+                                   d_blocks, ab_dtype, c_dtype, workspace_bytes, true);
+    if (s != SPMM_OK)
+        return s;
+    *plan = nullptr;
+    int dev = 0, n_cu = 0;
+    if ((s = current_device(&dev, &n_cu)) != SPMM_OK)
+        return s;
+    spmm_plan_s *pl = new (std::nothrow) spmm_plan_s();
+    if (!pl)
+        return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+    const int64_t nbr = ceil_div(m, b_row);
+    pl->fmt = 0;
+    pl->m = m; pl->k = k; pl->N = N;
+    pl->b_row = b_row; pl->b_col = b_col;
+    pl->ab = ab_dtype; pl->ct = c_dtype;
+    pl->A = reinterpret_cast<const uint16_t *>(d_blocks);
+    pl->col_idx = d_block_col_idx;
+    pl->n_items = nbr;
+    pl->stored_entries = (int64_t)h_block_row_ptr[nbr] * b_row * b_col;
+    pl->device = dev;
+    if (pl->n_items > 0x7fffffff) {
+        free_plan(pl);
+        return fail(SPMM_ERR_UNSUPPORTED, "too many block rows");
+    }
+    if ((s = upload(h_block_row_ptr, nbr + 1, &pl->d_row_ptr)) != SPMM_OK) {
+        free_plan(pl);
+        return s;
+    }
+    const double mean_k = nbr > 0 ? (double)h_block_row_ptr[nbr] * b_col / (double)nbr : 0.0;
+    choose_config(pl, mean_k, n_cu);
+    if (pl->n_col_tiles > 65535) {
+        free_plan(pl);
+        return fail(SPMM_ERR_UNSUPPORTED, "N too large for the column-tile grid");
+    }
+    pl->workspace = 0;
+    *workspace_bytes = 0;
+    *plan = pl;
+    return ok();
+}
+
+extern "C" spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
+                                        int32_t b_row, int32_t b_col,
+                                        const int32_t *h_window_row_ptr,
+                                        const int32_t *d_window_col_idx, const void *d_values,
+                                        spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
+                                        int64_t split_cols, size_t *workspace_bytes)
+{
+    spmm_status_t s = check_common(plan, m, k, N, b_row, b_col, h_window_row_ptr,
+                                   d_window_col_idx, d_values, ab_dtype, c_dtype, workspace_bytes,
+                                   false);
+    if (s != SPMM_OK)
+        return s;
+    *plan = nullptr;
+    if (split_cols < 0 || split_cols % 32 != 0)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "split_cols must be 0 or a positive multiple of 32");
+    int dev = 0, n_cu = 0;
+    if ((s = current_device(&dev, &n_cu)) != SPMM_OK)
+        return s;
+    const int64_t nw = ceil_div(m, b_row);
+    const int64_t P = h_window_row_ptr[nw];
+    if (split_cols == 0) {
+        // Sub-task size: twice the mean window width (at least 512 packed columns),
+        // so only windows well above the mean are cut.
+        const int64_t mean = nw > 0 ? ceil_div(P, nw) : 0;
+        split_cols = std::max<int64_t>(512, ceil_div(2 * mean, 32) * 32);
+        split_cols = env_int("SPMM_FORCE_SPLIT", (int)std::min<int64_t>(split_cols, 1 << 30));
+        if (split_cols <= 0 || split_cols % 32)
+            split_cols = 512;
+    }
+    spmm_plan_s *pl = new (std::nothrow) spmm_plan_s();
+    if (!pl)
+        return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+    pl->fmt = 1;
+    pl->m = m; pl->k = k; pl->N = N;
+    pl->b_row = b_row; pl->b_col = b_col;
+    pl->ab = ab_dtype; pl->ct = c_dtype;
+    pl->A = reinterpret_cast<const uint16_t *>(d_values);
+    pl->col_idx = d_window_col_idx;
+    pl->split_cols = split_cols;
+    pl->stored_entries = P * b_row;
+    pl->device = dev;
+    int64_t nt = 0, nm = 0;
+    if ((s = spmm_wcsr_split_count(nw, h_window_row_ptr, split_cols, &nt, &nm)) != SPMM_OK) {
+        free_plan(pl);
+        return s;
+    }
+    if (nt > 0x7fffffff) {
+        free_plan(pl);
+        return fail(SPMM_ERR_UNSUPPORTED, "too many tasks");
+    }
+    try {
+        std::vector<int32_t> tasks((size_t)nt * 4), merges((size_t)std::max<int64_t>(nm, 1) * 3);
+        if ((s = spmm_wcsr_split(nw, h_window_row_ptr, split_cols, tasks.data(), merges.data())) !=
+            SPMM_OK) {
+            free_plan(pl);
+            return s;
+        }
+        int64_t slots = 0;
+        for (int64_t i = 0; i < nm; ++i)
+            slots += merges[3 * i + 2];
+        pl->n_items = nt;
+        pl->n_merges = nm;
+        pl->n_slots = slots;
+        if ((s = upload(h_window_row_ptr, nw + 1, &pl->d_row_ptr)) != SPMM_OK ||
+            (s = upload(tasks.data(), nt * 4, &pl->d_tasks)) != SPMM_OK ||
+            (s = upload(merges.data(), nm * 3, &pl->d_merges)) != SPMM_OK) {
+            free_plan(pl);
+            return s;
+        }
+    } catch (const std::bad_alloc &) {
+        free_plan(pl);
+        return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+    const double mean_task = nt > 0 ? (double)P / (double)nt : 0.0;
+    choose_config(pl, mean_task, n_cu);
+    if (pl->n_col_tiles > 65535) {
+        free_plan(pl);
+        return fail(SPMM_ERR_UNSUPPORTED, "N too large for the column-tile grid");
+    }
+    if (nm > 0 && ceil_div((int64_t)b_row * (N / 8), 256) > 65535) {
+        free_plan(pl);
+        return fail(SPMM_ERR_UNSUPPORTED, "N too large for the merge grid");
+    }
+    pl->workspace = (size_t)pl->n_slots * (size_t)b_row * (size_t)N * sizeof(float);
+    *workspace_bytes = pl->workspace;
+    *plan = pl;
+    return ok();
+}
+
+extern "C" spmm_status_t spmm_bcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void *d_C,
+                                       int64_t ldc, void *d_workspace, void *stream)
+{
+    return run_plan(plan, 0, d_B, ldb, d_C, ldc, d_workspace, stream);
+}
+
+extern "C" spmm_status_t spmm_wcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void *d_C,
+                                       int64_t ldc, void *d_workspace, void *stream)
+{
+    return run_plan(plan, 1, d_B, ldb, d_C, ldc, d_workspace, stream);
+}
+
+extern "C" spmm_status_t spmm_plan_info(spmm_plan_t pl, spmm_plan_info_t *info)
+{
+    if (!pl || !info)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "null plan or info");
+    std::memset(info, 0, sizeof(*info));
+    info->format = pl->fmt;
+    info->tile_rows = pl->b_row;
+    info->tile_cols = (int32_t)pl->tile_cols;
+    info->waves_n = pl->waves_n;
+    info->waves_k = pl->waves_k;
+    info->cols_per_lane = pl->V;
+    info->split_cols = pl->fmt == 1 ? pl->split_cols : 0;
+    info->n_tasks = pl->fmt == 1 ? pl->n_items : 0;
+    info->n_merges = pl->n_merges;
+    info->n_slots = pl->n_slots;
+    info->stored_entries = pl->stored_entries;
+    info->workspace_bytes = pl->workspace;
+    return ok();
+}
+
+extern "C" spmm_status_t spmm_plan_destroy(spmm_plan_t plan)
+{
+    free_plan(plan);
+    return ok();
+}

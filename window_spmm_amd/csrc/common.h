@@ -1,0 +1,19 @@
+// Internal helpers shared by the host-side sources of the library.
+#pragma once
+
+#include "window_spmm.h"
+
+namespace wspmm {
+
+// Records a thread-local message for spmm_last_error() and returns `s`.
+spmm_status_t fail(spmm_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clears the thread-local message and returns SPMM_OK.
+spmm_status_t ok();
+
+// Checks a CSR pattern: row_ptr[0] = 0, non-decreasing, columns in [0, k) and
+// strictly increasing inside every row.
+spmm_status_t validate_csr(int64_t m, int64_t k, const int32_t *row_ptr, const int32_t *col_idx);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace wspmm

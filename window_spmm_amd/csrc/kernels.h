@@ -1,0 +1,48 @@
+// Launch interface between the host API (api.hip) and the device kernels
+// (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "window_spmm.h"
+
+namespace wspmm {
+
+// Arguments of the tile kernel (one work-group per (work item, column tile)).
+struct TileParams {
+    const uint16_t *A;        // BCSR blocks or WCSR window tiles (16-bit codes)
+    const int32_t *col_idx;   // block_col_idx or window_col_idx
+    const int32_t *row_ptr;   // block_row_ptr or window_row_ptr (plan-owned copy)
+    const int4 *tasks;        // WCSR task table (window, begin, end, slot); null for BCSR
+    const uint16_t *B;        // k x N codes, leading dimension ldb
+    int64_t ldb;
+    void *C;                  // m x N of c_dtype, leading dimension ldc
+    int64_t ldc;
+    float *partial;           // WCSR partial tiles [slot][R][N] (fp32)
+    int64_t m, k, N;
+    int32_t b_col;
+    int32_t tile_cols;        // columns per work-group tile = waves_n * 16 * V
+    int32_t waves_n;          // waves splitting the columns
+    int32_t waves_k;          // waves splitting the packed-column reduction
+    int32_t c_dtype;          // spmm_dtype_t of C
+};
+
+struct MergeParams {
+    const int3 *merges;       // (window, first_slot, n_slots)
+    const float *partial;     // [slot][R][N]
+    void *C;
+    int64_t ldc, m, N;
+    int32_t R;
+    int32_t c_dtype;
+};
+
+// LDS bytes the tile kernel needs for its cross-wave reduction.
+size_t tile_lds_bytes(int R, int V, int waves_n, int waves_k);
+
+// fmt: 0 = BCSR (grid.x = block rows), 1 = WCSR (grid.x = tasks).
+hipError_t launch_tiles(int fmt, int R, int V, int ab_dtype, const TileParams &p, int64_t n_items,
+                        int64_t n_col_tiles, hipStream_t stream);
+hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stream);
+
+}  // namespace wspmm
