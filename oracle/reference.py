@@ -97,16 +97,29 @@ def spmm(m: int, k: int, N: int, rows: np.ndarray, cols: np.ndarray, a_codes: np
     return C, Bd
 
 
-def within_tolerance(c_test: np.ndarray, c_ref: np.ndarray, bound: np.ndarray, tol: float = 2e-3):
-    """Acceptance test ``|C_test - C_ref| <= tol * Bound`` elementwise, C_test finite.
+# unit roundoff of the 16-bit output formats (8 and 11 significant bits)
+OUTPUT_ROUNDOFF = {"fp32": 0.0, "bf16": 2.0 ** -8, "fp16": 2.0 ** -11}
 
+
+def within_tolerance(c_test: np.ndarray, c_ref: np.ndarray, bound: np.ndarray, tol: float = 2e-3,
+                     out_dtype: str = "fp32"):
+    """Acceptance test, elementwise, C_test finite:
+
+        |C_test - C_ref| <= tol * Bound + u_out * |C_ref|
+
+    ``tol * Bound`` (Bound = sum |a||b|) covers fp16/bf16 products accumulated in
+    fp32; ``u_out`` is the unit roundoff of a 16-bit C (one final rounding to
+    nearest, 2^-8 for bfloat16, 2^-11 for binary16, 0 for an fp32 C).
     Where Bound is 0 (no product contributes) C_test must be exactly 0.
-    Returns ``(ok, worst_ratio, worst_index)`` with ratio = |diff| / Bound."""
+    Returns ``(ok, worst_ratio, worst_index)``; ratio = tol * |diff| / allowed, which is
+    |diff| / Bound for an fp32 C (acceptance: ratio <= tol)."""
     c_test = np.asarray(c_test, dtype=np.float64)
     diff = np.abs(c_test - c_ref)
-    bad = ~np.isfinite(c_test) | (diff > tol * bound)
+    allowed = tol * bound + OUTPUT_ROUNDOFF[out_dtype] * np.abs(c_ref)
+    bad = ~np.isfinite(c_test) | (diff > allowed)
     with np.errstate(divide="ignore", invalid="ignore"):
-        ratio = np.where(bound > 0, diff / np.where(bound > 0, bound, 1.0), np.where(diff > 0, np.inf, 0.0))
+        ratio = np.where(allowed > 0, diff / np.where(allowed > 0, allowed, 1.0) * tol,
+                         np.where(diff > 0, np.inf, 0.0))
     ratio = np.where(np.isfinite(c_test), ratio, np.inf)
     if ratio.size == 0:
         return True, 0.0, None

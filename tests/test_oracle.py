@@ -191,6 +191,21 @@ def test_tolerance_accepts_and_rejects():
     assert not ok
 
 
+def test_tolerance_allows_one_rounding_of_a_16bit_output():
+    # 16.6877 lies between the bfloat16 neighbours 16.625 and 16.75 (spacing 2^-3);
+    # nearest-even gives 16.75, 0.0623 away, more than 2e-3 * Bound when |C| ~ Bound
+    ref = np.array([16.687693680636585])
+    bound = np.array([23.422590876929462])
+    got = oracle.decode16(synth.bf16_bits(ref), "bf16")
+    assert got[0] == 16.75
+    assert not oracle.within_tolerance(got, ref, bound)[0]
+    assert oracle.within_tolerance(got, ref, bound, out_dtype="bf16")[0]
+    # the allowance is one rounding, not two
+    assert not oracle.within_tolerance(np.array([16.875]), ref, bound, out_dtype="bf16")[0]
+    got16 = oracle.decode16(synth.fp16_bits(ref), "fp16")
+    assert oracle.within_tolerance(got16, ref, bound * 1e-3, out_dtype="fp16")[0]
+
+
 # --------------------------------------------------------------------------
 # formats: Fig. 2, special cases, round trips, a loop re-implementation
 # --------------------------------------------------------------------------

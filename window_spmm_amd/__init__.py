@@ -22,6 +22,11 @@ if not os.path.exists(LIB_PATH):
     raise ImportError("window_spmm_amd: native library %s is missing; build it with "
                       "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
 
+# torch is loaded first on purpose: it ships its own HIP runtime with the same
+# soname as the system one, and the library must bind to the runtime that owns
+# the tensors and streams it is handed.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARGUMENT, ERR_BAD_FORMAT, ERR_UNSUPPORTED, ERR_OUT_OF_MEMORY, ERR_HIP = range(6)
