@@ -115,6 +115,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cold", action="store_true", help="also time with caches flushed")
+    ap.add_argument("--no-pad", action="store_true", help="B and C with leading dimension N")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -134,8 +135,10 @@ def main():
     A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
                         p.ab_dtype, p.c_dtype, device=dev, split_cols=args.split)
     info = A.plan.info()
-    B = torch.from_numpy(p.B.view(np.int16)).to(dev)
-    C = A.new_c(dev)
+    # B and C rows padded to the library's recommended leading dimension (only
+    # differs from N when the row pitch is a multiple of 4 KiB, e.g. N = 65536)
+    B = A.device_b(p.B, dev, padded=not args.no_pad)
+    C = A.new_c(dev, padded=not args.no_pad)
     alg = algorithmic(p, A)
 
     stream = torch.cuda.current_stream()
@@ -183,7 +186,8 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
     roof["kernel_us"] = t_kernel * 1e6
-    roof["kernels"] = "spmm_tile_kernel" + (" + wcsr_merge_kernel" if info["n_merges"] else "")
+    roof["kernels"] = ("bcsr64_lds_kernel" if info["kernel"] == 1 else "spmm_tile_kernel") + \
+        (" + wcsr_merge_kernel" if info["n_merges"] else "")
 
     value = alg["flops_true"] / (ms_step / 1e3) / 1e12
     out = {
@@ -200,9 +204,10 @@ def main():
         "dtype": p.ab_dtype,
         "data": "synthetic (seeded; no dataset)",
         "config": {"workload": workload, "format": p.fmt, "m": p.m, "k": p.k, "N": p.N,
+                   "ldb": int(B.stride(0)), "ldc": int(C.stride(0)),
                    "b_row": p.b_row, "b_col": p.b_col, "nnz": p.nnz,
                    "stored_entries": A.stored_entries, "c_dtype": p.c_dtype,
-                   "plan": {k: info[k] for k in ("tile_cols", "waves_n", "waves_k", "cols_per_lane",
+                   "plan": {k: info[k] for k in ("kernel", "tile_cols", "waves_n", "waves_k", "cols_per_lane",
                                                  "split_cols", "n_tasks", "n_merges")}},
         "tflops_true_event": alg["flops_true"] / t_kernel / 1e12,
         "tflops_stored_event": alg["flops_stored"] / t_kernel / 1e12,

@@ -52,6 +52,8 @@ typedef struct {
     int32_t waves_n;         /* waves splitting the tile's columns */
     int32_t waves_k;         /* waves splitting the reduction (packed columns) */
     int32_t cols_per_lane;   /* adjacent C columns each lane accumulates (V) */
+    int32_t kernel;          /* 0: generic tile kernel; 1: BCSR 64x64 kernel with LDS-shared A */
+    int32_t reserved;
     int64_t split_cols;      /* WCSR sub-task size T (0 for BCSR) */
     int64_t n_tasks;         /* WCSR tasks (= work-groups per column tile) */
     int64_t n_merges;        /* WCSR windows split into more than one task */
@@ -123,7 +125,8 @@ spmm_status_t spmm_wcsr_split(int64_t n_windows, const int32_t *h_window_row_ptr
  * stay valid and unchanged until spmm_plan_destroy.  A plan is immutable, so
  * runs on different streams may overlap if each has its own workspace and C.
  *
- * Supported: b_row in {16, 32, 64}; b_col a multiple of 8 (BCSR: at most 256);
+ * Supported: b_row in {16, 32, 64}; b_col a multiple of 8 (BCSR: a power of two
+ * in [8, 256]);
  * ab_dtype FP16 or BF16 (A and B alike); c_dtype FP32, BF16 or FP16; N a
  * multiple of 8 (m = 0 or N = 0 gives a plan whose runs do nothing); device
  * index and value arrays 16-byte aligned.  Otherwise UNSUPPORTED.
@@ -158,7 +161,8 @@ spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
  * m x N of c_dtype with leading dimension ldc.  Rows < m and columns < N of C
  * are overwritten (C is never read); rows without entries become 0.
  * Requirements (else UNSUPPORTED): d_B and d_C 16-byte aligned, ldb >= N and
- * ldc >= N, both multiples of 8.  d_workspace: at least workspace_bytes of
+ * ldc >= N, both multiples of 8, and k * ldb * 2 < 2^32 - 256 (B is read through
+ * 32-bit buffer offsets).  d_workspace: at least workspace_bytes of
  * device memory (16-byte aligned) when workspace_bytes > 0, else ignored.
  * Device-side faults surface at the caller's next synchronisation. */
 spmm_status_t spmm_bcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void *d_C, int64_t ldc,
@@ -167,6 +171,14 @@ spmm_status_t spmm_wcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void
                             void *d_workspace, void *stream);
 
 spmm_status_t spmm_plan_info(spmm_plan_t plan, spmm_plan_info_t *info);
+
+/* Leading dimension (elements) to allocate for a dense operand with N columns of
+ * elem_bytes-byte elements: N rounded up to 8, plus 64 when the row pitch would
+ * be a multiple of 4 KiB.  With power-of-two pitches the rows that one column
+ * tile gathers from B all fall into the same L2 sets; the pad spreads them.
+ * Any ldb/ldc >= N that is a multiple of 8 is valid; this only affects speed.
+ * Returns N unchanged for N <= 0 or elem_bytes <= 0. */
+int64_t spmm_recommended_ld(int64_t N, int32_t elem_bytes);
 
 /* Frees the plan's host and device memory.  NULL is accepted.  The caller must
  * make sure no run using the plan is still executing. */

@@ -18,7 +18,7 @@ def _declared():
     for fn in os.listdir(os.path.join(ROOT, "include")):
         if fn.endswith(".h"):
             text = open(os.path.join(ROOT, "include", fn)).read()
-            names |= set(re.findall(r"^\s*(?:spmm_status_t|const char \*)\s*(spmm_\w+)\s*\(", text, re.M))
+            names |= set(re.findall(r"^\s*(?:spmm_status_t|const char \*|int64_t)\s*(spmm_\w+)\s*\(", text, re.M))
     return names
 
 
@@ -76,3 +76,14 @@ def test_plan_without_gpu_reports_hip_error():
         pytest.skip("a GPU is present")
     ptr = np.array([0, 1], np.int32)
     assert _code(lambda: ws.bcsr_plan(16, 64, 64, 16, 16, ptr, 256, 256)) == ws.ERR_HIP
+
+
+def test_recommended_ld():
+    # pitches that are a multiple of 4 KiB get 64 extra elements; others are kept
+    assert ws.recommended_ld(65536, 2) == 65600
+    assert ws.recommended_ld(65536, 4) == 65600
+    assert ws.recommended_ld(2048, 2) == 2112
+    assert ws.recommended_ld(128, 2) == 128
+    assert ws.recommended_ld(1000, 2) == 1000
+    assert ws.recommended_ld(1001, 2) == 1008
+    assert ws.recommended_ld(0, 2) == 0

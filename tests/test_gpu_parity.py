@@ -258,3 +258,23 @@ def test_config5_sampled(ws):
     assert np.isfinite(got).all()
     rows = np.random.default_rng(3).choice(p.m, 2048, replace=False)
     check(p, got, rows=rows)
+
+
+@pytest.mark.parametrize("env", [{"SPMM_FORCE_WAVES_N": "2"}, {"SPMM_FORCE_WAVES_N": "4"},
+                                 {"SPMM_FORCE_KERNEL": "0"}], ids=lambda e: ",".join(e))
+def test_bcsr64_kernel_variants_padded_ld(ws, env, monkeypatch):
+    """The 64x64-block kernels (LDS-shared A at 2 or 4 waves, and the generic one)
+    on a wide N with padded leading dimensions and a partial last column tile."""
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, v_)
+    p = synth.block_problem(448, 640, 1288, 64, 64, 0.25, seed=31, ab_dtype="bf16", c_dtype="bf16")
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    info = A.plan.info()
+    assert info["kernel"] == (0 if env.get("SPMM_FORCE_KERNEL") == "0" else 1)
+    B = A.device_b(p.B, padded=True)
+    C = A.new_c(padded=True)
+    C.fill_(float("nan"))
+    A.run(B, C)
+    torch.cuda.synchronize()
+    check(p, C.float().cpu().numpy().astype(np.float64))

@@ -35,7 +35,7 @@ EXPORTED = [
     "spmm_csr_to_bcsr_count", "spmm_csr_to_bcsr", "spmm_csr_to_wcsr_count", "spmm_csr_to_wcsr",
     "spmm_wcsr_split_count", "spmm_wcsr_split", "spmm_bcsr_plan", "spmm_wcsr_plan",
     "spmm_bcsr_run", "spmm_wcsr_run", "spmm_plan_info", "spmm_plan_destroy",
-    "spmm_status_string", "spmm_last_error",
+    "spmm_status_string", "spmm_last_error", "spmm_recommended_ld",
 ]
 
 
@@ -43,6 +43,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
                 ("tile_cols", ctypes.c_int32), ("waves_n", ctypes.c_int32),
                 ("waves_k", ctypes.c_int32), ("cols_per_lane", ctypes.c_int32),
+                ("kernel", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("split_cols", ctypes.c_int64), ("n_tasks", ctypes.c_int64),
                 ("n_merges", ctypes.c_int64), ("n_slots", ctypes.c_int64),
                 ("stored_entries", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
@@ -78,6 +79,13 @@ _lib.spmm_status_string.argtypes = [ctypes.c_int]
 _lib.spmm_status_string.restype = ctypes.c_char_p
 _lib.spmm_last_error.argtypes = []
 _lib.spmm_last_error.restype = ctypes.c_char_p
+_lib.spmm_recommended_ld.argtypes = [ctypes.c_int64, ctypes.c_int32]
+_lib.spmm_recommended_ld.restype = ctypes.c_int64
+
+
+def recommended_ld(N: int, elem_bytes: int) -> int:
+    """Leading dimension to allocate for an N-column operand (see the C header)."""
+    return int(_lib.spmm_recommended_ld(int(N), int(elem_bytes)))
 
 
 class SpmmError(RuntimeError):
@@ -284,10 +292,26 @@ class DeviceSparse:
     def stored_entries(self) -> int:
         return int(self.h_vals.size)
 
-    def new_c(self, device="cuda"):
+    def new_c(self, device="cuda", padded: bool = False):
+        """Uninitialised C (m x N); ``padded`` allocates rows of recommended_ld
+        elements and returns the m x N view."""
         import torch
-        return torch.empty((self.m, self.N), dtype=getattr(torch, _TORCH_C[self.c_dtype]),
-                           device=device)
+        dt = getattr(torch, _TORCH_C[self.c_dtype])
+        if not padded:
+            return torch.empty((self.m, self.N), dtype=dt, device=device)
+        ld = recommended_ld(self.N, torch.empty(0, dtype=dt).element_size())
+        return torch.empty((self.m, ld), dtype=dt, device=device)[:, :self.N]
+
+    def device_b(self, codes: np.ndarray, device="cuda", padded: bool = False):
+        """Copies host 16-bit codes of B (k x N) to the device (padded rows optionally)."""
+        import torch
+        src = torch.from_numpy(np.ascontiguousarray(codes).view(np.int16))
+        if not padded:
+            return src.to(device)
+        ld = recommended_ld(self.N, 2)
+        out = torch.empty((self.k, ld), dtype=torch.int16, device=device)[:, :self.N]
+        out.copy_(src)
+        return out
 
     def run(self, B, C, stream=None):
         (bcsr_run if self.fmt == "bcsr" else wcsr_run)(self.plan, B, C, self.workspace, stream)

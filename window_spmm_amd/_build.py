@@ -21,8 +21,11 @@ HIP_SOURCES = ["kernels.hip", "api.hip"]
 HEADERS = ["common.h", "kernels.h"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
+# MFMA accumulators stay in ordinary VGPRs (the unified register file of gfx950),
+# which avoids AGPR<->VGPR copies around the software-pipelined loops.
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC,
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wall"]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wextra"]
 
 

@@ -24,6 +24,7 @@ struct spmm_plan_s {
     int64_t n_merges, n_slots, split_cols;
     int64_t stored_entries;
     int V, waves_n, waves_k;
+    int kernel;                 // 0: generic tile kernel, 1: BCSR 64x64 with LDS-shared A
     int64_t tile_cols, n_col_tiles;
     size_t workspace;
     int device;
@@ -31,6 +32,10 @@ struct spmm_plan_s {
 
 namespace wspmm {
 namespace {
+
+// Buffer resources address at most 2^32 bytes; the kernels use offsets above
+// this bound as "read zero".
+constexpr uint64_t kMaxBBytes = 0xFFFFFF00ull;
 
 int env_int(const char *name, int dflt)
 {
@@ -75,9 +80,9 @@ spmm_status_t check_common(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, i
         return fail(SPMM_ERR_INVALID_ARGUMENT, "block/window size must be positive");
     if (b_row != 16 && b_row != 32 && b_row != 64)
         return fail(SPMM_ERR_UNSUPPORTED, "b_row = %d: supported 16, 32, 64", b_row);
-    if (b_col % 8 != 0 || (bcsr && b_col > 256))
-        return fail(SPMM_ERR_UNSUPPORTED, "b_col = %d: must be a multiple of 8%s", b_col,
-                    bcsr ? " and at most 256" : "");
+    if (b_col % 8 != 0 || (bcsr && (b_col > 256 || (b_col & (b_col - 1)) != 0)))
+        return fail(SPMM_ERR_UNSUPPORTED, "b_col = %d: must be %s", b_col,
+                    bcsr ? "a power of two in [8, 256]" : "a multiple of 8");
     if (ab != SPMM_FP16 && ab != SPMM_BF16)
         return fail(SPMM_ERR_UNSUPPORTED, "A/B dtype must be FP16 or BF16");
     if (ct != SPMM_FP32 && ct != SPMM_BF16 && ct != SPMM_FP16)
@@ -113,14 +118,14 @@ void choose_config(spmm_plan_s *pl, double mean_kprime, int n_cu)
     const int64_t wave_cols = 16 * V;
     const int64_t col_waves = ceil_div(pl->N, wave_cols);
     int wn = (pl->b_row == 64 && col_waves >= 2) ? 2 : 1;
-    wn = std::max(1, std::min(8, env_int("SPMM_FORCE_WAVES_N", wn)));
+    wn = std::max(1, std::min(4, env_int("SPMM_FORCE_WAVES_N", wn)));
     const int64_t col_tiles = std::max<int64_t>(1, ceil_div(pl->N, wave_cols * wn));
     // add reduction waves while the grid is small and the items are long
     const int64_t waves = std::max<int64_t>(1, pl->n_items * col_tiles * wn);
     int wk = 1;
-    while (wn * wk * 2 <= 8 && waves * wk < int64_t(16) * n_cu && mean_kprime >= 64.0 * wk * 2)
+    while (wn * wk * 2 <= 4 && waves * wk < int64_t(16) * n_cu && mean_kprime >= 64.0 * wk * 2)
         wk *= 2;
-    wk = std::max(1, std::min(8 / wn, env_int("SPMM_FORCE_WAVES_K", wk)));
+    wk = std::max(1, std::min(4 / wn, env_int("SPMM_FORCE_WAVES_K", wk)));
     pl->V = V;
     pl->waves_n = wn;
     pl->waves_k = wk;
@@ -169,6 +174,8 @@ spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int
         return fail(SPMM_ERR_UNSUPPORTED, "B and C must be 16-byte aligned");
     if (ldb < pl->N || ldc < pl->N || ldb % 8 || ldc % 8)
         return fail(SPMM_ERR_UNSUPPORTED, "ldb/ldc must be >= N and multiples of 8");
+    if ((uint64_t)pl->k * (uint64_t)ldb * 2u >= kMaxBBytes)
+        return fail(SPMM_ERR_UNSUPPORTED, "B (k * ldb * 2 bytes) must be smaller than 4 GiB - 256");
     if (pl->workspace > 0 && (!ws || ((uintptr_t)ws & 15)))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "plan needs a 16-byte aligned workspace of %zu bytes",
                     pl->workspace);
@@ -203,12 +210,20 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.m = pl->m;
     p.k = pl->k;
     p.N = pl->N;
+    p.b_bytes = (uint64_t)pl->k * (uint64_t)ldb * 2u;
+    p.n_items = pl->n_items;
+    p.n_col_tiles = pl->n_col_tiles;
     p.b_col = pl->b_col;
+    p.log2_b_col = 0;
+    while ((1 << p.log2_b_col) < pl->b_col)
+        ++p.log2_b_col;
     p.tile_cols = (int32_t)pl->tile_cols;
     p.waves_n = pl->waves_n;
     p.waves_k = pl->waves_k;
     p.c_dtype = pl->ct;
-    hipError_t e = launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, pl->n_items, pl->n_col_tiles, st);
+    p.order = env_int("SPMM_FORCE_ORDER", 0) ? 1 : 0;
+    hipError_t e = pl->kernel == 1 ? launch_bcsr64_lds(pl->ab, p, st)
+                                   : launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, st);
     if (e != hipSuccess)
         return hip_fail(e, "tile kernel launch");
     if (pl->n_merges > 0) {
@@ -271,9 +286,21 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
     }
     const double mean_k = nbr > 0 ? (double)h_block_row_ptr[nbr] * b_col / (double)nbr : 0.0;
     choose_config(pl, mean_k, n_cu);
-    if (pl->n_col_tiles > 65535) {
+    // 64x64 blocks with at least one full 512-column tile: A blocks shared via LDS
+    pl->kernel = env_int("SPMM_FORCE_KERNEL", (b_row == 64 && b_col == 64 && N >= 256) ? 1 : 0);
+    if (pl->kernel == 1 && b_row == 64 && b_col == 64) {
+        const int nw = env_int("SPMM_FORCE_WAVES_N", 4) == 2 ? 2 : 4;
+        pl->V = 8;
+        pl->waves_n = nw;
+        pl->waves_k = 1;
+        pl->tile_cols = 128 * nw;
+        pl->n_col_tiles = ceil_div(N, pl->tile_cols);
+    } else {
+        pl->kernel = 0;
+    }
+    if (pl->n_items * pl->n_col_tiles > 0x7fffffff) {
         free_plan(pl);
-        return fail(SPMM_ERR_UNSUPPORTED, "N too large for the column-tile grid");
+        return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
     }
     pl->workspace = 0;
     *workspace_bytes = 0;
@@ -356,9 +383,9 @@ extern "C" spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
     }
     const double mean_task = nt > 0 ? (double)P / (double)nt : 0.0;
     choose_config(pl, mean_task, n_cu);
-    if (pl->n_col_tiles > 65535) {
+    if (pl->n_items * pl->n_col_tiles > 0x7fffffff) {
         free_plan(pl);
-        return fail(SPMM_ERR_UNSUPPORTED, "N too large for the column-tile grid");
+        return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
     }
     if (nm > 0 && ceil_div((int64_t)b_row * (N / 8), 256) > 65535) {
         free_plan(pl);
@@ -393,6 +420,7 @@ extern "C" spmm_status_t spmm_plan_info(spmm_plan_t pl, spmm_plan_info_t *info)
     info->waves_n = pl->waves_n;
     info->waves_k = pl->waves_k;
     info->cols_per_lane = pl->V;
+    info->kernel = pl->kernel;
     info->split_cols = pl->fmt == 1 ? pl->split_cols : 0;
     info->n_tasks = pl->fmt == 1 ? pl->n_items : 0;
     info->n_merges = pl->n_merges;
@@ -406,4 +434,15 @@ extern "C" spmm_status_t spmm_plan_destroy(spmm_plan_t plan)
 {
     free_plan(plan);
     return ok();
+}
+
+extern "C" int64_t spmm_recommended_ld(int64_t N, int32_t elem_bytes)
+{
+    if (N <= 0 || elem_bytes <= 0)
+        return N;
+    const int64_t ld = ceil_div(N, 8) * 8;
+    // Row pitches that are a multiple of 4 KiB put the rows of a column slice into
+    // the same L2 sets; 64 extra elements (an odd number of 128-byte lines for
+    // 16-bit data) spread them.
+    return (ld * elem_bytes) % 4096 == 0 ? ld + 64 : ld;
 }

@@ -21,11 +21,16 @@ struct TileParams {
     int64_t ldc;
     float *partial;           // WCSR partial tiles [slot][R][N] (fp32)
     int64_t m, k, N;
+    uint64_t b_bytes;         // k * ldb * 2: bytes of B the kernel may read (< 2^32 - 256)
+    int64_t n_items;          // block rows (BCSR) or tasks (WCSR)
+    int64_t n_col_tiles;      // column tiles; grid = n_items * n_col_tiles work-groups
     int32_t b_col;
+    int32_t log2_b_col;       // BCSR: b_col is a power of two
     int32_t tile_cols;        // columns per work-group tile = waves_n * 16 * V
     int32_t waves_n;          // waves splitting the columns
     int32_t waves_k;          // waves splitting the packed-column reduction
     int32_t c_dtype;          // spmm_dtype_t of C
+    int32_t order;            // 0: XCD-contiguous, column-tile major; 1: launch order
 };
 
 struct MergeParams {
@@ -40,9 +45,11 @@ struct MergeParams {
 // LDS bytes the tile kernel needs for its cross-wave reduction.
 size_t tile_lds_bytes(int R, int V, int waves_n, int waves_k);
 
-// fmt: 0 = BCSR (grid.x = block rows), 1 = WCSR (grid.x = tasks).
-hipError_t launch_tiles(int fmt, int R, int V, int ab_dtype, const TileParams &p, int64_t n_items,
-                        int64_t n_col_tiles, hipStream_t stream);
+// fmt: 0 = BCSR (work items = block rows), 1 = WCSR (work items = tasks).
+hipError_t launch_tiles(int fmt, int R, int V, int ab_dtype, const TileParams &p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stream);
+// BCSR with 64x64 blocks, waves_n (2 or 4) waves x 128 columns per work-group, A
+// shared through LDS (requires waves_k = 1, V = 8, tile_cols = 128 * waves_n).
+hipError_t launch_bcsr64_lds(int ab_dtype, const TileParams &p, hipStream_t stream);
 
 }  // namespace wspmm

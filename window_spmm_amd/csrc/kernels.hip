@@ -2,8 +2,8 @@
 //
 // Both formats reduce to the same per-tile computation.  A work-group tile owns
 // R consecutive rows of C (a BCSR block row or a WCSR window, R = b_row) and a
-// BN-wide slice of its columns.  Along the reduction the tile walks a "packed"
-// column axis k':
+// column slice of C.  Along the reduction the tile walks a "packed" column axis
+// k':
 //   BCSR  k' = q*b_col + kk  for the q-th stored block of the block row:
 //         A(r, k') = blocks[q][r][kk],  B row = block_col_idx[q]*b_col + kk
 //   WCSR  k' = p, a packed column of the window:
@@ -21,12 +21,26 @@
 // therefore hold V adjacent columns of each of its rows, which the epilogue
 // stores with one wide store per row.
 //
+// Memory access goes through buffer resources (base, size): a k' step past the
+// end of the work item, a -1 pad column or an index outside [0, k) gets an
+// offset beyond the resource size, and the hardware returns zeros.  There is no
+// branch in the main loop and no access outside the caller's arrays.
+//
+// Latency hiding: every wave runs a two-stage software pipeline.  The B-row
+// indices of step s+2 and the A/B data of step s+1 are in flight while the
+// MFMAs of step s execute (vmcnt ordering keeps the later loads outstanding).
+//
 // Waves of a work-group split the tile's columns (waves_n, each 16*V wide) and
 // the reduction (waves_k, interleaved 32-wide k' steps); the waves_k partial
 // sums are added in a fixed order through LDS, so results are deterministic.
 // WCSR tasks that cover only part of a long window write fp32 partial tiles to
 // a workspace slot; wcsr_merge adds the slots of a window in slot order and
 // rounds once (this replaces the paper's atomicAdd merge, Section III-C).
+//
+// Work-group order: dispatch hands consecutive work-group ids to the 8 XCDs in
+// turn.  The kernel renumbers ids so that each XCD receives a contiguous range
+// of (column tile, work item) pairs, column tile outermost: the work-groups
+// that share a column slice of B run on one XCD and share its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,8 +51,35 @@ namespace wspmm {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Word 3 of a raw buffer resource on gfx9-class devices (no format conversion,
+// no swizzle): the value the ROCm libraries use for gfx90a/gfx94x/gfx950.
+constexpr int kRsrcWord3 = 0x00020000;
+// Offset used for "no data": beyond any resource size the host allows.
+constexpr uint32_t kOOB = 0xFFFFFFF0u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+template <int DW>
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *out)
+{
+    if constexpr (DW == 4) {
+        u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    } else if constexpr (DW == 2) {
+        u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+        out[0] = v[0]; out[1] = v[1];
+    } else {
+        out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    }
+}
 
 template <int AB>
 __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
@@ -66,38 +107,27 @@ __device__ __forceinline__ uint32_t f32_to_f16(float f)
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// Loads DW dwords (DW = 1, 2, 4) from a naturally aligned address.
-template <int DW>
-__device__ __forceinline__ void load_dw(const uint16_t *p, uint32_t *out)
+// Stores V consecutive results of one row as c_dtype (NT: non-temporal stores).
+template <typename T>
+__device__ __forceinline__ void st(T *d, T x, bool nt)
 {
-    if constexpr (DW == 4) {
-        u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
-        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
-    } else if constexpr (DW == 2) {
-        u32x2_t v = *reinterpret_cast<const u32x2_t *>(p);
-        out[0] = v[0]; out[1] = v[1];
-    } else {
-        out[0] = *reinterpret_cast<const uint32_t *>(p);
-    }
+    if (nt)
+        __builtin_nontemporal_store(x, d);
+    else
+        *d = x;
 }
 
-// Stores V consecutive results of one row as c_dtype.
-template <int V>
+template <int V, bool NT = false>
 __device__ __forceinline__ void store_row(void *base, int64_t elem, int c_dtype, const float *v)
 {
     if (c_dtype == SPMM_FP32) {
         float *d = reinterpret_cast<float *>(base) + elem;
+        if constexpr (V >= 4) {
 #pragma unroll
-        for (int c = 0; c < V; c += 4) {
-            if constexpr (V >= 4) {
-                f32x4_t x = {v[c], v[c + 1], v[c + 2], v[c + 3]};
-                *reinterpret_cast<f32x4_t *>(d + c) = x;
-            }
-        }
-        if constexpr (V == 2) {
-            typedef float f32x2_t __attribute__((ext_vector_type(2)));
-            f32x2_t x = {v[0], v[1]};
-            *reinterpret_cast<f32x2_t *>(d) = x;
+            for (int c = 0; c < V; c += 4)
+                st(reinterpret_cast<f32x4_t *>(d + c), f32x4_t{v[c], v[c + 1], v[c + 2], v[c + 3]}, NT);
+        } else {
+            st(reinterpret_cast<f32x2_t *>(d), f32x2_t{v[0], v[1]}, NT);
         }
     } else {
         uint32_t w[V / 2];
@@ -108,51 +138,108 @@ __device__ __forceinline__ void store_row(void *base, int64_t elem, int c_dtype,
             w[c / 2] = lo | (hi << 16);
         }
         uint16_t *d = reinterpret_cast<uint16_t *>(base) + elem;
-        if constexpr (V == 8) {
-            u32x4_t x = {w[0], w[1], w[2], w[3]};
-            *reinterpret_cast<u32x4_t *>(d) = x;
-        } else if constexpr (V == 4) {
-            u32x2_t x = {w[0], w[1]};
-            *reinterpret_cast<u32x2_t *>(d) = x;
-        } else {
-            *reinterpret_cast<uint32_t *>(d) = w[0];
-        }
+        if constexpr (V == 8)
+            st(reinterpret_cast<u32x4_t *>(d), u32x4_t{w[0], w[1], w[2], w[3]}, NT);
+        else if constexpr (V == 4)
+            st(reinterpret_cast<u32x2_t *>(d), u32x2_t{w[0], w[1]}, NT);
+        else
+            st(reinterpret_cast<uint32_t *>(d), w[0], NT);
     }
 }
 
+// Work-group id -> (work item, column tile), XCD-contiguous and column-tile major.
+__device__ __forceinline__ void tile_of(int64_t n_items, int64_t total, int order, int64_t &item,
+                                        int64_t &ctile)
+{
+    const int64_t i = blockIdx.x;
+    const int64_t q = total >> 3, rem = total & 7;
+    const int64_t xcd = i & 7, local = i >> 3;
+    const int64_t logical = order ? i : xcd * q + (xcd < rem ? xcd : rem) + local;
+    // (readfirstlane: tell the compiler these are wave-uniform, so that the
+    // loads they address become scalar loads)
+    ctile = __builtin_amdgcn_readfirstlane((int)(logical / n_items));
+    item = __builtin_amdgcn_readfirstlane((int)(logical - ctile * n_items));
+}
+
+// One pipeline stage: the gathered B rows and the A fragments of one k' step.
+template <int MT, int DW>
+struct Stage {
+    uint32_t b[8][DW];
+    u32x4_t a[MT];
+};
+
+// Raw B-row index data of one k' step (WCSR: 8 indices, BCSR: 1 block column).
+template <int FMT>
+struct Idx;
+template <>
+struct Idx<0> {
+    uint32_t j;
+};
+template <>
+struct Idx<1> {
+    uint32_t v[8];
+};
+
 template <int FMT, int R, int V, int AB>
-__global__ __launch_bounds__(512) void spmm_tile_kernel(TileParams p)
+__global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
 {
     constexpr int MT = R / 16;  // 16-row MFMA tiles per work-group tile
     constexpr int DW = V / 2;   // dwords of one gathered row segment per lane
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave % p.waves_n;
     const int wk = wave / p.waves_n;
     const int g = lane >> 4;
     const int li = lane & 15;
 
-    // ---- work item -------------------------------------------------------
-    int64_t row0, kbegin, kend, a_base = 0, wcols = 0, blk0 = 0;
+    int64_t item, ctile;
+    tile_of(p.n_items, p.n_items * p.n_col_tiles, p.order, item, ctile);
+
+    // ---- work item: rows, packed-column range, A/index resources ----------
+    int64_t row0, kbegin, kend;
     int32_t slot = -1;
+    __amdgpu_buffer_rsrc_t rA, rI;
+    uint32_t a_row_stride;  // bytes between rows of A inside the work item
     if constexpr (FMT == 0) {
-        const int64_t I = blockIdx.x;
-        blk0 = p.row_ptr[I];
-        row0 = I * R;
+        const int64_t blk0 = p.row_ptr[item];
+        const int64_t nblk = p.row_ptr[item + 1] - blk0;
+        row0 = item * R;
         kbegin = 0;
-        kend = (int64_t)(p.row_ptr[I + 1] - blk0) * p.b_col;
+        kend = nblk * p.b_col;
+        rA = make_rsrc(p.A + blk0 * R * p.b_col, (uint32_t)(nblk * R * p.b_col * 2));
+        rI = make_rsrc(p.col_idx + blk0, (uint32_t)(nblk * 4));
+        a_row_stride = (uint32_t)p.b_col * 2;
     } else {
-        const int4 t = p.tasks[blockIdx.x];
+        const int4 t = p.tasks[item];
         const int64_t w = t.x;
+        const int64_t wbase = p.row_ptr[w];
+        const int64_t W = p.row_ptr[w + 1] - wbase;
         row0 = w * R;
         kbegin = t.y;
         kend = t.z;
         slot = t.w;
-        a_base = p.row_ptr[w];                  // packed column where the window starts
-        wcols = p.row_ptr[w + 1] - a_base;      // window width W
+        rA = make_rsrc(p.A + R * wbase, (uint32_t)(R * W * 2));
+        rI = make_rsrc(p.col_idx + kbegin, (uint32_t)((kend - kbegin) * 4));
+        a_row_stride = (uint32_t)W * 2;
+        kbegin -= wbase;  // from here on k' counts from the window start
+        kend -= wbase;
     }
-    const int64_t ncol = (int64_t)blockIdx.y * p.tile_cols + wn * 16 * V + li * V;
-    const bool ncol_ok = ncol < p.N;
+    // B resource starts at this wave's first column; rows are ldb apart.
+    const int64_t col0 = ctile * p.tile_cols + wn * 16 * V;
+    const uint64_t b_skip = (uint64_t)col0 * 2;
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc(p.B + col0, (uint32_t)(p.b_bytes > b_skip ? p.b_bytes - b_skip : 0));
+    const uint32_t ldb2 = (uint32_t)p.ldb * 2;
+    const uint32_t lane_col_bytes = (uint32_t)li * V * 2;
+    const uint32_t k32 = (uint32_t)p.k;
+    const uint32_t nbc = (uint32_t)((p.k + p.b_col - 1) >> p.log2_b_col);  // block columns
+    const int64_t kspan = kend - kbegin - 32 * wk;
+    const int nsteps = kspan > 0 ? (int)((kspan + 32 * p.waves_k - 1) / (32 * p.waves_k)) : 0;
+    // first k' of this lane at step s: kfirst + s * kstride (relative to the item start)
+    const uint32_t kfirst = (uint32_t)(kbegin + 32 * wk + 8 * g);
+    const uint32_t kstride = 32u * p.waves_k;
+    const uint32_t klimit = (uint32_t)kend;
+    const uint32_t idx_base = (uint32_t)kbegin;  // WCSR index resource starts here
 
     f32x4_t acc[MT][V];
 #pragma unroll
@@ -161,77 +248,98 @@ __global__ __launch_bounds__(512) void spmm_tile_kernel(TileParams p)
         for (int c = 0; c < V; ++c)
             acc[mt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t kb = kbegin + 32 * wk; kb < kend; kb += 32 * p.waves_k) {
-        const int64_t kg = kb + 8 * g;        // this lane's first k'
-        const bool gvalid = kg < kend;
-
-        // ---- B row of each of the 8 k' (index translation) ----
-        int64_t brow[8];
+    // Loaded registers are never modified before use: validity of a step is
+    // recomputed where the data is consumed, so no load forces an early wait.
+    auto load_idx = [&](int s, Idx<FMT> &ix) {
+        const uint32_t kg = kfirst + (uint32_t)s * kstride;
+        const bool ok = kg < klimit;
         if constexpr (FMT == 0) {
-            int64_t q = kg / p.b_col;
-            int64_t kk = kg - q * p.b_col;
-            int64_t J = gvalid ? (int64_t)p.col_idx[blk0 + q] : -1;
-            int64_t r0 = J >= 0 ? J * p.b_col + kk : -1;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                brow[j] = r0 >= 0 ? r0 + j : -1;
+            buf_load<1>(rI, ok ? (kg >> p.log2_b_col) * 4u : kOOB, &ix.j);
         } else {
-            if (gvalid) {
-                const int4 *ip = reinterpret_cast<const int4 *>(p.col_idx + kg);
-                int4 x0 = ip[0], x1 = ip[1];
-                brow[0] = x0.x; brow[1] = x0.y; brow[2] = x0.z; brow[3] = x0.w;
-                brow[4] = x1.x; brow[5] = x1.y; brow[6] = x1.z; brow[7] = x1.w;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    brow[j] = -1;
-            }
+            const uint32_t off = ok ? (kg - idx_base) * 4u : kOOB;
+            buf_load<4>(rI, off, ix.v);
+            buf_load<4>(rI, off + 16u, ix.v + 4);
         }
+    };
 
-        // ---- gather V columns of the 8 B rows ----
-        uint32_t bw[8][DW];
+    auto issue = [&](int s, const Idx<FMT> &ix, Stage<MT, DW> &st) {
+        const uint32_t kg = kfirst + (uint32_t)s * kstride;
+        const bool ok = kg < klimit;
+        uint32_t a_off;
+        if constexpr (FMT == 0) {
+            const uint32_t q = kg >> p.log2_b_col;
+            const uint32_t kk = kg & (uint32_t)(p.b_col - 1);
+            const bool jv = ok & (ix.j < nbc);
+            const uint32_t r0 = (jv ? ix.j : 0u) * (uint32_t)p.b_col + kk;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (ncol_ok && brow[j] >= 0 && brow[j] < p.k) {
-                load_dw<DW>(p.B + brow[j] * p.ldb + ncol, bw[j]);
-            } else {
-#pragma unroll
-                for (int d = 0; d < DW; ++d)
-                    bw[j][d] = 0;
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t r = r0 + j;
+                const bool rv = jv & (r < k32);
+                buf_load<DW>(rB, rv ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
             }
+            a_off = ((q * R + li) * (uint32_t)p.b_col + kk) * 2u;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t r = ix.v[j];
+                const uint32_t off = r * ldb2 + lane_col_bytes;
+                buf_load<DW>(rB, (ok & (r < k32)) ? off : kOOB, st.b[j]);
+            }
+            a_off = li * a_row_stride + kg * 2u;
         }
-
-        // ---- A fragments: row li of each 16-row tile, 8 consecutive k' ----
-        u32x4_t af[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            if (gvalid) {
-                int64_t off;
-                if constexpr (FMT == 0) {
-                    int64_t q = kg / p.b_col;
-                    off = (blk0 + q) * (int64_t)(R * p.b_col) + (int64_t)(mt * 16 + li) * p.b_col +
-                          (kg - q * p.b_col);
-                } else {
-                    off = R * a_base + (int64_t)(mt * 16 + li) * wcols + (kg - a_base);
-                }
-                af[mt] = *reinterpret_cast<const u32x4_t *>(p.A + off);
-            } else {
-                af[mt] = u32x4_t{0u, 0u, 0u, 0u};
-            }
+            uint32_t t[4];
+            buf_load<4>(rA, ok ? a_off + (uint32_t)(mt * 16) * a_row_stride : kOOB, t);
+            st.a[mt] = u32x4_t{t[0], t[1], t[2], t[3]};
         }
+    };
 
-        // ---- transpose 8 rows x V columns into V operands of 8 k' each ----
+    auto compute = [&](const Stage<MT, DW> &st) {
 #pragma unroll
         for (int c = 0; c < V; ++c) {
             const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
             u32x4_t bf;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                bf[q] = __builtin_amdgcn_perm(bw[2 * q + 1][c >> 1], bw[2 * q][c >> 1], sel);
+                bf[q] = __builtin_amdgcn_perm(st.b[2 * q + 1][c >> 1], st.b[2 * q][c >> 1], sel);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                acc[mt][c] = mfma16x16x32<AB>(af[mt], bf, acc[mt][c]);
+                acc[mt][c] = mfma16x16x32<AB>(st.a[mt], bf, acc[mt][c]);
         }
+    };
+
+    // ---- two-stage pipeline over the k' steps (nsteps is wave-uniform) ----
+    // Loads are issued unconditionally (a step past the end reads zeros), so the
+    // wait-count bookkeeping sees the same outstanding loads on every path.
+    if (nsteps > 0) {
+        Idx<FMT> ix0, ix1;
+        Stage<MT, DW> st0, st1;
+        load_idx(0, ix0);
+        load_idx(1, ix1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(0, ix0, st0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_idx(2, ix0);
+        __builtin_amdgcn_sched_barrier(0);
+        // invariant at the top: st0 = data of step s, ix1 = indices of s+1, ix0 of s+2
+        // (sched_barrier keeps the compiler from sinking the prefetches below
+        // the MFMAs, which would serialise loads and compute again)
+        int s = 0;
+        for (; s + 1 < nsteps; s += 2) {
+            issue(s + 1, ix1, st1);
+            load_idx(s + 3, ix1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st0);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(s + 2, ix0, st0);
+            load_idx(s + 4, ix0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (s < nsteps)
+            compute(st0);
     }
 
     // ---- fixed-order sum of the waves_k partial tiles through LDS ----
@@ -266,7 +374,8 @@ __global__ __launch_bounds__(512) void spmm_tile_kernel(TileParams p)
     }
 
     // ---- epilogue: row 4g+q of each 16-row tile, V adjacent columns ----
-    if (!ncol_ok)
+    const int64_t ncol = col0 + li * V;
+    if (ncol >= p.N)
         return;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -282,6 +391,159 @@ __global__ __launch_bounds__(512) void spmm_tile_kernel(TileParams p)
             } else if (row0 + r < p.m) {
                 store_row<V>(p.C, (row0 + r) * p.ldc + ncol, p.c_dtype, v);
             }
+        }
+    }
+}
+
+// Waits until this wave's LDS operations are done, then joins the work-group
+// barrier.  Unlike __syncthreads() it does not wait for outstanding global
+// loads, so prefetched B rows stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+    __builtin_amdgcn_s_barrier();
+}
+
+// BCSR with 64 x 64 blocks and a wide column tile (NW waves x 128 columns).
+// Same MFMA mapping and B pipeline as spmm_tile_kernel, but the A block is
+// shared: the work-group loads each 64 x 64 block once (non-temporal, it is
+// streamed) into one of two padded LDS buffers, and every wave reads its A
+// fragments from there.  Block-column indices are work-group uniform and come
+// through scalar loads.  One LDS barrier per block.
+template <int AB, int NW>
+__global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
+                                                             const int32_t *__restrict__ block_cols)
+{
+    constexpr int R = 64, BC = 64, MT = 4, V = 8, DW = 4;
+    constexpr int NT = NW * 64;                    // threads per work-group
+    constexpr int STRIDE = BC * 2 + 16;            // padded LDS row: conflict-free b128 reads
+    constexpr int ABUF = R * STRIDE;               // bytes of one A buffer
+    constexpr int CPT = R * BC / 8 / NT;           // 16-byte chunks per thread per block
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * ABUF];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int li = lane & 15;
+
+    int64_t item, ctile;
+    tile_of(p.n_items, p.n_items * p.n_col_tiles, p.order, item, ctile);
+    const int64_t blk0 = p.row_ptr[item];
+    const int nblk = p.row_ptr[item + 1] - (int)blk0;
+    const int64_t row0 = item * R;
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(p.A + blk0 * R * BC, (uint32_t)((int64_t)nblk * R * BC * 2));
+    const int64_t col0 = ctile * p.tile_cols + wave * 16 * V;
+    const uint64_t b_skip = (uint64_t)col0 * 2;
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc(p.B + col0, (uint32_t)(p.b_bytes > b_skip ? p.b_bytes - b_skip : 0));
+    const uint32_t ldb2 = (uint32_t)p.ldb * 2;
+    const uint32_t lane_col_bytes = (uint32_t)li * V * 2;
+    const uint32_t k32 = (uint32_t)p.k;
+    const uint32_t nbc = (uint32_t)((p.k + BC - 1) / BC);
+
+    f32x4_t acc[MT][V];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int c = 0; c < V; ++c)
+            acc[mt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // cooperative A-block copy: chunk c of a block = row c/8, 8 columns (c%8)*8
+    auto load_a = [&](int q, u32x4_t (&r)[CPT]) {
+#pragma unroll
+        for (int t = 0; t < CPT; ++t) {
+            const int c = threadIdx.x + t * NT;
+            r[t] = __builtin_amdgcn_raw_buffer_load_b128(
+                rA, (int)(((uint32_t)q * R * BC + (uint32_t)c * 8) * 2), 0, 2 /* nt */);
+        }
+    };
+    auto store_a = [&](int buf, const u32x4_t (&r)[CPT]) {
+#pragma unroll
+        for (int t = 0; t < CPT; ++t) {
+            const int c = threadIdx.x + t * NT;
+            *reinterpret_cast<u32x4_t *>(lds_a + buf * ABUF + (c >> 3) * STRIDE + (c & 7) * 16) =
+                r[t];
+        }
+    };
+    // Block column of block q (work-group uniform, so a scalar load); -1 past the end.
+    auto block_col = [&](int q) -> uint32_t {
+        const int at = __builtin_amdgcn_readfirstlane((int)blk0 + (q < nblk ? q : 0));
+        const uint32_t J = (uint32_t)block_cols[at];
+        return q < nblk ? J : 0xFFFFFFFFu;
+    };
+    // B rows of k' step s of block column J (half s%2): J*64 + 32*(s%2) + 8g + j
+    auto issue_b = [&](int s, uint32_t J, Stage<MT, DW> &st) {
+        const bool jv = J < nbc;
+        const uint32_t r0 = (jv ? J : 0u) * BC + (uint32_t)(s & 1) * 32 + 8 * g;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t r = r0 + j;
+            buf_load<DW>(rB, (jv & (r < k32)) ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
+        }
+    };
+    auto compute = [&](const Stage<MT, DW> &st, int buf, int half) {
+        u32x4_t af[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            af[mt] = *reinterpret_cast<const u32x4_t *>(lds_a + buf * ABUF + (mt * 16 + li) * STRIDE +
+                                                       (half * 32 + 8 * g) * 2);
+#pragma unroll
+        for (int c = 0; c < V; ++c) {
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            u32x4_t bf;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                bf[q] = __builtin_amdgcn_perm(st.b[2 * q + 1][c >> 1], st.b[2 * q][c >> 1], sel);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt][c] = mfma16x16x32<AB>(af[mt], bf, acc[mt][c]);
+        }
+    };
+
+    if (nblk > 0) {
+        u32x4_t areg[CPT];
+        Stage<MT, DW> st0, st1;
+        uint32_t Jcur = block_col(0);
+        load_a(0, areg);
+        issue_b(0, Jcur, st0);
+        store_a(0, areg);
+        lds_barrier();
+        for (int q = 0; q < nblk; ++q) {
+            // first half of block q: prefetch its second half, the next A block and
+            // the next block column
+            const uint32_t Jnext = block_col(q + 1);
+            issue_b(1, Jcur, st1);
+            load_a(q + 1 < nblk ? q + 1 : q, areg);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st0, q & 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // second half: prefetch the first half of block q+1
+            issue_b(0, Jnext, st0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st1, q & 1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            store_a((q + 1) & 1, areg);
+            lds_barrier();
+            Jcur = Jnext;
+        }
+    }
+
+    // epilogue (non-temporal stores: C is written once)
+    const int64_t ncol = col0 + li * V;
+    if (ncol >= p.N)
+        return;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = mt * 16 + 4 * g + q;
+            float v[V];
+#pragma unroll
+            for (int c = 0; c < V; ++c)
+                v[c] = acc[mt][c][q];
+            if (row0 + r < p.m)
+                store_row<V, true>(p.C, (row0 + r) * p.ldc + ncol, p.c_dtype, v);
         }
     }
 }
@@ -353,10 +615,30 @@ size_t tile_lds_bytes(int R, int V, int waves_n, int waves_k)
     return waves_k > 1 ? (size_t)waves_n * (R / 16) * V * 4 * 64 * sizeof(float) : 0;
 }
 
-hipError_t launch_tiles(int fmt, int R, int V, int ab, const TileParams &p, int64_t n_items,
-                        int64_t n_col_tiles, hipStream_t stream)
+template <int NW>
+static void launch_lds_nw(int ab, const TileParams &p, hipStream_t stream)
 {
-    dim3 grid((unsigned)n_items, (unsigned)n_col_tiles);
+    dim3 grid((unsigned)(p.n_items * p.n_col_tiles));
+    if (ab == SPMM_FP16)
+        hipLaunchKernelGGL((bcsr64_lds_kernel<SPMM_FP16, NW>), grid, dim3(NW * 64), 0, stream, p,
+                           p.col_idx);
+    else
+        hipLaunchKernelGGL((bcsr64_lds_kernel<SPMM_BF16, NW>), grid, dim3(NW * 64), 0, stream, p,
+                           p.col_idx);
+}
+
+hipError_t launch_bcsr64_lds(int ab, const TileParams &p, hipStream_t stream)
+{
+    if (p.waves_n == 2)
+        launch_lds_nw<2>(ab, p, stream);
+    else
+        launch_lds_nw<4>(ab, p, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_tiles(int fmt, int R, int V, int ab, const TileParams &p, hipStream_t stream)
+{
+    dim3 grid((unsigned)(p.n_items * p.n_col_tiles));
     dim3 block(64 * p.waves_n * p.waves_k);
     size_t lds = tile_lds_bytes(R, V, p.waves_n, p.waves_k);
     return fmt == 0 ? by_r<0>(R, V, ab, p, grid, block, lds, stream)
