@@ -54,10 +54,10 @@ typedef struct {
     int32_t cols_per_lane;   /* adjacent C columns each lane accumulates (V) */
     int32_t kernel;          /* 0: generic tile kernel; 1: BCSR 64x64 kernel with LDS-shared A */
     int32_t reserved;
-    int64_t split_cols;      /* WCSR sub-task size T (0 for BCSR) */
-    int64_t n_tasks;         /* WCSR tasks (= work-groups per column tile) */
-    int64_t n_merges;        /* WCSR windows split into more than one task */
-    int64_t n_slots;         /* WCSR partial-result slots in the workspace */
+    int64_t split_cols;      /* sub-task size T in packed columns (0: whole block rows) */
+    int64_t n_tasks;         /* tasks (= work-groups per column tile; 0: whole block rows) */
+    int64_t n_merges;        /* row tiles split into more than one task */
+    int64_t n_slots;         /* partial-result slots in the workspace */
     int64_t stored_entries;  /* b_row*b_col*nnz_blocks (BCSR) or b_row*P (WCSR) */
     size_t workspace_bytes;  /* bytes of d_workspace spmm_*_run needs */
 } spmm_plan_info_t;
@@ -139,7 +139,10 @@ spmm_status_t spmm_wcsr_split(int64_t n_windows, const int32_t *h_window_row_ptr
 /* BCSR plan.  h_block_row_ptr[ceil(m/b_row)+1] (host, read during the call);
  * d_block_col_idx[nnz_blocks], d_blocks[nnz_blocks*b_row*b_col] (device).
  * Block-column indices are not read on the host; an index whose block lies
- * outside [0, k) contributes nothing (its B rows read as zero). */
+ * outside [0, k) contributes nothing (its B rows read as zero).  Long block rows
+ * may be split into sub-tasks exactly like WCSR windows (same rule, counted in
+ * packed columns = blocks * b_col) and merged in a fixed order; the plan then
+ * needs a workspace.  UNSUPPORTED if nnz_blocks * b_col >= 2^31. */
 spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
                              int32_t b_col, const int32_t *h_block_row_ptr,
                              const int32_t *d_block_col_idx, const void *d_blocks,
@@ -148,8 +151,8 @@ spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
 /* WCSR plan.  h_window_row_ptr[ceil(m/b_row)+1] (host; every window width a
  * multiple of b_col, else BAD_FORMAT); d_window_col_idx[P], d_values[b_row*P]
  * (device).  A column index outside [0, k) (the -1 pads included) reads B as
- * zero.  split_cols: sub-task size T (positive multiple of 32), or 0 to let the
- * plan choose. */
+ * zero.  split_cols: sub-task size T (positive multiple of 32, at most 8192), or
+ * 0 to let the plan choose. */
 spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
                              int32_t b_col, const int32_t *h_window_row_ptr,
                              const int32_t *d_window_col_idx, const void *d_values,

@@ -179,7 +179,7 @@ def test_wcsr_split_invariance_and_determinism(ws):
     p = synth.random_problem(400, 3000, 128, 0.06, seed=5, ab_dtype="fp16", c_dtype="fp32",
                              kind="int", fmt="wcsr", b_row=16, b_col=8)
     ref, _ = oracle.spmm(p.m, p.k, p.N, p.coo_rows(), p.col_idx, p.vals, p.B, "fp16")
-    for T in (32, 64, 160, 1 << 20):
+    for T in (32, 64, 160, 8192):   # 8192: the largest sub-task, no window is cut
         assert np.array_equal(run_gpu(ws, p, split_cols=T), ref), T
     q = synth.random_problem(400, 3000, 128, 0.06, seed=6, ab_dtype="fp16", c_dtype="fp32",
                              fmt="wcsr", b_row=16, b_col=8)

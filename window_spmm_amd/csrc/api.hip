@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <functional>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -22,6 +23,7 @@ struct spmm_plan_s {
     int32_t *d_merges;          // WCSR (window, first_slot, n_slots)
     int64_t n_items;            // block rows (BCSR) or tasks (WCSR)
     int64_t n_merges, n_slots, split_cols;
+    int64_t lds_idx_ints;       // LDS index area of the generic kernel (ints)
     int64_t stored_entries;
     int V, waves_n, waves_k;
     int kernel;                 // 0: generic tile kernel, 1: BCSR 64x64 with LDS-shared A
@@ -222,6 +224,7 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.waves_k = pl->waves_k;
     p.c_dtype = pl->ct;
     p.order = env_int("SPMM_FORCE_ORDER", 0) ? 1 : 0;
+    p.lds_idx_ints = (int32_t)pl->lds_idx_ints;
     hipError_t e = pl->kernel == 1 ? launch_bcsr64_lds(pl->ab, p, st)
                                    : launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, st);
     if (e != hipSuccess)
@@ -248,6 +251,84 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
 
 using namespace wspmm;
 
+namespace wspmm {
+namespace {
+
+// Sub-task size when the caller leaves it to the plan.  If the longest row tile
+// is within 4x the mean width, T covers it (no tile is cut, no merge pass);
+// otherwise T is twice the mean, so only the long tail is cut.  T is a multiple
+// of `align`, at least 512 and at most kMaxSplit.
+constexpr int64_t kMaxSplit = 8192;
+
+int64_t auto_split(int64_t n_rows, const std::function<int64_t(int64_t)> &start, int64_t align)
+{
+    int64_t total = start(n_rows) - start(0), longest = 0;
+    for (int64_t w = 0; w < n_rows; ++w)
+        longest = std::max(longest, start(w + 1) - start(w));
+    const int64_t mean = n_rows > 0 ? ceil_div(total, n_rows) : 0;
+    int64_t T = longest <= 4 * mean ? longest : 2 * mean;
+    T = std::max<int64_t>(512, ceil_div(T, align) * align);
+    T = std::min<int64_t>(T, kMaxSplit);
+    const int64_t forced = env_int("SPMM_FORCE_SPLIT", 0);
+    if (forced > 0 && forced % align == 0 && forced <= kMaxSplit)
+        T = forced;
+    return T;
+}
+
+// Splits the row tiles into tasks (row tile w covers packed columns
+// [start(w), start(w+1))), uploads task and merge tables, sizes the LDS index
+// area (`shift`: log2 of packed columns per index entry) and the workspace.
+spmm_status_t make_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<int64_t(int64_t)> &start,
+                         int64_t split_cols, int shift)
+{
+    try {
+        std::vector<int32_t> tasks, merges;
+        split_tasks(n_rows, start, split_cols, tasks, merges);
+        const int64_t nt = (int64_t)tasks.size() / 4, nm = (int64_t)merges.size() / 3;
+        int64_t slots = 0, max_idx = 0;
+        for (int64_t i = 0; i < nm; ++i)
+            slots += merges[3 * i + 2];
+        for (int64_t i = 0; i < nt; ++i)
+            max_idx = std::max<int64_t>(max_idx, (int64_t)(tasks[4 * i + 2] - tasks[4 * i + 1]) >> shift);
+        pl->n_items = nt;
+        pl->n_merges = nm;
+        pl->n_slots = slots;
+        pl->split_cols = split_cols;
+        // the staging copies whole 256-entry runs; index reads start at most 8 before the end
+        pl->lds_idx_ints = ceil_div(max_idx, 256) * 256 + 256;
+        spmm_status_t s;
+        if ((s = upload(tasks.data(), nt * 4, &pl->d_tasks)) != SPMM_OK ||
+            (s = upload(merges.data(), nm * 3, &pl->d_merges)) != SPMM_OK)
+            return s;
+    } catch (const std::bad_alloc &) {
+        return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+    if (pl->n_merges > 0 && ceil_div((int64_t)pl->b_row * (pl->N / 8), 256) > 65535)
+        return fail(SPMM_ERR_UNSUPPORTED, "N too large for the merge grid");
+    pl->workspace = (size_t)pl->n_slots * (size_t)pl->b_row * (size_t)pl->N * sizeof(float);
+    return SPMM_OK;
+}
+
+spmm_plan_s *new_plan(int fmt, int64_t m, int64_t k, int64_t N, int32_t b_row, int32_t b_col,
+                      spmm_dtype_t ab, spmm_dtype_t ct, const void *d_vals, const int32_t *d_idx,
+                      int dev)
+{
+    spmm_plan_s *pl = new (std::nothrow) spmm_plan_s();
+    if (!pl)
+        return nullptr;
+    pl->fmt = fmt;
+    pl->m = m; pl->k = k; pl->N = N;
+    pl->b_row = b_row; pl->b_col = b_col;
+    pl->ab = ab; pl->ct = ct;
+    pl->A = reinterpret_cast<const uint16_t *>(d_vals);
+    pl->col_idx = d_idx;
+    pl->device = dev;
+    return pl;
+}
+
+}  // namespace
+}  // namespace wspmm
+
 extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
                                         int32_t b_row, int32_t b_col,
                                         const int32_t *h_block_row_ptr,
@@ -260,50 +341,54 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
     if (s != SPMM_OK)
         return s;
     *plan = nullptr;
+    const int64_t nbr = ceil_div(m, b_row);
+    const int64_t nnzb = h_block_row_ptr[nbr];
+    if (nnzb * b_col >= (int64_t(1) << 31))
+        return fail(SPMM_ERR_UNSUPPORTED, "nnz_blocks * b_col must be below 2^31");
     int dev = 0, n_cu = 0;
     if ((s = current_device(&dev, &n_cu)) != SPMM_OK)
         return s;
-    spmm_plan_s *pl = new (std::nothrow) spmm_plan_s();
+    spmm_plan_s *pl = new_plan(0, m, k, N, b_row, b_col, ab_dtype, c_dtype, d_blocks,
+                               d_block_col_idx, dev);
     if (!pl)
         return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
-    const int64_t nbr = ceil_div(m, b_row);
-    pl->fmt = 0;
-    pl->m = m; pl->k = k; pl->N = N;
-    pl->b_row = b_row; pl->b_col = b_col;
-    pl->ab = ab_dtype; pl->ct = c_dtype;
-    pl->A = reinterpret_cast<const uint16_t *>(d_blocks);
-    pl->col_idx = d_block_col_idx;
-    pl->n_items = nbr;
-    pl->stored_entries = (int64_t)h_block_row_ptr[nbr] * b_row * b_col;
-    pl->device = dev;
-    if (pl->n_items > 0x7fffffff) {
-        free_plan(pl);
-        return fail(SPMM_ERR_UNSUPPORTED, "too many block rows");
-    }
+    pl->stored_entries = nnzb * b_row * b_col;
     if ((s = upload(h_block_row_ptr, nbr + 1, &pl->d_row_ptr)) != SPMM_OK) {
         free_plan(pl);
         return s;
     }
-    const double mean_k = nbr > 0 ? (double)h_block_row_ptr[nbr] * b_col / (double)nbr : 0.0;
-    choose_config(pl, mean_k, n_cu);
-    // 64x64 blocks with at least one full 512-column tile: A blocks shared via LDS
+    // 64x64 blocks and at least one full 256-column tile: the kernel that shares
+    // each A block through LDS walks whole block rows
     pl->kernel = env_int("SPMM_FORCE_KERNEL", (b_row == 64 && b_col == 64 && N >= 256) ? 1 : 0);
     if (pl->kernel == 1 && b_row == 64 && b_col == 64) {
         const int nw = env_int("SPMM_FORCE_WAVES_N", 4) == 2 ? 2 : 4;
+        pl->n_items = nbr;
         pl->V = 8;
         pl->waves_n = nw;
         pl->waves_k = 1;
         pl->tile_cols = 128 * nw;
         pl->n_col_tiles = ceil_div(N, pl->tile_cols);
+        pl->workspace = 0;
     } else {
         pl->kernel = 0;
+        const int align = std::max(32, (int)b_col);
+        const auto start = [&](int64_t w) { return (int64_t)h_block_row_ptr[w] * b_col; };
+        const int64_t T = auto_split(nbr, start, align);
+        int shift = 0;
+        while ((1 << shift) < b_col)
+            ++shift;
+        if ((s = make_tasks(pl, nbr, start, T, shift)) != SPMM_OK) {
+            free_plan(pl);
+            return s;
+        }
+        const double mean_task = pl->n_items > 0 ? (double)(nnzb * b_col) / pl->n_items : 0.0;
+        choose_config(pl, mean_task, n_cu);
     }
     if (pl->n_items * pl->n_col_tiles > 0x7fffffff) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
     }
-    pl->workspace = 0;
-    *workspace_bytes = 0;
+    *workspace_bytes = pl->workspace;
     *plan = pl;
     return ok();
 }
@@ -321,77 +406,34 @@ extern "C" spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
     if (s != SPMM_OK)
         return s;
     *plan = nullptr;
-    if (split_cols < 0 || split_cols % 32 != 0)
-        return fail(SPMM_ERR_INVALID_ARGUMENT, "split_cols must be 0 or a positive multiple of 32");
+    if (split_cols < 0 || split_cols % 32 != 0 || split_cols > kMaxSplit)
+        return fail(SPMM_ERR_INVALID_ARGUMENT,
+                    "split_cols must be 0 or a positive multiple of 32 up to %lld",
+                    (long long)kMaxSplit);
     int dev = 0, n_cu = 0;
     if ((s = current_device(&dev, &n_cu)) != SPMM_OK)
         return s;
     const int64_t nw = ceil_div(m, b_row);
     const int64_t P = h_window_row_ptr[nw];
-    if (split_cols == 0) {
-        // Sub-task size: twice the mean window width (at least 512 packed columns),
-        // so only windows well above the mean are cut.
-        const int64_t mean = nw > 0 ? ceil_div(P, nw) : 0;
-        split_cols = std::max<int64_t>(512, ceil_div(2 * mean, 32) * 32);
-        split_cols = env_int("SPMM_FORCE_SPLIT", (int)std::min<int64_t>(split_cols, 1 << 30));
-        if (split_cols <= 0 || split_cols % 32)
-            split_cols = 512;
-    }
-    spmm_plan_s *pl = new (std::nothrow) spmm_plan_s();
+    const auto start = [&](int64_t w) { return (int64_t)h_window_row_ptr[w]; };
+    if (split_cols == 0)
+        split_cols = auto_split(nw, start, 32);
+    spmm_plan_s *pl = new_plan(1, m, k, N, b_row, b_col, ab_dtype, c_dtype, d_values,
+                               d_window_col_idx, dev);
     if (!pl)
         return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
-    pl->fmt = 1;
-    pl->m = m; pl->k = k; pl->N = N;
-    pl->b_row = b_row; pl->b_col = b_col;
-    pl->ab = ab_dtype; pl->ct = c_dtype;
-    pl->A = reinterpret_cast<const uint16_t *>(d_values);
-    pl->col_idx = d_window_col_idx;
-    pl->split_cols = split_cols;
     pl->stored_entries = P * b_row;
-    pl->device = dev;
-    int64_t nt = 0, nm = 0;
-    if ((s = spmm_wcsr_split_count(nw, h_window_row_ptr, split_cols, &nt, &nm)) != SPMM_OK) {
+    if ((s = upload(h_window_row_ptr, nw + 1, &pl->d_row_ptr)) != SPMM_OK ||
+        (s = make_tasks(pl, nw, start, split_cols, 0)) != SPMM_OK) {
         free_plan(pl);
         return s;
     }
-    if (nt > 0x7fffffff) {
-        free_plan(pl);
-        return fail(SPMM_ERR_UNSUPPORTED, "too many tasks");
-    }
-    try {
-        std::vector<int32_t> tasks((size_t)nt * 4), merges((size_t)std::max<int64_t>(nm, 1) * 3);
-        if ((s = spmm_wcsr_split(nw, h_window_row_ptr, split_cols, tasks.data(), merges.data())) !=
-            SPMM_OK) {
-            free_plan(pl);
-            return s;
-        }
-        int64_t slots = 0;
-        for (int64_t i = 0; i < nm; ++i)
-            slots += merges[3 * i + 2];
-        pl->n_items = nt;
-        pl->n_merges = nm;
-        pl->n_slots = slots;
-        if ((s = upload(h_window_row_ptr, nw + 1, &pl->d_row_ptr)) != SPMM_OK ||
-            (s = upload(tasks.data(), nt * 4, &pl->d_tasks)) != SPMM_OK ||
-            (s = upload(merges.data(), nm * 3, &pl->d_merges)) != SPMM_OK) {
-            free_plan(pl);
-            return s;
-        }
-    } catch (const std::bad_alloc &) {
-        free_plan(pl);
-        return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
-    }
-    const double mean_task = nt > 0 ? (double)P / (double)nt : 0.0;
+    const double mean_task = pl->n_items > 0 ? (double)P / (double)pl->n_items : 0.0;
     choose_config(pl, mean_task, n_cu);
     if (pl->n_items * pl->n_col_tiles > 0x7fffffff) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
     }
-    if (nm > 0 && ceil_div((int64_t)b_row * (N / 8), 256) > 65535) {
-        free_plan(pl);
-        return fail(SPMM_ERR_UNSUPPORTED, "N too large for the merge grid");
-    }
-    pl->workspace = (size_t)pl->n_slots * (size_t)b_row * (size_t)N * sizeof(float);
     *workspace_bytes = pl->workspace;
     *plan = pl;
     return ok();
@@ -421,8 +463,8 @@ extern "C" spmm_status_t spmm_plan_info(spmm_plan_t pl, spmm_plan_info_t *info)
     info->waves_k = pl->waves_k;
     info->cols_per_lane = pl->V;
     info->kernel = pl->kernel;
-    info->split_cols = pl->fmt == 1 ? pl->split_cols : 0;
-    info->n_tasks = pl->fmt == 1 ? pl->n_items : 0;
+    info->split_cols = pl->kernel == 0 ? pl->split_cols : 0;
+    info->n_tasks = pl->kernel == 0 ? pl->n_items : 0;
     info->n_merges = pl->n_merges;
     info->n_slots = pl->n_slots;
     info->stored_entries = pl->stored_entries;

@@ -1,6 +1,9 @@
 // Internal helpers shared by the host-side sources of the library.
 #pragma once
 
+#include <functional>
+#include <vector>
+
 #include "window_spmm.h"
 
 namespace wspmm {
@@ -15,5 +18,11 @@ spmm_status_t ok();
 spmm_status_t validate_csr(int64_t m, int64_t k, const int32_t *row_ptr, const int32_t *col_idx);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The window-splitting rule (see spmm_wcsr_split) over any row pointer:
+// start(w) is the first packed column of row tile w, start(n_rows) the end.
+// Appends (tile, begin, end, slot) to tasks and (tile, first_slot, n_slots) to merges.
+void split_tasks(int64_t n_rows, const std::function<int64_t(int64_t)> &start, int64_t split_cols,
+                 std::vector<int32_t> &tasks, std::vector<int32_t> &merges);
 
 }  // namespace wspmm

@@ -3,6 +3,7 @@
 // Section III-C.  Integer work only: values are 16-bit codes copied verbatim.
 #include <algorithm>
 #include <cstring>
+#include <functional>
 #include <new>
 #include <vector>
 
@@ -263,6 +264,32 @@ spmm_status_t check_split_args(int64_t n_windows, const int32_t *wptr, int64_t s
 
 }  // namespace
 
+namespace wspmm {
+
+void split_tasks(int64_t n_rows, const std::function<int64_t(int64_t)> &start, int64_t split_cols,
+                 std::vector<int32_t> &tasks, std::vector<int32_t> &merges)
+{
+    tasks.clear();
+    merges.clear();
+    int64_t slot = 0;
+    for (int64_t w = 0; w < n_rows; ++w) {
+        const int64_t p0 = start(w), p1 = start(w + 1);
+        if (p1 - p0 <= split_cols) {
+            tasks.insert(tasks.end(), {(int32_t)w, (int32_t)p0, (int32_t)p1, -1});
+            continue;
+        }
+        const int64_t parts = ceil_div(p1 - p0, split_cols);
+        merges.insert(merges.end(), {(int32_t)w, (int32_t)slot, (int32_t)parts});
+        for (int64_t q = 0; q < parts; ++q)
+            tasks.insert(tasks.end(), {(int32_t)w, (int32_t)(p0 + q * split_cols),
+                                       (int32_t)std::min(p1, p0 + (q + 1) * split_cols),
+                                       (int32_t)(slot + q)});
+        slot += parts;
+    }
+}
+
+}  // namespace wspmm
+
 extern "C" spmm_status_t spmm_wcsr_split_count(int64_t n_windows, const int32_t *wptr,
                                                int64_t split_cols, int64_t *n_tasks,
                                                int64_t *n_merges)
@@ -296,25 +323,13 @@ extern "C" spmm_status_t spmm_wcsr_split(int64_t n_windows, const int32_t *wptr,
         return s;
     if ((nt > 0 && !tasks) || (nm > 0 && !merges))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "null tasks or merges pointer");
-    int64_t t = 0, mg = 0, slot = 0;
-    for (int64_t w = 0; w < n_windows; ++w) {
-        const int64_t p0 = wptr[w], p1 = wptr[w + 1];
-        if (p1 - p0 <= split_cols) {
-            int32_t *d = tasks + 4 * t++;
-            d[0] = (int32_t)w; d[1] = (int32_t)p0; d[2] = (int32_t)p1; d[3] = -1;
-            continue;
-        }
-        const int64_t parts = ceil_div(p1 - p0, split_cols);
-        int32_t *mrec = merges + 3 * mg++;
-        mrec[0] = (int32_t)w; mrec[1] = (int32_t)slot; mrec[2] = (int32_t)parts;
-        for (int64_t q = 0; q < parts; ++q) {
-            int32_t *d = tasks + 4 * t++;
-            d[0] = (int32_t)w;
-            d[1] = (int32_t)(p0 + q * split_cols);
-            d[2] = (int32_t)std::min(p1, p0 + (q + 1) * split_cols);
-            d[3] = (int32_t)(slot + q);
-        }
-        slot += parts;
+    try {
+        std::vector<int32_t> t, m;
+        split_tasks(n_windows, [wptr](int64_t w) { return (int64_t)wptr[w]; }, split_cols, t, m);
+        std::copy(t.begin(), t.end(), tasks);
+        std::copy(m.begin(), m.end(), merges);
+    } catch (const std::bad_alloc &) {
+        return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
     }
     return ok();
 }

@@ -14,7 +14,8 @@ struct TileParams {
     const uint16_t *A;        // BCSR blocks or WCSR window tiles (16-bit codes)
     const int32_t *col_idx;   // block_col_idx or window_col_idx
     const int32_t *row_ptr;   // block_row_ptr or window_row_ptr (plan-owned copy)
-    const int4 *tasks;        // WCSR task table (window, begin, end, slot); null for BCSR
+    const int4 *tasks;        // tasks (row tile, first packed column, end, slot); the BCSR
+                              // LDS-A kernel walks whole block rows and ignores it
     const uint16_t *B;        // k x N codes, leading dimension ldb
     int64_t ldb;
     void *C;                  // m x N of c_dtype, leading dimension ldc
@@ -31,6 +32,8 @@ struct TileParams {
     int32_t waves_k;          // waves splitting the packed-column reduction
     int32_t c_dtype;          // spmm_dtype_t of C
     int32_t order;            // 0: XCD-contiguous, column-tile major; 1: launch order
+    int32_t lds_idx_ints;     // LDS index area (ints): every task's index count rounded up to
+                              // 256, plus 256
 };
 
 struct MergeParams {
@@ -42,10 +45,10 @@ struct MergeParams {
     int32_t c_dtype;
 };
 
-// LDS bytes the tile kernel needs for its cross-wave reduction.
-size_t tile_lds_bytes(int R, int V, int waves_n, int waves_k);
+// LDS bytes the tile kernel needs (task indices, reused for the cross-wave reduction).
+size_t tile_lds_bytes(int R, int V, int waves_n, int waves_k, int64_t lds_idx_ints);
 
-// fmt: 0 = BCSR (work items = block rows), 1 = WCSR (work items = tasks).
+// fmt: 0 = BCSR, 1 = WCSR; work items are tasks in both (p.n_items of them).
 hipError_t launch_tiles(int fmt, int R, int V, int ab_dtype, const TileParams &p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stream);
 // BCSR with 64x64 blocks, waves_n (2 or 4) waves x 128 columns per work-group, A

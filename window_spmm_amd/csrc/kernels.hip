@@ -67,17 +67,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              kRsrcWord3);
 }
 
-template <int DW>
+// Cache-policy bits of buffer instructions: non-temporal.  (Measured: on the
+// generic kernel's A stream this is slower, the data then bypasses the MALL.)
+constexpr int kNT = 2;
+
+template <int DW, int POL = 0>
 __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *out)
 {
     if constexpr (DW == 4) {
-        u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+        u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POL);
         out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
     } else if constexpr (DW == 2) {
-        u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+        u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, POL);
         out[0] = v[0]; out[1] = v[1];
     } else {
-        out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+        out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, POL);
     }
 }
 
@@ -161,6 +165,15 @@ __device__ __forceinline__ void tile_of(int64_t n_items, int64_t total, int orde
     item = __builtin_amdgcn_readfirstlane((int)(logical - ctile * n_items));
 }
 
+// Waits until this wave's LDS operations are done, then joins the work-group
+// barrier.  Unlike __syncthreads() it does not wait for outstanding global
+// loads, so prefetched B rows stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+    __builtin_amdgcn_s_barrier();
+}
+
 // One pipeline stage: the gathered B rows and the A fragments of one k' step.
 template <int MT, int DW>
 struct Stage {
@@ -168,62 +181,101 @@ struct Stage {
     u32x4_t a[MT];
 };
 
-// Raw B-row index data of one k' step (WCSR: 8 indices, BCSR: 1 block column).
-template <int FMT>
-struct Idx;
-template <>
-struct Idx<0> {
-    uint32_t j;
-};
-template <>
-struct Idx<1> {
-    uint32_t v[8];
-};
+// Steps of B/A loads kept in flight ahead of the MFMAs (odd, so that the ring of
+// D+1 register stages has an even size).  Chosen so that the ring, the
+// accumulators and the addressing state fit about 240 VGPRs: two waves per SIMD.
+template <int R, int V>
+constexpr int pipe_depth()
+{
+    constexpr int acc = (R / 16) * V * 4;
+    constexpr int stage = 8 * (V / 2) + (R / 16) * 4;
+    constexpr int ring = (200 - acc) / stage;  // stages that fit
+    return ring >= 4 ? 3 : 1;
+}
 
+// Generic tile kernel: one work-group per (task, column tile).  A task is a row
+// tile (a BCSR block row or a WCSR window) and a range [kb0, kb1) of its packed
+// columns; tasks that cover part of a row tile write an fp32 partial slot.
+//   * The task's B-row indices (WCSR column indices, or BCSR block columns) are
+//     copied into LDS once, so the main loop never waits on an index load queued
+//     behind in-flight B loads.
+//   * Each wave keeps D steps of A/B loads in flight in a ring of D+1 register
+//     stages; all loads are issued unconditionally (steps past the end read
+//     zeros), so the wait-count bookkeeping is the same on every path.
 template <int FMT, int R, int V, int AB>
 __global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
 {
     constexpr int MT = R / 16;  // 16-row MFMA tiles per work-group tile
     constexpr int DW = V / 2;   // dwords of one gathered row segment per lane
+    constexpr int D = pipe_depth<R, V>();
+    constexpr int Q = D + 1;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    int32_t *lidx = reinterpret_cast<int32_t *>(smem);
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave % p.waves_n;
     const int wk = wave / p.waves_n;
     const int g = lane >> 4;
     const int li = lane & 15;
+    const int nthreads = 64 * p.waves_n * p.waves_k;
 
     int64_t item, ctile;
     tile_of(p.n_items, p.n_items * p.n_col_tiles, p.order, item, ctile);
 
-    // ---- work item: rows, packed-column range, A/index resources ----------
-    int64_t row0, kbegin, kend;
-    int32_t slot = -1;
-    __amdgpu_buffer_rsrc_t rA, rI;
-    uint32_t a_row_stride;  // bytes between rows of A inside the work item
+    // ---- task: row tile, packed-column range, A / index sources ------------
+    const int4 t = p.tasks[item];
+    const int64_t tile = t.x;
+    const int32_t slot = t.w;
+    const int64_t row0 = tile * R;
+    const uint32_t klen = (uint32_t)(t.z - t.y);  // packed columns of the task
+    const int64_t base = p.row_ptr[tile];
+    const int64_t width = p.row_ptr[tile + 1] - base;  // WCSR window width
+    const int32_t *gidx;
+    uint32_t n_idx;              // index entries of the task
+    __amdgpu_buffer_rsrc_t rA;
+    uint32_t a_row_stride;       // bytes between A rows
+    uint32_t a_col0;             // bytes to the task's first packed column in a row
     if constexpr (FMT == 0) {
-        const int64_t blk0 = p.row_ptr[item];
-        const int64_t nblk = p.row_ptr[item + 1] - blk0;
-        row0 = item * R;
-        kbegin = 0;
-        kend = nblk * p.b_col;
-        rA = make_rsrc(p.A + blk0 * R * p.b_col, (uint32_t)(nblk * R * p.b_col * 2));
-        rI = make_rsrc(p.col_idx + blk0, (uint32_t)(nblk * 4));
+        const int64_t blk0 = (int64_t)t.y >> p.log2_b_col;  // first block of the task
+                                                             // (t.y counts from block 0)
+        n_idx = klen >> p.log2_b_col;
+        gidx = p.col_idx + blk0;
+        rA = make_rsrc(p.A + blk0 * R * p.b_col, (uint32_t)((int64_t)n_idx * R * p.b_col * 2));
         a_row_stride = (uint32_t)p.b_col * 2;
+        a_col0 = 0;
     } else {
-        const int4 t = p.tasks[item];
-        const int64_t w = t.x;
-        const int64_t wbase = p.row_ptr[w];
-        const int64_t W = p.row_ptr[w + 1] - wbase;
-        row0 = w * R;
-        kbegin = t.y;
-        kend = t.z;
-        slot = t.w;
-        rA = make_rsrc(p.A + R * wbase, (uint32_t)(R * W * 2));
-        rI = make_rsrc(p.col_idx + kbegin, (uint32_t)((kend - kbegin) * 4));
-        a_row_stride = (uint32_t)W * 2;
-        kbegin -= wbase;  // from here on k' counts from the window start
-        kend -= wbase;
+        n_idx = klen;
+        gidx = p.col_idx + t.y;
+        rA = make_rsrc(p.A + R * base, (uint32_t)(R * width * 2));
+        a_row_stride = (uint32_t)width * 2;
+        a_col0 = (uint32_t)(t.y - base) * 2;
     }
+
+    // ---- stage the task's indices in LDS (one burst per task) --------------
+    // Direct-to-LDS buffer loads: each wave instruction fills a contiguous LDS run
+    // (lane i -> bytes 16i or 4i); no VGPRs, one wait for the whole burst.
+    {
+        typedef __attribute__((address_space(3))) void lds_void;
+        const __amdgpu_buffer_rsrc_t rI = make_rsrc(gidx, n_idx * 4);
+        const int nwaves = p.waves_n * p.waves_k;
+        if constexpr (FMT == 1) {
+            // window column indices: n_idx is a multiple of 8, 16 bytes per lane
+            for (int c = wave; c * 256 < (int)n_idx; c += nwaves)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rI, (lds_void *)(lidx + c * 256), 16,
+                                                         (unsigned)((c * 64 + lane) * 16), 0, 0, 0);
+        } else {
+            // block columns: any count, 4 bytes per lane
+            for (int c = wave; c * 64 < (int)n_idx; c += nwaves)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rI, (lds_void *)(lidx + c * 64), 4,
+                                                         (unsigned)((c * 64 + lane) * 4), 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+        lds_barrier();
+    }
+    // last valid start of an index read (reads past the task are masked anyway)
+    const uint32_t idx_cap = (uint32_t)(p.lds_idx_ints > 8 ? p.lds_idx_ints - 8 : 0);
+
     // B resource starts at this wave's first column; rows are ldb apart.
     const int64_t col0 = ctile * p.tile_cols + wn * 16 * V;
     const uint64_t b_skip = (uint64_t)col0 * 2;
@@ -233,13 +285,11 @@ __global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
     const uint32_t lane_col_bytes = (uint32_t)li * V * 2;
     const uint32_t k32 = (uint32_t)p.k;
     const uint32_t nbc = (uint32_t)((p.k + p.b_col - 1) >> p.log2_b_col);  // block columns
-    const int64_t kspan = kend - kbegin - 32 * wk;
-    const int nsteps = kspan > 0 ? (int)((kspan + 32 * p.waves_k - 1) / (32 * p.waves_k)) : 0;
-    // first k' of this lane at step s: kfirst + s * kstride (relative to the item start)
-    const uint32_t kfirst = (uint32_t)(kbegin + 32 * wk + 8 * g);
+    const int kspan = (int)klen - 32 * wk;
+    const int nsteps = kspan > 0 ? (kspan + 32 * p.waves_k - 1) / (32 * p.waves_k) : 0;
+    // this lane's first packed column (task-relative) at step s: kfirst + s * kstride
+    const uint32_t kfirst = 32u * wk + 8u * g;
     const uint32_t kstride = 32u * p.waves_k;
-    const uint32_t klimit = (uint32_t)kend;
-    const uint32_t idx_base = (uint32_t)kbegin;  // WCSR index resource starts here
 
     f32x4_t acc[MT][V];
 #pragma unroll
@@ -248,50 +298,40 @@ __global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
         for (int c = 0; c < V; ++c)
             acc[mt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Loaded registers are never modified before use: validity of a step is
-    // recomputed where the data is consumed, so no load forces an early wait.
-    auto load_idx = [&](int s, Idx<FMT> &ix) {
-        const uint32_t kg = kfirst + (uint32_t)s * kstride;
-        const bool ok = kg < klimit;
-        if constexpr (FMT == 0) {
-            buf_load<1>(rI, ok ? (kg >> p.log2_b_col) * 4u : kOOB, &ix.j);
-        } else {
-            const uint32_t off = ok ? (kg - idx_base) * 4u : kOOB;
-            buf_load<4>(rI, off, ix.v);
-            buf_load<4>(rI, off + 16u, ix.v + 4);
-        }
-    };
-
-    auto issue = [&](int s, const Idx<FMT> &ix, Stage<MT, DW> &st) {
-        const uint32_t kg = kfirst + (uint32_t)s * kstride;
-        const bool ok = kg < klimit;
+    // Issues the A and B loads of step s into st.
+    auto issue = [&](int s, Stage<MT, DW> &st) {
+        const uint32_t kl = kfirst + (uint32_t)s * kstride;  // task-relative packed column
+        const bool ok = kl < klen;
         uint32_t a_off;
         if constexpr (FMT == 0) {
-            const uint32_t q = kg >> p.log2_b_col;
-            const uint32_t kk = kg & (uint32_t)(p.b_col - 1);
-            const bool jv = ok & (ix.j < nbc);
-            const uint32_t r0 = (jv ? ix.j : 0u) * (uint32_t)p.b_col + kk;
+            const uint32_t q = kl >> p.log2_b_col;
+            const uint32_t kk = kl & (uint32_t)(p.b_col - 1);
+            const uint32_t J = (uint32_t)lidx[q < idx_cap ? q : idx_cap];  // in-bounds read
+            const bool jv = ok & (J < nbc);
+            const uint32_t r0 = (jv ? J : 0u) * (uint32_t)p.b_col + kk;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t r = r0 + j;
-                const bool rv = jv & (r < k32);
-                buf_load<DW>(rB, rv ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
+                buf_load<DW>(rB, (jv & (r < k32)) ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
             }
             a_off = ((q * R + li) * (uint32_t)p.b_col + kk) * 2u;
         } else {
+            const uint32_t kr = kl < idx_cap ? kl : idx_cap;  // in-bounds LDS read
+            const u32x4_t i0 = *reinterpret_cast<const u32x4_t *>(lidx + kr);
+            const u32x4_t i1 = *reinterpret_cast<const u32x4_t *>(lidx + kr + 4);
+            const uint32_t ix[8] = {i0[0], i0[1], i0[2], i0[3], i1[0], i1[1], i1[2], i1[3]};
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const uint32_t r = ix.v[j];
-                const uint32_t off = r * ldb2 + lane_col_bytes;
-                buf_load<DW>(rB, (ok & (r < k32)) ? off : kOOB, st.b[j]);
+                const uint32_t r = ix[j];
+                buf_load<DW>(rB, (ok & (r < k32)) ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
             }
-            a_off = li * a_row_stride + kg * 2u;
+            a_off = li * a_row_stride + a_col0 + kl * 2u;
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            uint32_t t[4];
-            buf_load<4>(rA, ok ? a_off + (uint32_t)(mt * 16) * a_row_stride : kOOB, t);
-            st.a[mt] = u32x4_t{t[0], t[1], t[2], t[3]};
+            uint32_t w[4];
+            buf_load<4>(rA, ok ? a_off + (uint32_t)(mt * 16) * a_row_stride : kOOB, w);
+            st.a[mt] = u32x4_t{w[0], w[1], w[2], w[3]};
         }
     };
 
@@ -309,44 +349,29 @@ __global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
         }
     };
 
-    // ---- two-stage pipeline over the k' steps (nsteps is wave-uniform) ----
-    // Loads are issued unconditionally (a step past the end reads zeros), so the
-    // wait-count bookkeeping sees the same outstanding loads on every path.
+    // ---- D-deep pipeline over the k' steps (nsteps is wave-uniform) --------
     if (nsteps > 0) {
-        Idx<FMT> ix0, ix1;
-        Stage<MT, DW> st0, st1;
-        load_idx(0, ix0);
-        load_idx(1, ix1);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(0, ix0, st0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_idx(2, ix0);
-        __builtin_amdgcn_sched_barrier(0);
-        // invariant at the top: st0 = data of step s, ix1 = indices of s+1, ix0 of s+2
-        // (sched_barrier keeps the compiler from sinking the prefetches below
-        // the MFMAs, which would serialise loads and compute again)
-        int s = 0;
-        for (; s + 1 < nsteps; s += 2) {
-            issue(s + 1, ix1, st1);
-            load_idx(s + 3, ix1);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(st0);
-            __builtin_amdgcn_sched_barrier(0);
-            issue(s + 2, ix0, st0);
-            load_idx(s + 4, ix0);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(st1);
-            __builtin_amdgcn_sched_barrier(0);
+        Stage<MT, DW> st[Q];
+#pragma unroll
+        for (int u = 0; u < D; ++u)
+            issue(u, st[u]);
+        for (int s = 0; s < nsteps; s += Q) {
+#pragma unroll
+            for (int u = 0; u < Q; ++u) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue(s + u + D, st[(u + D) % Q]);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(st[u]);  // steps past the end hold zeros: no branch in the ring
+            }
         }
-        if (s < nsteps)
-            compute(st0);
     }
 
     // ---- fixed-order sum of the waves_k partial tiles through LDS ----
     if (p.waves_k > 1) {
-        extern __shared__ float red[];  // [waves_n][MT*V*4][64]
         constexpr int NR = MT * V * 4;
+        float *red = reinterpret_cast<float *>(smem);  // [waves_n][NR][64], reuses the index area
         float *mine = red + (int64_t)wn * NR * 64 + lane;
+        lds_barrier();  // every wave is done reading indices
         for (int s = p.waves_k - 1; s >= 1; --s) {
             if (wk == s) {
 #pragma unroll
@@ -357,7 +382,7 @@ __global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
                         for (int q = 0; q < 4; ++q)
                             mine[((mt * V + c) * 4 + q) * 64] = acc[mt][c][q];
             }
-            __syncthreads();
+            lds_barrier();
             if (wk == 0) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
@@ -367,7 +392,7 @@ __global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
                         for (int q = 0; q < 4; ++q)
                             acc[mt][c][q] += mine[((mt * V + c) * 4 + q) * 64];
             }
-            __syncthreads();
+            lds_barrier();
         }
         if (wk != 0)
             return;
@@ -393,15 +418,6 @@ __global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
             }
         }
     }
-}
-
-// Waits until this wave's LDS operations are done, then joins the work-group
-// barrier.  Unlike __syncthreads() it does not wait for outstanding global
-// loads, so prefetched B rows stay in flight across the barrier.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
-    __builtin_amdgcn_s_barrier();
 }
 
 // BCSR with 64 x 64 blocks and a wide column tile (NW waves x 128 columns).
@@ -455,7 +471,7 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
         for (int t = 0; t < CPT; ++t) {
             const int c = threadIdx.x + t * NT;
             r[t] = __builtin_amdgcn_raw_buffer_load_b128(
-                rA, (int)(((uint32_t)q * R * BC + (uint32_t)c * 8) * 2), 0, 2 /* nt */);
+                rA, (int)(((uint32_t)q * R * BC + (uint32_t)c * 8) * 2), 0, kNT);
         }
     };
     auto store_a = [&](int buf, const u32x4_t (&r)[CPT]) {
@@ -610,9 +626,11 @@ static hipError_t by_r(int r, int v, int ab, const TileParams &p, dim3 g, dim3 b
     }
 }
 
-size_t tile_lds_bytes(int R, int V, int waves_n, int waves_k)
+size_t tile_lds_bytes(int R, int V, int waves_n, int waves_k, int64_t lds_idx_ints)
 {
-    return waves_k > 1 ? (size_t)waves_n * (R / 16) * V * 4 * 64 * sizeof(float) : 0;
+    const size_t red = waves_k > 1 ? (size_t)waves_n * (R / 16) * V * 4 * 64 * sizeof(float) : 0;
+    const size_t idx = (size_t)lds_idx_ints * sizeof(int32_t);
+    return red > idx ? red : idx;
 }
 
 template <int NW>
@@ -640,7 +658,7 @@ hipError_t launch_tiles(int fmt, int R, int V, int ab, const TileParams &p, hipS
 {
     dim3 grid((unsigned)(p.n_items * p.n_col_tiles));
     dim3 block(64 * p.waves_n * p.waves_k);
-    size_t lds = tile_lds_bytes(R, V, p.waves_n, p.waves_k);
+    size_t lds = tile_lds_bytes(R, V, p.waves_n, p.waves_k, p.lds_idx_ints);
     return fmt == 0 ? by_r<0>(R, V, ab, p, grid, block, lds, stream)
                     : by_r<1>(R, V, ab, p, grid, block, lds, stream);
 }
