@@ -188,6 +188,29 @@ def test_wcsr_split_invariance_and_determinism(ws):
     check(q, outs[0])
 
 
+@pytest.mark.parametrize("source", ["lists", "spread"])
+@pytest.mark.parametrize("fmt", ["wcsr", "bcsr"])
+def test_work_sources_repeated_launches(ws, fmt, source, monkeypatch):
+    """Both ways of handing tasks to the work-groups (a list of several tasks
+    per persistent work-group, or one task per work-group left to the hardware
+    dispatcher) give the oracle's result and the same bits on every one of
+    many launches of one plan."""
+    monkeypatch.setenv("SPMM_FORCE_SPREAD", "1" if source == "spread" else "0")
+    if fmt == "wcsr":
+        p = synth.random_problem(1500, 5000, 136, 0.03, seed=21, ab_dtype="fp16", c_dtype="fp32",
+                                 fmt="wcsr", b_row=16, b_col=8)
+        split = 96
+    else:
+        p = synth.random_problem(1300, 1100, 72, 0.02, seed=22, ab_dtype="bf16", c_dtype="bf16",
+                                 fmt="bcsr", b_row=32, b_col=16)
+        split = 0
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, split_cols=split)
+    outs = run_gpu(ws, p, A=A, repeats=12)
+    assert all(np.array_equal(o, outs[0]) for o in outs[1:])
+    check(p, outs[0])
+
+
 def test_bcsr_deterministic(ws):
     p = synth.block_problem(640, 640, 256, 64, 64, 0.3, seed=9, ab_dtype="bf16", c_dtype="fp32")
     outs = run_gpu(ws, p, repeats=10)

@@ -6,6 +6,7 @@
 #include <functional>
 #include <cstring>
 #include <new>
+#include <queue>
 #include <vector>
 
 #include "common.h"
@@ -19,11 +20,18 @@ struct spmm_plan_s {
     const uint16_t *A;
     const int32_t *col_idx;
     int32_t *d_row_ptr;         // plan-owned copy of the block / window row pointer
-    int32_t *d_tasks;           // WCSR (window, begin, end, slot)
-    int32_t *d_merges;          // WCSR (window, first_slot, n_slots)
-    int64_t n_items;            // block rows (BCSR) or tasks (WCSR)
+    int32_t *d_tasks;           // work-item descriptors, 8 ints each (TileParams::tasks)
+    int32_t *d_lists;           // per-work-group ranges of d_tasks (TileParams::lists)
+    bool two_buffers;           // work-groups run several entries (TileParams::two_buffers)
+    int64_t n_entries;          // entries of d_tasks
+    int32_t *d_merges;          // (row tile, first_slot, n_slots)
+    int64_t n_items;            // work items per column tile: block rows (LDS kernel)
+                                // or task-table entries, padding included (tile kernel)
+    int64_t n_tasks;            // tasks without the padding
+    int order;                  // work-group -> item mapping (TileParams::order)
     int64_t n_merges, n_slots, split_cols;
-    int64_t lds_idx_ints;       // LDS index area of the generic kernel (ints)
+    int64_t lds_idx_ints;       // ints of each LDS index buffer of the generic kernel
+    int64_t grid;               // persistent work-groups of the generic kernel
     int64_t stored_entries;
     int V, waves_n, waves_k;
     int kernel;                 // 0: generic tile kernel, 1: BCSR 64x64 with LDS-shared A
@@ -51,7 +59,7 @@ spmm_status_t hip_fail(hipError_t e, const char *what)
 }
 
 // The library only runs on gfx950; find out whether the current device is one.
-spmm_status_t current_device(int *dev, int *n_cu)
+spmm_status_t current_device(int *dev, int *n_cu, int64_t *lds_per_cu, int64_t *l2_bytes)
 {
     int count = 0;
     hipError_t e = hipGetDeviceCount(&count);
@@ -66,6 +74,8 @@ spmm_status_t current_device(int *dev, int *n_cu)
         return fail(SPMM_ERR_HIP, "device %d is %s, this library is built for gfx950", *dev,
                     prop.gcnArchName);
     *n_cu = prop.multiProcessorCount;
+    *lds_per_cu = (int64_t)prop.maxSharedMemoryPerMultiProcessor;
+    *l2_bytes = (int64_t)prop.l2CacheSize;
     return SPMM_OK;
 }
 
@@ -117,6 +127,9 @@ void choose_config(spmm_plan_s *pl, double mean_kprime, int n_cu)
     V = env_int("SPMM_FORCE_V", V);
     if (V != 2 && V != 4 && V != 8)
         V = 8;
+    if (pl->b_row >= 32 && V > 4)
+        V = 4;  // taller tiles: the accumulators at V = 8 leave no room for the ring
+                // (the kernel has no such instantiation)
     const int64_t wave_cols = 16 * V;
     const int64_t col_waves = ceil_div(pl->N, wave_cols);
     int wn = (pl->b_row == 64 && col_waves >= 2) ? 2 : 1;
@@ -159,6 +172,7 @@ void free_plan(spmm_plan_s *pl)
         return;
     if (pl->d_row_ptr) (void)hipFree(pl->d_row_ptr);
     if (pl->d_tasks) (void)hipFree(pl->d_tasks);
+    if (pl->d_lists) (void)hipFree(pl->d_lists);
     if (pl->d_merges) (void)hipFree(pl->d_merges);
     delete pl;
 }
@@ -178,6 +192,8 @@ spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int
         return fail(SPMM_ERR_UNSUPPORTED, "ldb/ldc must be >= N and multiples of 8");
     if ((uint64_t)pl->k * (uint64_t)ldb * 2u >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "B (k * ldb * 2 bytes) must be smaller than 4 GiB - 256");
+    if (pl->kernel == 0 && (uint64_t)pl->b_row * (uint64_t)ldc * (pl->ct == SPMM_FP32 ? 4u : 2u) >= kMaxBBytes)
+        return fail(SPMM_ERR_UNSUPPORTED, "b_row rows of C (b_row * ldc * element bytes) must be below 4 GiB");
     if (pl->workspace > 0 && (!ws || ((uintptr_t)ws & 15)))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "plan needs a 16-byte aligned workspace of %zu bytes",
                     pl->workspace);
@@ -203,7 +219,10 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.A = pl->A;
     p.col_idx = pl->col_idx;
     p.row_ptr = pl->d_row_ptr;
-    p.tasks = reinterpret_cast<const int4 *>(pl->d_tasks);
+    p.tasks = pl->d_tasks;
+    p.lists = pl->d_lists;
+    p.two_buffers = pl->two_buffers ? 1 : 0;
+    p.n_entries = pl->n_entries;
     p.B = reinterpret_cast<const uint16_t *>(B);
     p.ldb = ldb;
     p.C = C;
@@ -223,8 +242,9 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.waves_n = pl->waves_n;
     p.waves_k = pl->waves_k;
     p.c_dtype = pl->ct;
-    p.order = env_int("SPMM_FORCE_ORDER", 0) ? 1 : 0;
+    p.order = pl->order;
     p.lds_idx_ints = (int32_t)pl->lds_idx_ints;
+    p.grid = pl->grid;
     hipError_t e = pl->kernel == 1 ? launch_bcsr64_lds(pl->ab, p, st)
                                    : launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, st);
     if (e != hipSuccess)
@@ -254,19 +274,23 @@ using namespace wspmm;
 namespace wspmm {
 namespace {
 
-// Sub-task size when the caller leaves it to the plan.  If the longest row tile
-// is within 4x the mean width, T covers it (no tile is cut, no merge pass);
-// otherwise T is twice the mean, so only the long tail is cut.  T is a multiple
-// of `align`, at least 512 and at most kMaxSplit.
+// Sub-task size when the caller leaves it to the plan.  `slots` work-groups of
+// the tile kernel are resident at once.  If no row tile is longer than the
+// total work divided by the slots, T covers the longest one (nothing is cut, no
+// merge pass); otherwise T is that quotient, so that no task outlasts the
+// average work of a slot.  T is a multiple of `align`, at least 512 and at
+// most kMaxSplit.
 constexpr int64_t kMaxSplit = 8192;
 
-int64_t auto_split(int64_t n_rows, const std::function<int64_t(int64_t)> &start, int64_t align)
+int64_t auto_split(int64_t n_rows, const std::function<int64_t(int64_t)> &start, int64_t align,
+                   int64_t slots)
 {
-    int64_t total = start(n_rows) - start(0), longest = 0;
+    const int64_t total = start(n_rows) - start(0);
+    int64_t longest = 0;
     for (int64_t w = 0; w < n_rows; ++w)
         longest = std::max(longest, start(w + 1) - start(w));
-    const int64_t mean = n_rows > 0 ? ceil_div(total, n_rows) : 0;
-    int64_t T = longest <= 4 * mean ? longest : 2 * mean;
+    const int64_t share = ceil_div(total, std::max<int64_t>(1, slots));
+    int64_t T = longest <= share ? longest : share;
     T = std::max<int64_t>(512, ceil_div(T, align) * align);
     T = std::min<int64_t>(T, kMaxSplit);
     const int64_t forced = env_int("SPMM_FORCE_SPLIT", 0);
@@ -275,11 +299,32 @@ int64_t auto_split(int64_t n_rows, const std::function<int64_t(int64_t)> &start,
     return T;
 }
 
+// Work of an item for the assignment: its packed columns plus a fixed share
+// for the per-task start-up and finish.
+constexpr int64_t kTaskOverhead = 512;
+// Work-groups g and g + n_cu share a CU (dispatch fills every CU once before
+// any twice).  Where two share a SIMD the waves of the later one issue after
+// those of the earlier one; measured on the WCSR and BCSR workloads, the later
+// work-group then progresses about 1.6 to 1.8 times slower, so the assignment
+// charges its work at this factor (in tenths).
+constexpr int64_t kLateSlotCost10 = 16;
+// Items per resident work-group from which every item gets a work-group of its
+// own and the hardware dispatcher balances the load (the real cost of a task
+// also depends on how its B rows hit the caches, which a static plan does not
+// see; with few items per work-group the static plan, whose work-groups
+// overlap one task's start with the previous task, is better).
+constexpr int64_t kSpreadItems = 6;
+
 // Splits the row tiles into tasks (row tile w covers packed columns
-// [start(w), start(w+1))), uploads task and merge tables, sizes the LDS index
-// area (`shift`: log2 of packed columns per index entry) and the workspace.
+// [start(w), start(w+1))), sizes the two LDS index buffers (`shift`: log2 of
+// packed columns per index entry; they also hold the cross-wave reduction) and
+// the workspace, sets the persistent grid, and assigns the work items (task,
+// column tile) to the work-groups: longest first, each to the least loaded
+// work-group (ties: lowest index), a work-group running its items in the order
+// they were assigned.  Uploads the descriptor table (work-group major), the
+// per-work-group ranges and the merge table.
 spmm_status_t make_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<int64_t(int64_t)> &start,
-                         int64_t split_cols, int shift)
+                         int64_t split_cols, int shift, int n_cu, bool spread, bool local)
 {
     try {
         std::vector<int32_t> tasks, merges;
@@ -290,14 +335,102 @@ spmm_status_t make_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
             slots += merges[3 * i + 2];
         for (int64_t i = 0; i < nt; ++i)
             max_idx = std::max<int64_t>(max_idx, (int64_t)(tasks[4 * i + 2] - tasks[4 * i + 1]) >> shift);
+        pl->n_tasks = nt;
         pl->n_items = nt;
         pl->n_merges = nm;
         pl->n_slots = slots;
         pl->split_cols = split_cols;
-        // the staging copies whole 256-entry runs; index reads start at most 8 before the end
+        // index copies write whole 256-int runs; reads start at most 8 before the end
         pl->lds_idx_ints = ceil_div(max_idx, 256) * 256 + 256;
+        pl->two_buffers = !spread;
+        const size_t lds = tile_lds_bytes(pl->lds_idx_ints, pl->b_row, pl->V, pl->waves_n, pl->waves_k,
+                                          pl->two_buffers);
+        const int per_cu = tiles_blocks_per_cu(pl->fmt, pl->b_row, pl->V, pl->ab,
+                                               64 * pl->waves_n * pl->waves_k, lds);
+        if (per_cu < 1)
+            return fail(SPMM_ERR_HIP, "tile kernel cannot be resident (LDS %zu bytes)", lds);
+        const int64_t n_work = nt * pl->n_col_tiles;
+        // spread: one work-group per item, in longest-first order
+        const int64_t G = spread ? std::max<int64_t>(1, n_work)
+                                 : std::max<int64_t>(1, std::min<int64_t>(n_work, (int64_t)n_cu * per_cu));
+
+        // Greedy longest-first assignment.  Work-group g runs on XCD g mod 8
+        // (dispatch is round-robin over the XCDs), so with several column
+        // tiles the items of one column tile go to the work-groups of a fixed
+        // subset of XCDs: each XCD's L2 then holds only its column slices of B.
+        const int64_t n_ct = pl->n_col_tiles;
+        const int64_t groups =
+            (n_ct > 1 && n_ct <= 8 && 8 % n_ct == 0) ? n_ct : (n_ct > 8 && n_ct % 8 == 0) ? 8 : 1;
+        const int64_t xcd_groups = env_int("SPMM_FORCE_XCD_GROUPS", 1) ? groups : 1;
+        std::vector<int64_t> order(n_work);
+        for (int64_t i = 0; i < n_work; ++i)
+            order[i] = i;
+        const auto cost = [&](int64_t item) {
+            const int64_t t = item % std::max<int64_t>(1, nt);
+            return (int64_t)tasks[4 * t + 2] - tasks[4 * t + 1] + kTaskOverhead;
+        };
+        if (spread && local) {
+            // Row order, each XCD a contiguous range (work-group g runs on XCD
+            // g mod 8): B is much larger than an L2, and neighbouring row tiles
+            // of banded patterns gather the same B rows.
+            const int64_t q = n_work / 8, rem = n_work % 8;
+            for (int64_t g = 0; g < n_work; ++g) {
+                const int64_t x = g % 8, l = g / 8;
+                order[g] = x * q + std::min(x, rem) + l;
+            }
+        } else {
+            std::stable_sort(order.begin(), order.end(),
+                             [&](int64_t a, int64_t b) { return cost(a) > cost(b); });
+        }
+        // SIMD-sharing level of work-group g: 0 for the first waves on each SIMD
+        const int waves_wg = pl->waves_n * pl->waves_k;
+        const int64_t late10 = env_int("SPMM_FORCE_SLOT_COST10", (int)kLateSlotCost10);
+        const auto weight10 = [&](int64_t g) -> int64_t {
+            return ((g / n_cu) * waves_wg) / 4 > 0 ? late10 : 10;
+        };
+        typedef std::pair<int64_t, int64_t> load_t;  // (load in tenths, work-group)
+        typedef std::priority_queue<load_t, std::vector<load_t>, std::greater<load_t>> heap_t;
+        std::vector<heap_t> heap(xcd_groups);
+        for (int64_t g = 0; g < G; ++g)
+            heap[(g % 8) % xcd_groups].push({0, g});
+        for (auto &h : heap)
+            if (h.empty())
+                return fail(SPMM_ERR_UNSUPPORTED, "grid of %lld work-groups too small", (long long)G);
+        std::vector<int64_t> owner(n_work), count(G + 1, 0);
+        for (int64_t i = 0; i < n_work; ++i) {
+            if (spread) {
+                owner[i] = i;
+                ++count[i + 1];
+                continue;
+            }
+            heap_t &h = heap[(order[i] / std::max<int64_t>(1, nt)) % xcd_groups];
+            load_t l = h.top();
+            h.pop();
+            owner[i] = l.second;
+            ++count[l.second + 1];
+            h.push({l.first + cost(order[i]) * weight10(l.second), l.second});
+        }
+        std::vector<int32_t> lists(G + 1, 0);
+        for (int64_t g = 0; g < G; ++g)
+            lists[g + 1] = (int32_t)(lists[g] + count[g + 1]);
+        std::vector<int32_t> fill(lists.begin(), lists.end() - 1);
+        std::vector<int32_t> desc(8 * n_work, 0);
+        for (int64_t i = 0; i < n_work; ++i) {
+            const int64_t item = order[i], t = item % nt;
+            const int32_t *src = &tasks[4 * t];
+            int32_t *d = &desc[8 * (int64_t)fill[owner[i]]++];
+            std::copy_n(src, 4, d);
+            if (pl->fmt == 1) {
+                d[4] = (int32_t)start(src[0]);
+                d[5] = (int32_t)(start(src[0] + 1) - start(src[0]));
+            }
+            d[6] = (int32_t)(item / nt);  // column tile
+        }
+        pl->grid = G;
+        pl->n_entries = n_work;
         spmm_status_t s;
-        if ((s = upload(tasks.data(), nt * 4, &pl->d_tasks)) != SPMM_OK ||
+        if ((s = upload(desc.data(), n_work * 8, &pl->d_tasks)) != SPMM_OK ||
+            (s = upload(lists.data(), G + 1, &pl->d_lists)) != SPMM_OK ||
             (s = upload(merges.data(), nm * 3, &pl->d_merges)) != SPMM_OK)
             return s;
     } catch (const std::bad_alloc &) {
@@ -305,8 +438,80 @@ spmm_status_t make_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
     }
     if (pl->n_merges > 0 && ceil_div((int64_t)pl->b_row * (pl->N / 8), 256) > 65535)
         return fail(SPMM_ERR_UNSUPPORTED, "N too large for the merge grid");
+    if (pl->n_merges > 0 && (uint64_t)pl->b_row * (uint64_t)pl->N * 4u >= kMaxBBytes)
+        return fail(SPMM_ERR_UNSUPPORTED, "b_row * N * 4 bytes of a partial tile must be below 4 GiB");
     pl->workspace = (size_t)pl->n_slots * (size_t)pl->b_row * (size_t)pl->N * sizeof(float);
     return SPMM_OK;
+}
+
+// Whether the pattern is banded: the median column span (last minus first
+// column) of up to 64 row tiles spread over the matrix is below k/8.  Reads
+// the first index and the last b_col indices (WCSR pads with -1 at the end) of
+// each sampled tile from the device.  `ptr` is the host row pointer, `idx` the
+// device index array, `unit` the columns per index (b_col for BCSR, 1 for WCSR).
+bool banded_pattern(int64_t n_rows, const int32_t *ptr, const int32_t *idx, int64_t unit, int64_t k,
+                    int64_t tail)
+{
+    std::vector<int64_t> spans;
+    const int64_t samples = std::min<int64_t>(64, n_rows);
+    for (int64_t i = 0; i < samples; ++i) {
+        const int64_t w = (2 * i + 1) * n_rows / (2 * samples);
+        const int64_t a = ptr[w], b = ptr[w + 1];
+        if (b <= a)
+            continue;
+        int32_t lo = 0;
+        std::vector<int32_t> hi((size_t)std::min<int64_t>(tail, b - a));
+        if (hipMemcpy(&lo, idx + a, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(hi.data(), idx + b - (int64_t)hi.size(), hi.size() * sizeof(int32_t),
+                      hipMemcpyDeviceToHost) != hipSuccess)
+            return false;
+        int32_t top = lo;
+        for (int32_t v : hi)
+            top = std::max(top, v);
+        spans.push_back((int64_t)(top - lo) * unit);
+    }
+    if (spans.empty())
+        return false;
+    std::nth_element(spans.begin(), spans.begin() + spans.size() / 2, spans.end());
+    return spans[spans.size() / 2] * 8 < k;
+}
+
+// Tile shape, split size and work assignment of the tile kernel for row tiles
+// whose packed columns are [start(w), start(w+1)).  split_cols = 0: chosen here.
+spmm_status_t plan_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<int64_t(int64_t)> &start,
+                         int64_t split_cols, int64_t align, int shift, int n_cu, int64_t lds_per_cu,
+                         int64_t l2_bytes, const int32_t *h_ptr)
+{
+    const int64_t total = start(n_rows) - start(0);
+    pl->n_items = n_rows;
+    choose_config(pl, n_rows > 0 ? (double)total / (double)n_rows : 0.0, n_cu);
+    const int threads = 64 * pl->waves_n * pl->waves_k;
+    // work-groups per CU that registers allow
+    const size_t lds0 = tile_lds_bytes(0, pl->b_row, pl->V, pl->waves_n, pl->waves_k, true);
+    const int per_cu_regs = std::max(1, tiles_blocks_per_cu(pl->fmt, pl->b_row, pl->V, pl->ab,
+                                                            threads, lds0));
+    const int64_t slots = (int64_t)n_cu * per_cu_regs;
+    const bool spread =
+        env_int("SPMM_FORCE_SPREAD", n_rows * pl->n_col_tiles >= kSpreadItems * slots ? 1 : 0) != 0;
+    if (split_cols == 0) {
+        // the index buffers of every resident work-group must fit its share of
+        // the LDS, which caps the task length
+        const int64_t buf_max = ((lds_per_cu / per_cu_regs - (int64_t)lds0) / 4) / (spread ? 1 : 2);
+        int64_t cap = ((buf_max - 256) / 256 * 256) << shift;
+        cap = std::max<int64_t>(512, cap / align * align);
+        split_cols = auto_split(n_rows, start, align, slots / std::max<int64_t>(1, pl->n_col_tiles));
+        if (env_int("SPMM_FORCE_SPLIT", 0) == 0)
+            split_cols = std::min(split_cols, std::max<int64_t>(align, cap));
+    }
+    // Spread work-groups run in row order when B is much larger than an L2 and
+    // the pattern is banded (neighbouring row tiles then share B rows);
+    // otherwise longest first, which balances better.
+    int local = env_int("SPMM_FORCE_LOCAL", -1);
+    if (local < 0)
+        local = spread && pl->k * pl->N * 2 > 2 * std::max<int64_t>(1, l2_bytes) &&
+                banded_pattern(n_rows, h_ptr, pl->col_idx, pl->fmt == 0 ? pl->b_col : 1, pl->k,
+                               pl->fmt == 0 ? 1 : pl->b_col);
+    return make_tasks(pl, n_rows, start, split_cols, shift, n_cu, spread, local != 0);
 }
 
 spmm_plan_s *new_plan(int fmt, int64_t m, int64_t k, int64_t N, int32_t b_row, int32_t b_col,
@@ -346,7 +551,8 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
     if (nnzb * b_col >= (int64_t(1) << 31))
         return fail(SPMM_ERR_UNSUPPORTED, "nnz_blocks * b_col must be below 2^31");
     int dev = 0, n_cu = 0;
-    if ((s = current_device(&dev, &n_cu)) != SPMM_OK)
+    int64_t lds_cu = 0, l2 = 0;
+    if ((s = current_device(&dev, &n_cu, &lds_cu, &l2)) != SPMM_OK)
         return s;
     spmm_plan_s *pl = new_plan(0, m, k, N, b_row, b_col, ab_dtype, c_dtype, d_blocks,
                                d_block_col_idx, dev);
@@ -369,20 +575,17 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
         pl->tile_cols = 128 * nw;
         pl->n_col_tiles = ceil_div(N, pl->tile_cols);
         pl->workspace = 0;
+        pl->order = env_int("SPMM_FORCE_ORDER", 0) ? 1 : 0;
     } else {
         pl->kernel = 0;
-        const int align = std::max(32, (int)b_col);
         const auto start = [&](int64_t w) { return (int64_t)h_block_row_ptr[w] * b_col; };
-        const int64_t T = auto_split(nbr, start, align);
         int shift = 0;
         while ((1 << shift) < b_col)
             ++shift;
-        if ((s = make_tasks(pl, nbr, start, T, shift)) != SPMM_OK) {
+        if ((s = plan_tasks(pl, nbr, start, 0, std::max(32, (int)b_col), shift, n_cu, lds_cu, l2, h_block_row_ptr)) != SPMM_OK) {
             free_plan(pl);
             return s;
         }
-        const double mean_task = pl->n_items > 0 ? (double)(nnzb * b_col) / pl->n_items : 0.0;
-        choose_config(pl, mean_task, n_cu);
     }
     if (pl->n_items * pl->n_col_tiles > 0x7fffffff) {
         free_plan(pl);
@@ -411,25 +614,29 @@ extern "C" spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
                     "split_cols must be 0 or a positive multiple of 32 up to %lld",
                     (long long)kMaxSplit);
     int dev = 0, n_cu = 0;
-    if ((s = current_device(&dev, &n_cu)) != SPMM_OK)
+    int64_t lds_cu = 0, l2 = 0;
+    if ((s = current_device(&dev, &n_cu, &lds_cu, &l2)) != SPMM_OK)
         return s;
     const int64_t nw = ceil_div(m, b_row);
     const int64_t P = h_window_row_ptr[nw];
     const auto start = [&](int64_t w) { return (int64_t)h_window_row_ptr[w]; };
-    if (split_cols == 0)
-        split_cols = auto_split(nw, start, 32);
     spmm_plan_s *pl = new_plan(1, m, k, N, b_row, b_col, ab_dtype, c_dtype, d_values,
                                d_window_col_idx, dev);
     if (!pl)
         return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
     pl->stored_entries = P * b_row;
+    int64_t widest = 0;
+    for (int64_t w = 0; w < nw; ++w)
+        widest = std::max<int64_t>(widest, (int64_t)h_window_row_ptr[w + 1] - h_window_row_ptr[w]);
+    if ((uint64_t)widest * (uint64_t)b_row * 2u >= kMaxBBytes) {
+        free_plan(pl);
+        return fail(SPMM_ERR_UNSUPPORTED, "a window tile (b_row * width * 2 bytes) must be below 4 GiB");
+    }
     if ((s = upload(h_window_row_ptr, nw + 1, &pl->d_row_ptr)) != SPMM_OK ||
-        (s = make_tasks(pl, nw, start, split_cols, 0)) != SPMM_OK) {
+        (s = plan_tasks(pl, nw, start, split_cols, 32, 0, n_cu, lds_cu, l2, h_window_row_ptr)) != SPMM_OK) {
         free_plan(pl);
         return s;
     }
-    const double mean_task = pl->n_items > 0 ? (double)P / (double)pl->n_items : 0.0;
-    choose_config(pl, mean_task, n_cu);
     if (pl->n_items * pl->n_col_tiles > 0x7fffffff) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
@@ -464,7 +671,7 @@ extern "C" spmm_status_t spmm_plan_info(spmm_plan_t pl, spmm_plan_info_t *info)
     info->cols_per_lane = pl->V;
     info->kernel = pl->kernel;
     info->split_cols = pl->kernel == 0 ? pl->split_cols : 0;
-    info->n_tasks = pl->kernel == 0 ? pl->n_items : 0;
+    info->n_tasks = pl->kernel == 0 ? pl->n_tasks : 0;
     info->n_merges = pl->n_merges;
     info->n_slots = pl->n_slots;
     info->stored_entries = pl->stored_entries;

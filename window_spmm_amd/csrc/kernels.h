@@ -9,31 +9,36 @@
 
 namespace wspmm {
 
-// Arguments of the tile kernel (one work-group per (work item, column tile)).
+// Arguments of the tile kernels.
 struct TileParams {
     const uint16_t *A;        // BCSR blocks or WCSR window tiles (16-bit codes)
     const int32_t *col_idx;   // block_col_idx or window_col_idx
     const int32_t *row_ptr;   // block_row_ptr or window_row_ptr (plan-owned copy)
-    const int4 *tasks;        // tasks (row tile, first packed column, end, slot); the BCSR
-                              // LDS-A kernel walks whole block rows and ignores it
+    const int32_t *tasks;     // generic kernel: work-item descriptors, 8 ints each:
+                              // row tile, first packed column, end, slot (-1: writes C),
+                              // WCSR window's first packed column, WCSR window width,
+                              // column tile, 0
+    const int32_t *lists;     // generic kernel: work-group b runs entries lists[b] .. lists[b+1]-1
+    int64_t n_entries;        // generic kernel: descriptor table entries
     const uint16_t *B;        // k x N codes, leading dimension ldb
     int64_t ldb;
     void *C;                  // m x N of c_dtype, leading dimension ldc
     int64_t ldc;
-    float *partial;           // WCSR partial tiles [slot][R][N] (fp32)
+    float *partial;           // partial tiles [slot][R][N] (fp32)
     int64_t m, k, N;
     uint64_t b_bytes;         // k * ldb * 2: bytes of B the kernel may read (< 2^32 - 256)
-    int64_t n_items;          // block rows (BCSR) or tasks (WCSR)
-    int64_t n_col_tiles;      // column tiles; grid = n_items * n_col_tiles work-groups
+    int64_t n_items;          // tasks (generic kernel) or block rows (LDS-A kernel)
+    int64_t n_col_tiles;      // column tiles; work items = n_items * n_col_tiles
+    int64_t grid;             // generic kernel: persistent work-groups
     int32_t b_col;
     int32_t log2_b_col;       // BCSR: b_col is a power of two
     int32_t tile_cols;        // columns per work-group tile = waves_n * 16 * V
     int32_t waves_n;          // waves splitting the columns
     int32_t waves_k;          // waves splitting the packed-column reduction
     int32_t c_dtype;          // spmm_dtype_t of C
-    int32_t order;            // 0: XCD-contiguous, column-tile major; 1: launch order
-    int32_t lds_idx_ints;     // LDS index area (ints): every task's index count rounded up to
-                              // 256, plus 256
+    int32_t order;            // LDS-A kernel: 0 XCD-contiguous, column-tile major; 1 launch order
+    int32_t lds_idx_ints;     // generic kernel: ints of each LDS index buffer
+    int32_t two_buffers;      // generic kernel: 0 if every work-group runs one entry (one buffer)
 };
 
 struct MergeParams {
@@ -45,11 +50,15 @@ struct MergeParams {
     int32_t c_dtype;
 };
 
-// LDS bytes the tile kernel needs (task indices, reused for the cross-wave reduction).
-size_t tile_lds_bytes(int R, int V, int waves_n, int waves_k, int64_t lds_idx_ints);
+// Dynamic LDS bytes of the generic tile kernel: one or two index buffers of
+// buf_ints ints, the sink and the cross-wave reduction area of its tile shape.
+size_t tile_lds_bytes(int64_t buf_ints, int R, int V, int waves_n, int waves_k, bool two_buffers);
 
-// fmt: 0 = BCSR, 1 = WCSR; work items are tasks in both (p.n_items of them).
+// Generic tile kernel, fmt: 0 = BCSR, 1 = WCSR; p.grid persistent work-groups.
 hipError_t launch_tiles(int fmt, int R, int V, int ab_dtype, const TileParams &p, hipStream_t stream);
+// Work-groups of the tile kernel <fmt, R, V, ab_dtype> resident per CU with
+// `threads` threads and `lds_bytes` of dynamic LDS (0 if the query fails).
+int tiles_blocks_per_cu(int fmt, int R, int V, int ab_dtype, int threads, size_t lds_bytes);
 hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stream);
 // BCSR with 64x64 blocks, waves_n (2 or 4) waves x 128 columns per work-group, A
 // shared through LDS (requires waves_k = 1, V = 8, tile_cols = 128 * waves_n).

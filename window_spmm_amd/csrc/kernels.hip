@@ -181,36 +181,109 @@ struct Stage {
     u32x4_t a[MT];
 };
 
-// Steps of B/A loads kept in flight ahead of the MFMAs (odd, so that the ring of
-// D+1 register stages has an even size).  Chosen so that the ring, the
-// accumulators and the addressing state fit about 240 VGPRs: two waves per SIMD.
+// Steps of B/A loads kept in flight ahead of the MFMAs (1 to 3): as many as let
+// the ring of D+1 register stages and the accumulators fit a register budget
+// that leaves room for addressing at two waves per SIMD (256 VGPRs); taller
+// tiles need more addressing registers, so their budget is smaller.
 template <int R, int V>
 constexpr int pipe_depth()
 {
     constexpr int acc = (R / 16) * V * 4;
     constexpr int stage = 8 * (V / 2) + (R / 16) * 4;
-    constexpr int ring = (200 - acc) / stage;  // stages that fit
-    return ring >= 4 ? 3 : 1;
+    constexpr int budget = R == 16 ? 190 : R == 32 ? 175 : 150;
+    constexpr int ring = (budget - acc) / stage;  // stages that fit
+    return ring >= 4 ? 3 : ring >= 2 ? ring - 1 : 1;
 }
 
-// Generic tile kernel: one work-group per (task, column tile).  A task is a row
-// tile (a BCSR block row or a WCSR window) and a range [kb0, kb1) of its packed
-// columns; tasks that cover part of a row tile write an fp32 partial slot.
-//   * The task's B-row indices (WCSR column indices, or BCSR block columns) are
-//     copied into LDS once, so the main loop never waits on an index load queued
-//     behind in-flight B loads.
-//   * Each wave keeps D steps of A/B loads in flight in a ring of D+1 register
-//     stages; all loads are issued unconditionally (steps past the end read
-//     zeros), so the wait-count bookkeeping is the same on every path.
-template <int FMT, int R, int V, int AB>
-__global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
+// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: expcnt and lgkmcnt at
+// their maxima, vmcnt split over bits 3:0 and 15:14).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Stores the V results of one row of one lane (V adjacent columns) at byte
+// offset `off` of r; kOOB drops the store.  For a given V both the fp32 and the
+// 16-bit forms issue the same number of store instructions, so wait counts on
+// loads issued before the stores stay exact whatever the destination.
+template <int V>
+__device__ __forceinline__ void buf_store_row(__amdgpu_buffer_rsrc_t r, uint32_t off, int dt,
+                                              const float *v)
 {
-    constexpr int MT = R / 16;  // 16-row MFMA tiles per work-group tile
-    constexpr int DW = V / 2;   // dwords of one gathered row segment per lane
+    if (dt == SPMM_FP32) {
+        if constexpr (V >= 4) {
+#pragma unroll
+            for (int c = 0; c < V; c += 4)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4_t{__builtin_bit_cast(uint32_t, v[c]), __builtin_bit_cast(uint32_t, v[c + 1]),
+                            __builtin_bit_cast(uint32_t, v[c + 2]), __builtin_bit_cast(uint32_t, v[c + 3])},
+                    r, (int)(off == kOOB ? kOOB : off + 4 * c), 0, 0);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2_t{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1])}, r,
+                (int)off, 0, 0);
+        }
+    } else {
+        uint32_t w[V / 2];
+#pragma unroll
+        for (int c = 0; c < V; c += 2) {
+            const uint32_t lo = dt == SPMM_BF16 ? f32_to_bf16(v[c]) : f32_to_f16(v[c]);
+            const uint32_t hi = dt == SPMM_BF16 ? f32_to_bf16(v[c + 1]) : f32_to_f16(v[c + 1]);
+            w[c / 2] = lo | (hi << 16);
+        }
+        if constexpr (V == 8) {
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[0], w[1], w[2], w[3]}, r, (int)off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(0u, r, (int)kOOB, 0, 0);  // count filler
+        } else if constexpr (V == 4) {
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w[0], w[1]}, r, (int)off, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b32(w[0], r, (int)off, 0, 0);
+        }
+    }
+}
+
+// Wave-uniform state of one task of the tile kernel (raw fields; buffer
+// resources are rebuilt where they are used).
+struct TaskCtx {
+    const uint16_t *a;   // A values of the task's row tile (BCSR: its first block)
+    uint32_t klen;       // packed columns (0: nothing to load)
+    uint32_t begin;      // first packed column (counted from the start of the format)
+    uint32_t width;      // WCSR window width (A row pitch); BCSR: b_col
+    uint32_t a_col0;     // WCSR: the task's first packed column inside its window
+    int32_t tile;        // row tile
+    int32_t slot;        // partial slot, or -1: the task writes C
+    int32_t ctile;       // column tile
+    uint32_t lds;        // first int of the task's LDS index buffer
+};
+
+// Generic tile kernel.  A task is a row tile (a BCSR block row or a WCSR window)
+// and a range of its packed columns; a work item is a (task, column tile) pair.
+// The grid is persistent: work-group b runs the items of its own list, entries
+// list[b] .. list[b+1]-1 of the descriptor table, which the host fills by
+// greedy longest-first assignment of the items to the least loaded work-group.
+//   * Two LDS index buffers.  While a task runs, its waves copy the B-row
+//     indices (WCSR column indices or BCSR block columns) of the next task into
+//     the other buffer with direct-to-LDS loads, one copy per ring iteration;
+//     the next descriptor (8 ints, lane j holds int j) is loaded a task ahead.
+//   * Each wave keeps D steps of A/B loads in flight in a ring of D+1 register
+//     stages.  The ring runs across tasks: the last iteration of a task issues
+//     the first D steps of the next one, so the pipeline fills once per
+//     work-group.
+//   * Every task issues the same branch-free sequence of vector memory
+//     instructions (loads past a task's end and stores that are masked off use
+//     out-of-range offsets), so the compiler's wait counts stay exact and loads
+//     of the next task are never waited for behind the stores of this one.
+//   * Tasks that cover part of a row tile write an fp32 partial slot; the
+//     waves_k partial sums are added in a fixed order through LDS.
+template <int FMT, int R, int V, int AB>
+__global__ __launch_bounds__(256, 2) void spmm_tile_kernel(TileParams p)
+{
+    constexpr int MT = R / 16;           // 16-row MFMA tiles per work-group tile
+    constexpr int DW = V / 2;            // dwords of one gathered row segment per lane
     constexpr int D = pipe_depth<R, V>();
     constexpr int Q = D + 1;
+    constexpr int kStageOps = 8 + MT;    // vector memory instructions per ring stage
+    constexpr uint32_t RUN = FMT == 1 ? 256 : 64;  // index ints per direct-to-LDS copy
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    int32_t *lidx = reinterpret_cast<int32_t *>(smem);
+    int32_t *const lds = reinterpret_cast<int32_t *>(smem);
+    typedef __attribute__((address_space(3))) void lds_void;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -218,90 +291,105 @@ __global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
     const int wk = wave / p.waves_n;
     const int g = lane >> 4;
     const int li = lane & 15;
-    const int nthreads = 64 * p.waves_n * p.waves_k;
+    const int nwaves = p.waves_n * p.waves_k;
 
-    int64_t item, ctile;
-    tile_of(p.n_items, p.n_items * p.n_col_tiles, p.order, item, ctile);
+    // This work-group's entries of the descriptor table: lists[b] .. lists[b+1]-1.
+    const uint32_t first = (uint32_t)p.lists[blockIdx.x];
+    const uint32_t limit = (uint32_t)p.lists[blockIdx.x + 1];
+    // LDS: index buffer 0 (buf_ints ints), a 256-int sink for copies that
+    // carry nothing, the cross-wave reduction area (waves_k > 1), then index
+    // buffer 1, which the host leaves out when every work-group runs one entry
+    constexpr int NR = 4 * MT * V;  // accumulator floats per lane
+    const uint32_t buf_ints = (uint32_t)p.lds_idx_ints;
+    const uint32_t sink = buf_ints;
+    const uint32_t red_ints = p.waves_k > 1 ? (uint32_t)(nwaves * NR * 64) : 0u;
+    const uint32_t buf1 = buf_ints + 256 + red_ints;
+    const uint32_t idx_cap = buf_ints - 8;               // last valid start of an index read
 
-    // ---- task: row tile, packed-column range, A / index sources ------------
-    const int4 t = p.tasks[item];
-    const int64_t tile = t.x;
-    const int32_t slot = t.w;
-    const int64_t row0 = tile * R;
-    const uint32_t klen = (uint32_t)(t.z - t.y);  // packed columns of the task
-    const int64_t base = p.row_ptr[tile];
-    const int64_t width = p.row_ptr[tile + 1] - base;  // WCSR window width
-    const int32_t *gidx;
-    uint32_t n_idx;              // index entries of the task
-    __amdgpu_buffer_rsrc_t rA;
-    uint32_t a_row_stride;       // bytes between A rows
-    uint32_t a_col0;             // bytes to the task's first packed column in a row
-    if constexpr (FMT == 0) {
-        const int64_t blk0 = (int64_t)t.y >> p.log2_b_col;  // first block of the task
-                                                             // (t.y counts from block 0)
-        n_idx = klen >> p.log2_b_col;
-        gidx = p.col_idx + blk0;
-        rA = make_rsrc(p.A + blk0 * R * p.b_col, (uint32_t)((int64_t)n_idx * R * p.b_col * 2));
-        a_row_stride = (uint32_t)p.b_col * 2;
-        a_col0 = 0;
-    } else {
-        n_idx = klen;
-        gidx = p.col_idx + t.y;
-        rA = make_rsrc(p.A + R * base, (uint32_t)(R * width * 2));
-        a_row_stride = (uint32_t)width * 2;
-        a_col0 = (uint32_t)(t.y - base) * 2;
-    }
-
-    // ---- stage the task's indices in LDS (one burst per task) --------------
-    // Direct-to-LDS buffer loads: each wave instruction fills a contiguous LDS run
-    // (lane i -> bytes 16i or 4i); no VGPRs, one wait for the whole burst.
-    {
-        typedef __attribute__((address_space(3))) void lds_void;
-        const __amdgpu_buffer_rsrc_t rI = make_rsrc(gidx, n_idx * 4);
-        const int nwaves = p.waves_n * p.waves_k;
-        if constexpr (FMT == 1) {
-            // window column indices: n_idx is a multiple of 8, 16 bytes per lane
-            for (int c = wave; c * 256 < (int)n_idx; c += nwaves)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rI, (lds_void *)(lidx + c * 256), 16,
-                                                         (unsigned)((c * 64 + lane) * 16), 0, 0, 0);
+    // Descriptor of entry e: lane l < 8 holds int l (zeros for an invalid entry).
+    const __amdgpu_buffer_rsrc_t rT = make_rsrc(p.tasks, (uint32_t)(p.n_entries * 32));
+    auto load_desc = [&](uint32_t e) -> uint32_t {
+        return __builtin_amdgcn_raw_buffer_load_b32(
+            rT, e < limit ? (e * 8u + (uint32_t)(lane & 7)) * 4u : kOOB, 0, 0);
+    };
+    auto make_ctx = [&](uint32_t dv, uint32_t buf) {
+        TaskCtx c;
+        c.tile = __builtin_amdgcn_readlane((int)dv, 0);
+        c.begin = (uint32_t)__builtin_amdgcn_readlane((int)dv, 1);
+        c.klen = (uint32_t)__builtin_amdgcn_readlane((int)dv, 2) - c.begin;
+        c.slot = __builtin_amdgcn_readlane((int)dv, 3);
+        c.ctile = __builtin_amdgcn_readlane((int)dv, 6);
+        c.lds = buf ? buf1 : 0u;
+        if constexpr (FMT == 0) {
+            c.a = p.A + ((int64_t)c.begin >> p.log2_b_col) * R * p.b_col;
+            c.width = (uint32_t)p.b_col;
+            c.a_col0 = 0;
         } else {
-            // block columns: any count, 4 bytes per lane
-            for (int c = wave; c * 64 < (int)n_idx; c += nwaves)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rI, (lds_void *)(lidx + c * 64), 4,
-                                                         (unsigned)((c * 64 + lane) * 4), 0, 0, 0);
+            const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)dv, 4);
+            c.a = p.A + (int64_t)R * base;
+            c.width = (uint32_t)__builtin_amdgcn_readlane((int)dv, 5);
+            c.a_col0 = c.begin - base;
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-        lds_barrier();
-    }
-    // last valid start of an index read (reads past the task are masked anyway)
-    const uint32_t idx_cap = (uint32_t)(p.lds_idx_ints > 8 ? p.lds_idx_ints - 8 : 0);
+        return c;
+    };
+    // The empty task: loads nothing (every offset out of range), stores nothing.
+    auto null_ctx = [&](const TaskCtx &like) {
+        TaskCtx c = like;
+        c.klen = 0;
+        return c;
+    };
+    auto n_idx_of = [&](const TaskCtx &c) -> uint32_t {
+        if constexpr (FMT == 0)
+            return c.klen >> p.log2_b_col;
+        else
+            return c.klen;
+    };
+    auto nit_of = [&](const TaskCtx &c) -> int32_t {
+        const uint32_t steps0 = (c.klen + 32u * p.waves_k - 1) / (32u * p.waves_k);  // wave 0's
+        return (int32_t)((steps0 + Q - 1) / Q);
+    };
+    auto col0_of = [&](const TaskCtx &c) -> int64_t {
+        return (int64_t)c.ctile * p.tile_cols + wn * 16 * V;
+    };
+    // Copy r of a task's indices into its buffer (a dummy copy into the sink if
+    // the task has no run r or `enable` is false).
+    auto copy_run = [&](const TaskCtx &c, uint32_t r, bool enable = true) {
+        const uint32_t n_idx = n_idx_of(c);
+        const int32_t *gidx = p.col_idx + (FMT == 0 ? (c.begin >> p.log2_b_col) : c.begin);
+        const __amdgpu_buffer_rsrc_t rI = make_rsrc(gidx, n_idx * 4u);
+        const bool real = enable & (r < (n_idx + RUN - 1) / RUN);
+        const uint32_t dst = real ? c.lds + r * RUN : sink;
+        if constexpr (FMT == 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rI, (lds_void *)(lds + dst), 16,
+                                                     real ? (r * 64u + lane) * 16u : kOOB, 0, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rI, (lds_void *)(lds + dst), 4,
+                                                     real ? (r * 64u + lane) * 4u : kOOB, 0, 0, 0);
+    };
+    auto n_runs = [&](const TaskCtx &c) { return (n_idx_of(c) + RUN - 1) / RUN; };
 
-    // B resource starts at this wave's first column; rows are ldb apart.
-    const int64_t col0 = ctile * p.tile_cols + wn * 16 * V;
-    const uint64_t b_skip = (uint64_t)col0 * 2;
-    const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc(p.B + col0, (uint32_t)(p.b_bytes > b_skip ? p.b_bytes - b_skip : 0));
     const uint32_t ldb2 = (uint32_t)p.ldb * 2;
     const uint32_t lane_col_bytes = (uint32_t)li * V * 2;
     const uint32_t k32 = (uint32_t)p.k;
     const uint32_t nbc = (uint32_t)((p.k + p.b_col - 1) >> p.log2_b_col);  // block columns
-    const int kspan = (int)klen - 32 * wk;
-    const int nsteps = kspan > 0 ? (kspan + 32 * p.waves_k - 1) / (32 * p.waves_k) : 0;
     // this lane's first packed column (task-relative) at step s: kfirst + s * kstride
     const uint32_t kfirst = 32u * wk + 8u * g;
     const uint32_t kstride = 32u * p.waves_k;
 
     f32x4_t acc[MT][V];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int c = 0; c < V; ++c)
-            acc[mt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Issues the A and B loads of step s into st.
-    auto issue = [&](int s, Stage<MT, DW> &st) {
+    // Issues the A and B loads of step s of task c into st.
+    auto issue = [&](const TaskCtx &c, int s, Stage<MT, DW> &st) {
         const uint32_t kl = kfirst + (uint32_t)s * kstride;  // task-relative packed column
-        const bool ok = kl < klen;
+        const bool ok = kl < c.klen;
+        const int32_t *lidx = lds + c.lds;
+        const int64_t col0 = col0_of(c);
+        const uint64_t b_skip = (uint64_t)col0 * 2;
+        const __amdgpu_buffer_rsrc_t rB =
+            make_rsrc(p.B + col0, (uint32_t)(p.b_bytes > b_skip ? p.b_bytes - b_skip : 0));
+        const uint32_t a_row_stride = c.width * 2u;
+        const __amdgpu_buffer_rsrc_t rA =
+            make_rsrc(c.a, FMT == 0 ? n_idx_of(c) * (uint32_t)(R * p.b_col * 2) : (uint32_t)R * a_row_stride);
         uint32_t a_off;
         if constexpr (FMT == 0) {
             const uint32_t q = kl >> p.log2_b_col;
@@ -325,7 +413,7 @@ __global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
                 const uint32_t r = ix[j];
                 buf_load<DW>(rB, (ok & (r < k32)) ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
             }
-            a_off = li * a_row_stride + a_col0 + kl * 2u;
+            a_off = li * a_row_stride + (c.a_col0 + kl) * 2u;
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -349,75 +437,169 @@ __global__ __launch_bounds__(256) void spmm_tile_kernel(TileParams p)
         }
     };
 
-    // ---- D-deep pipeline over the k' steps (nsteps is wave-uniform) --------
-    if (nsteps > 0) {
-        Stage<MT, DW> st[Q];
+    // Finishes task c: with waves_k > 1 every wave writes its partial tile to
+    // its own slice of the reduction area, and after one barrier each wave adds
+    // the waves_k partials of a quarter (waves_k = 4), a half (2) or all of the
+    // tile rows, in wave order (the same sum whichever wave does it), and stores
+    // those rows: rows 4g+q of each 16-row tile, V adjacent columns per lane.
+    // Every wave issues the same stores; rows it does not own, rows past m and
+    // columns past N get out-of-range offsets.
+    float *const red = reinterpret_cast<float *>(lds + buf_ints + 256);
+    auto finish = [&](const TaskCtx &c, bool real) {
+        const int qn = 4 / p.waves_k;   // rows q this wave stores: [q0, q0 + qn)
+        const int q0 = wk * qn;
+        if (real && p.waves_k > 1) {
+            float *mine = red + wave * NR * 64 + lane;
 #pragma unroll
-        for (int u = 0; u < D; ++u)
-            issue(u, st[u]);
-        for (int s = 0; s < nsteps; s += Q) {
-#pragma unroll
-            for (int u = 0; u < Q; ++u) {
-                __builtin_amdgcn_sched_barrier(0);
-                issue(s + u + D, st[(u + D) % Q]);
-                __builtin_amdgcn_sched_barrier(0);
-                compute(st[u]);  // steps past the end hold zeros: no branch in the ring
-            }
-        }
-    }
-
-    // ---- fixed-order sum of the waves_k partial tiles through LDS ----
-    if (p.waves_k > 1) {
-        constexpr int NR = MT * V * 4;
-        float *red = reinterpret_cast<float *>(smem);  // [waves_n][NR][64], reuses the index area
-        float *mine = red + (int64_t)wn * NR * 64 + lane;
-        lds_barrier();  // every wave is done reading indices
-        for (int s = p.waves_k - 1; s >= 1; --s) {
-            if (wk == s) {
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int c = 0; c < V; ++c)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            mine[((mt * V + c) * 4 + q) * 64] = acc[mt][c][q];
-            }
+                    for (int cc = 0; cc < V; ++cc)
+                        mine[((q * MT + mt) * V + cc) * 64] = acc[mt][cc][q];
             lds_barrier();
-            if (wk == 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q < q0 || q >= q0 + qn)
+                    continue;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int c = 0; c < V; ++c)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            acc[mt][c][q] += mine[((mt * V + c) * 4 + q) * 64];
+                    for (int cc = 0; cc < V; ++cc) {
+                        const int e = ((q * MT + mt) * V + cc) * 64 + lane;
+                        // waves_k is 2 or 4 here: partials of waves wn, wn + waves_n, ...
+                        float sum = red[wn * NR * 64 + e];
+                        sum += red[(p.waves_n + wn) * NR * 64 + e];
+                        if (p.waves_k > 2) {
+                            sum += red[(2 * p.waves_n + wn) * NR * 64 + e];
+                            sum += red[(3 * p.waves_n + wn) * NR * 64 + e];
+                        }
+                        acc[mt][cc][q] = sum;
+                    }
             }
-            lds_barrier();
         }
-        if (wk != 0)
-            return;
-    }
+        const bool to_partial = c.slot >= 0;
+        const int64_t row0 = (int64_t)c.tile * R;
+        const int64_t col0 = col0_of(c);
+        const int dt = to_partial ? SPMM_FP32 : p.c_dtype;
+        const uint32_t esz = dt == SPMM_FP32 ? 4u : 2u;
+        const int64_t stride = to_partial ? p.N : p.ldc;  // elements between rows
+        void *base = to_partial ? (void *)(p.partial + ((int64_t)c.slot * R * p.N + col0))
+                                : (void *)((uint8_t *)p.C + (row0 * p.ldc + col0) * esz);
+        const __amdgpu_buffer_rsrc_t rO = make_rsrc(base, (uint32_t)(R * stride) * esz);
+        const bool lane_ok = real & (col0 + li * V < p.N);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = mt * 16 + 4 * g + q;
+                float v[V];
+#pragma unroll
+                for (int cc = 0; cc < V; ++cc)
+                    v[cc] = acc[mt][cc][q];
+                const bool mine_q = (q >= q0) & (q < q0 + qn);
+                const bool row_ok = to_partial | (row0 + r < p.m);
+                const uint32_t off = (lane_ok & mine_q & row_ok)
+                                         ? ((uint32_t)r * (uint32_t)stride + li * V) * esz
+                                         : kOOB;
+                buf_store_row<V>(rO, off, dt, v);
+            }
+        }
+    };
 
-    // ---- epilogue: row 4g+q of each 16-row tile, V adjacent columns ----
-    const int64_t ncol = col0 + li * V;
-    if (ncol >= p.N)
+    // ---- entries of the first three turns -----------------------------------
+    const uint32_t e0 = first;
+    uint32_t e_next = first + 1, e_next2 = first + 2;
+    if (e0 >= limit)
         return;
+
+    // ---- first task: indices staged before the ring starts ----------------
+    TaskCtx cur = make_ctx(load_desc(e0), 0);
+    for (uint32_t r = wave; r < n_runs(cur); r += nwaves)
+        copy_run(cur, r);
+    uint32_t d_next = load_desc(e_next);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+    Stage<MT, DW> st[Q];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int u = 0; u < D; ++u)
+        issue(cur, u, st[u]);
+
+    TaskCtx prev = cur;
+    bool have_prev = false;
+    for (uint32_t j = 0;; ++j) {
+        // ---- finish the previous task (its last steps ran in the last turn) ----
+        finish(prev, have_prev);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = mt * 16 + 4 * g + q;
-            float v[V];
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int c = 0; c < V; ++c)
-                v[c] = acc[mt][c][q];
-            if (slot >= 0) {
-                store_row<V>(p.partial, ((int64_t)slot * R + r) * p.N + ncol, SPMM_FP32, v);
-            } else if (row0 + r < p.m) {
-                store_row<V>(p.C, (row0 + r) * p.ldc + ncol, p.c_dtype, v);
+                acc[mt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        const bool has_next = e_next < limit;
+        const TaskCtx nxt = has_next ? make_ctx(d_next, (j + 1) & 1) : null_ctx(cur);
+        const uint32_t d_next2 = load_desc(e_next2);
+
+        // ---- the task's steps.  Every iteration issues one index copy of the
+        // next task and Q ring stages; in the last one the copy is a dummy and
+        // the stages beyond this task's end are the next task's first D. ----
+        const int32_t nit_cur = nit_of(cur);
+        const uint32_t copied = nit_cur > 1 ? (uint32_t)(nit_cur - 1) * nwaves : 0u;
+        // The next task's indices must be in LDS before its first issue; the
+        // barrier also ends every wave's reads of this task's buffer, which the
+        // copies for the task after next overwrite.
+        auto boundary = [&]() {
+            if (n_runs(nxt) > copied) {
+                for (uint32_t r = copied + wave; r < n_runs(nxt); r += nwaves)
+                    copy_run(nxt, r);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            } else {
+                // every real copy was followed by more than D ring stages
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(D * kStageOps));
+            }
+            lds_barrier();
+        };
+        int s = 0;
+        for (int it = 0; it < nit_cur; ++it, s += Q) {
+            const bool last = it + 1 == nit_cur;
+            copy_run(nxt, (uint32_t)(it * nwaves + wave), !last);
+#pragma unroll
+            for (int u = 0; u < Q; ++u) {
+                if (u == Q - D) {
+                    // this task's indices have been read for the last time;
+                    // from here on the last iteration reads the next task's
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (last)
+                        boundary();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (u + D < Q) {
+                    issue(cur, s + u + D, st[(u + D) % Q]);
+                } else {
+                    // wave-uniform selection between this task's step and the next's
+                    TaskCtx c = last ? nxt : cur;
+                    issue(c, last ? u + D - Q : s + u + D, st[(u + D) % Q]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                compute(st[u]);  // steps past the end hold zeros
             }
         }
+        if (nit_cur == 0) {
+            boundary();
+#pragma unroll
+            for (int u = 0; u < D; ++u)
+                issue(nxt, u, st[u]);
+        }
+        prev = cur;
+        have_prev = true;
+        if (!has_next)
+            break;
+        cur = nxt;
+        d_next = d_next2;
+        e_next = e_next2;
+        e_next2 = e_next2 + 1;
     }
+    finish(prev, true);
 }
 
 // BCSR with 64 x 64 blocks and a wide column tile (NW waves x 128 columns).
@@ -589,48 +771,43 @@ __global__ __launch_bounds__(256) void wcsr_merge_kernel(MergeParams p)
     store_row<8>(p.C, row * p.ldc + col, p.c_dtype, s);
 }
 
-template <int FMT, int R, int V, int AB>
-static hipError_t launch_one(const TileParams &p, dim3 grid, dim3 block, size_t lds,
-                             hipStream_t stream)
-{
-    hipLaunchKernelGGL((spmm_tile_kernel<FMT, R, V, AB>), grid, block, lds, stream, p);
-    return hipGetLastError();
-}
+// The tile kernel instantiation for (format, tile rows, columns per lane, A/B type).
+typedef void (*tile_fn_t)(TileParams);
 
 template <int FMT, int R, int V>
-static hipError_t by_ab(int ab, const TileParams &p, dim3 g, dim3 b, size_t lds, hipStream_t s)
+static tile_fn_t tile_fn_ab(int ab)
 {
-    return ab == SPMM_FP16 ? launch_one<FMT, R, V, SPMM_FP16>(p, g, b, lds, s)
-                           : launch_one<FMT, R, V, SPMM_BF16>(p, g, b, lds, s);
+    return ab == SPMM_FP16 ? spmm_tile_kernel<FMT, R, V, SPMM_FP16>
+                           : spmm_tile_kernel<FMT, R, V, SPMM_BF16>;
 }
 
+// V = 8 exists for 16-row tiles only: taller tiles would need the ring's
+// registers for their accumulators (the host never plans them).
 template <int FMT, int R>
-static hipError_t by_v(int v, int ab, const TileParams &p, dim3 g, dim3 b, size_t lds,
-                       hipStream_t s)
+static tile_fn_t tile_fn_v(int v, int ab)
 {
-    switch (v) {
-    case 2: return by_ab<FMT, R, 2>(ab, p, g, b, lds, s);
-    case 4: return by_ab<FMT, R, 4>(ab, p, g, b, lds, s);
-    default: return by_ab<FMT, R, 8>(ab, p, g, b, lds, s);
-    }
+    if constexpr (R == 16)
+        if (v == 8)
+            return tile_fn_ab<FMT, R, 8>(ab);
+    return v == 2 ? tile_fn_ab<FMT, R, 2>(ab) : v == 4 ? tile_fn_ab<FMT, R, 4>(ab) : nullptr;
 }
 
 template <int FMT>
-static hipError_t by_r(int r, int v, int ab, const TileParams &p, dim3 g, dim3 b, size_t lds,
-                       hipStream_t s)
+static tile_fn_t tile_fn_r(int r, int v, int ab)
 {
-    switch (r) {
-    case 16: return by_v<FMT, 16>(v, ab, p, g, b, lds, s);
-    case 32: return by_v<FMT, 32>(v, ab, p, g, b, lds, s);
-    default: return by_v<FMT, 64>(v, ab, p, g, b, lds, s);
-    }
+    return r == 16 ? tile_fn_v<FMT, 16>(v, ab) : r == 32 ? tile_fn_v<FMT, 32>(v, ab)
+                                                         : tile_fn_v<FMT, 64>(v, ab);
 }
 
-size_t tile_lds_bytes(int R, int V, int waves_n, int waves_k, int64_t lds_idx_ints)
+static tile_fn_t tile_fn(int fmt, int R, int V, int ab)
 {
-    const size_t red = waves_k > 1 ? (size_t)waves_n * (R / 16) * V * 4 * 64 * sizeof(float) : 0;
-    const size_t idx = (size_t)lds_idx_ints * sizeof(int32_t);
-    return red > idx ? red : idx;
+    return fmt == 0 ? tile_fn_r<0>(R, V, ab) : tile_fn_r<1>(R, V, ab);
+}
+
+size_t tile_lds_bytes(int64_t buf_ints, int R, int V, int waves_n, int waves_k, bool two_buffers)
+{
+    const int64_t red = waves_k > 1 ? (int64_t)waves_n * waves_k * 4 * (R / 16) * V * 64 : 0;
+    return (size_t)((two_buffers ? 2 : 1) * buf_ints + 256 + red) * sizeof(int32_t);
 }
 
 template <int NW>
@@ -656,11 +833,25 @@ hipError_t launch_bcsr64_lds(int ab, const TileParams &p, hipStream_t stream)
 
 hipError_t launch_tiles(int fmt, int R, int V, int ab, const TileParams &p, hipStream_t stream)
 {
-    dim3 grid((unsigned)(p.n_items * p.n_col_tiles));
+    if (!tile_fn(fmt, R, V, ab))
+        return hipErrorInvalidValue;
+    dim3 grid((unsigned)p.grid);
     dim3 block(64 * p.waves_n * p.waves_k);
-    size_t lds = tile_lds_bytes(R, V, p.waves_n, p.waves_k, p.lds_idx_ints);
-    return fmt == 0 ? by_r<0>(R, V, ab, p, grid, block, lds, stream)
-                    : by_r<1>(R, V, ab, p, grid, block, lds, stream);
+    TileParams arg = p;
+    void *args[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void *>(tile_fn(fmt, R, V, ab)), grid, block,
+                           args, tile_lds_bytes(p.lds_idx_ints, R, V, p.waves_n, p.waves_k, p.two_buffers != 0),
+                           stream);
+}
+
+int tiles_blocks_per_cu(int fmt, int R, int V, int ab, int threads, size_t lds)
+{
+    int n = 0;
+    const tile_fn_t f = tile_fn(fmt, R, V, ab);
+    if (!f || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(f),
+                                                           threads, lds) != hipSuccess)
+        return 0;
+    return n;
 }
 
 hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stream)
