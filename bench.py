@@ -15,6 +15,7 @@ gate_proj shape, 5: block-sparse P*V).  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -73,6 +74,48 @@ def algorithmic(p, A):
             "bytes_alg": float(bytes_alg), "b_rows_referenced": brows}
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "window_spmm_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_sha256() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload_key: str):
+    """HBM bytes per launch of the dominant kernel from the rocprofv3 counters
+    recorded in profiles/traffic.json (FETCH_SIZE and WRITE_SIZE per dispatch,
+    each scaled by what the same counter reads for a plain device copy of known
+    size), or None when there is no record for this workload or the kernel
+    source has changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    w = rec.get("workloads", {}).get(workload_key)
+    if not w or w.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    cp = rec["copy"]
+    f_fetch = cp["bytes"] / (cp["fetch_kib"] * 1024.0)
+    f_write = cp["bytes"] / (cp["write_kib"] * 1024.0)
+    return w["fetch_kib"] * 1024.0 * f_fetch + w["write_kib"] * 1024.0 * f_write
+
+
+def copy_probe():
+    """A plain device-to-device copy of known size (calibrates the FETCH_SIZE and
+    WRITE_SIZE counters; run under rocprofv3 --pmc)."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 5}))
+
+
 def cpu_baseline(p, budget_s: float):
     """The oracle, as it stands, on all cores of this process, on the same input.
     Repeats the full product until ``budget_s`` has passed (at least once)."""
@@ -116,7 +159,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cold", action="store_true", help="also time with caches flushed")
     ap.add_argument("--no-pad", action="store_true", help="B and C with leading dimension N")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -184,7 +233,10 @@ def main():
         roof = {"bound": "mfma", "achieved": alg["flops_stored"] / t_kernel / 1e12,
                 "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    key = "config%d" % args.config + ("_" + args.which if args.config == 4 else "") + \
+          ("_m%d_n%d" % (args.member, args.n3) if args.config == 3 else "")
+    roof["traffic"] = measured_traffic(key)
+    roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["kernel_us"] = t_kernel * 1e6
     roof["kernels"] = ("bcsr64_lds_kernel" if info["kernel"] == 1 else "spmm_tile_kernel") + \
         (" + wcsr_merge_kernel" if info["n_merges"] else "")

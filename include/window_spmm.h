@@ -128,8 +128,9 @@ spmm_status_t spmm_wcsr_split(int64_t n_windows, const int32_t *h_window_row_ptr
  * Supported: b_row in {16, 32, 64}; b_col a multiple of 8 (BCSR: a power of two
  * in [8, 256]);
  * ab_dtype FP16 or BF16 (A and B alike); c_dtype FP32, BF16 or FP16; N a
- * multiple of 8 (m = 0 or N = 0 gives a plan whose runs do nothing); device
- * index and value arrays 16-byte aligned.  Otherwise UNSUPPORTED.
+ * multiple of 8 (m = 0 or N = 0 gives a plan whose runs do nothing); k < 2^24
+ * (B row numbers are multiplied in 24-bit arithmetic); device index and value
+ * arrays 16-byte aligned.  Otherwise UNSUPPORTED.
  * Accumulation is fp32; 16-bit C is rounded once (nearest-even).
  * The plan needs a gfx950 device (SPMM_ERR_HIP otherwise).
  * *workspace_bytes receives the size of the workspace every run needs (0 if
@@ -152,7 +153,8 @@ spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
  * multiple of b_col, else BAD_FORMAT); d_window_col_idx[P], d_values[b_row*P]
  * (device).  A column index outside [0, k) (the -1 pads included) reads B as
  * zero.  split_cols: sub-task size T (positive multiple of 32, at most 8192), or
- * 0 to let the plan choose. */
+ * 0 to let the plan choose.  UNSUPPORTED if a window tile (b_row * width * 2
+ * bytes) reaches 2^32 - 256. */
 spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
                              int32_t b_col, const int32_t *h_window_row_ptr,
                              const int32_t *d_window_col_idx, const void *d_values,
@@ -164,8 +166,9 @@ spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
  * m x N of c_dtype with leading dimension ldc.  Rows < m and columns < N of C
  * are overwritten (C is never read); rows without entries become 0.
  * Requirements (else UNSUPPORTED): d_B and d_C 16-byte aligned, ldb >= N and
- * ldc >= N, both multiples of 8, and k * ldb * 2 < 2^32 - 256 (B is read through
- * 32-bit buffer offsets).  d_workspace: at least workspace_bytes of
+ * ldc >= N, both multiples of 8, ldb < 2^23, k * ldb * 2 < 2^32 - 256 and
+ * b_row * ldc * (C element bytes) < 2^32 - 256 (B and a tile's rows of C are
+ * addressed through 32-bit buffer offsets).  d_workspace: at least workspace_bytes of
  * device memory (16-byte aligned) when workspace_bytes > 0, else ignored.
  * Device-side faults surface at the caller's next synchronisation. */
 spmm_status_t spmm_bcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void *d_C, int64_t ldc,

@@ -52,6 +52,9 @@ def test_plan_argument_checks_before_device():
     assert _code(lambda: ws.bcsr_plan(16, 64, 60, 16, 16, ptr, 256, 256)) == ws.ERR_UNSUPPORTED
     # misaligned device arrays
     assert _code(lambda: ws.bcsr_plan(16, 64, 64, 16, 16, ptr, 258, 256)) == ws.ERR_UNSUPPORTED
+    # k at the 24-bit limit of B row numbers
+    assert _code(lambda: ws.wcsr_plan(16, 1 << 24, 64, 16, 8, np.array([0, 8], np.int32), 256, 256)) \
+        == ws.ERR_UNSUPPORTED
     # row pointer going backwards
     assert _code(lambda: ws.bcsr_plan(32, 64, 64, 16, 16, np.array([0, 2, 1], np.int32), 256, 256)) \
         == ws.ERR_BAD_FORMAT

@@ -103,6 +103,8 @@ spmm_status_t check_common(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, i
         return fail(SPMM_ERR_UNSUPPORTED, "N = %lld must be a multiple of 8", (long long)N);
     if (N > (int64_t(1) << 28) || m >= (int64_t(1) << 31) || k >= (int64_t(1) << 31))
         return fail(SPMM_ERR_UNSUPPORTED, "matrix dimension too large");
+    if (k >= (int64_t(1) << 24))
+        return fail(SPMM_ERR_UNSUPPORTED, "k = %lld: must be below 2^24", (long long)k);
     if (((uintptr_t)d_idx | (uintptr_t)d_vals) & 15)
         return fail(SPMM_ERR_UNSUPPORTED, "device index/value arrays must be 16-byte aligned");
     const int64_t nrow = ceil_div(m, b_row);
@@ -190,6 +192,8 @@ spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int
         return fail(SPMM_ERR_UNSUPPORTED, "B and C must be 16-byte aligned");
     if (ldb < pl->N || ldc < pl->N || ldb % 8 || ldc % 8)
         return fail(SPMM_ERR_UNSUPPORTED, "ldb/ldc must be >= N and multiples of 8");
+    if (ldb >= (int64_t(1) << 23))
+        return fail(SPMM_ERR_UNSUPPORTED, "ldb must be below 2^23");
     if ((uint64_t)pl->k * (uint64_t)ldb * 2u >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "B (k * ldb * 2 bytes) must be smaller than 4 GiB - 256");
     if (pl->kernel == 0 && (uint64_t)pl->b_row * (uint64_t)ldc * (pl->ct == SPMM_FP32 ? 4u : 2u) >= kMaxBBytes)

@@ -183,14 +183,15 @@ struct Stage {
 
 // Steps of B/A loads kept in flight ahead of the MFMAs (1 to 3): as many as let
 // the ring of D+1 register stages and the accumulators fit a register budget
-// that leaves room for addressing at two waves per SIMD (256 VGPRs); taller
-// tiles need more addressing registers, so their budget is smaller.
+// that leaves room for addressing at two waves per SIMD (256 VGPRs).  For
+// 16-row tiles the budget stops at two steps: measured on the WCSR workloads,
+// a third step in flight gains nothing.
 template <int R, int V>
 constexpr int pipe_depth()
 {
     constexpr int acc = (R / 16) * V * 4;
     constexpr int stage = 8 * (V / 2) + (R / 16) * 4;
-    constexpr int budget = R == 16 ? 190 : R == 32 ? 175 : 150;
+    constexpr int budget = R == 16 ? 140 : R == 32 ? 175 : 150;
     constexpr int ring = (budget - acc) / stage;  // stages that fit
     return ring >= 4 ? 3 : ring >= 2 ? ring - 1 : 1;
 }
@@ -390,19 +391,27 @@ __global__ __launch_bounds__(256, 2) void spmm_tile_kernel(TileParams p)
         const uint32_t a_row_stride = c.width * 2u;
         const __amdgpu_buffer_rsrc_t rA =
             make_rsrc(c.a, FMT == 0 ? n_idx_of(c) * (uint32_t)(R * p.b_col * 2) : (uint32_t)R * a_row_stride);
-        uint32_t a_off;
+        // A fragments first, then the B rows: the MFMAs of a stage wait for its
+        // last B row, which also covers its A
+        const uint32_t q = kl >> p.log2_b_col;            // BCSR: block of the task
+        const uint32_t kk = kl & (uint32_t)(p.b_col - 1);  // BCSR: column in the block
+        const uint32_t a_off = FMT == 0 ? ((q * R + li) * (uint32_t)p.b_col + kk) * 2u
+                                        : li * a_row_stride + (c.a_col0 + kl) * 2u;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            uint32_t w[4];
+            buf_load<4>(rA, ok ? a_off + (uint32_t)(mt * 16) * a_row_stride : kOOB, w);
+            st.a[mt] = u32x4_t{w[0], w[1], w[2], w[3]};
+        }
         if constexpr (FMT == 0) {
-            const uint32_t q = kl >> p.log2_b_col;
-            const uint32_t kk = kl & (uint32_t)(p.b_col - 1);
             const uint32_t J = (uint32_t)lidx[q < idx_cap ? q : idx_cap];  // in-bounds read
             const bool jv = ok & (J < nbc);
             const uint32_t r0 = (jv ? J : 0u) * (uint32_t)p.b_col + kk;
+            // rows r0 .. r0+7 are consecutive: one 24-bit multiply, then + j*ldb2
+            const uint32_t base = __umul24(r0, ldb2) + lane_col_bytes;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t r = r0 + j;
-                buf_load<DW>(rB, (jv & (r < k32)) ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
-            }
-            a_off = ((q * R + li) * (uint32_t)p.b_col + kk) * 2u;
+            for (int j = 0; j < 8; ++j)
+                buf_load<DW>(rB, (jv & (r0 + j < k32)) ? base + (uint32_t)j * ldb2 : kOOB, st.b[j]);
         } else {
             const uint32_t kr = kl < idx_cap ? kl : idx_cap;  // in-bounds LDS read
             const u32x4_t i0 = *reinterpret_cast<const u32x4_t *>(lidx + kr);
@@ -411,15 +420,9 @@ __global__ __launch_bounds__(256, 2) void spmm_tile_kernel(TileParams p)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t r = ix[j];
-                buf_load<DW>(rB, (ok & (r < k32)) ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
+                // (k < 2^24 and ldb * 2 < 2^24: the host checks both)
+                buf_load<DW>(rB, (ok & (r < k32)) ? __umul24(r, ldb2) + lane_col_bytes : kOOB, st.b[j]);
             }
-            a_off = li * a_row_stride + (c.a_col0 + kl) * 2u;
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            uint32_t w[4];
-            buf_load<4>(rA, ok ? a_off + (uint32_t)(mt * 16) * a_row_stride : kOOB, w);
-            st.a[mt] = u32x4_t{w[0], w[1], w[2], w[3]};
         }
     };
 
