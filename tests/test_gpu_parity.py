@@ -283,18 +283,27 @@ def test_config5_sampled(ws):
     check(p, got, rows=rows)
 
 
-@pytest.mark.parametrize("env", [{"SPMM_FORCE_WAVES_N": "2"}, {"SPMM_FORCE_WAVES_N": "4"},
-                                 {"SPMM_FORCE_KERNEL": "0"}], ids=lambda e: ",".join(e))
+@pytest.mark.parametrize("env", [{"SPMM_FORCE_KERNEL": "2", "SPMM_FORCE_RING_DEPTH": "5"},
+                                 {"SPMM_FORCE_KERNEL": "2", "SPMM_FORCE_RING_DEPTH": "3"},
+                                 {"SPMM_FORCE_KERNEL": "2", "SPMM_FORCE_ORDER": "0"},
+                                 {"SPMM_FORCE_KERNEL": "1", "SPMM_FORCE_WAVES_N": "2"},
+                                 {"SPMM_FORCE_KERNEL": "1", "SPMM_FORCE_WAVES_N": "4"},
+                                 {"SPMM_FORCE_KERNEL": "0"}],
+                         ids=lambda e: "-".join("%s%s" % (k[11:].lower(), v) for k, v in e.items()))
 def test_bcsr64_kernel_variants_padded_ld(ws, env, monkeypatch):
-    """The 64x64-block kernels (LDS-shared A at 2 or 4 waves, and the generic one)
-    on a wide N with padded leading dimensions and a partial last column tile."""
+    """The 64x64-block kernels (the deep-ring kernel at both depths and both
+    work-group orders, the LDS-shared-A kernel at 2 or 4 waves, the generic one)
+    on a wide N with padded leading dimensions, a partial last column tile,
+    empty block rows and odd block counts."""
     for k_, v_ in env.items():
         monkeypatch.setenv(k_, v_)
-    p = synth.block_problem(448, 640, 1288, 64, 64, 0.25, seed=31, ab_dtype="bf16", c_dtype="bf16")
+    p = synth.block_problem(1280, 640, 1288, 64, 64, 0.25, seed=31, ab_dtype="bf16", c_dtype="bf16")
     A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
                         p.ab_dtype, p.c_dtype)
     info = A.plan.info()
-    assert info["kernel"] == (0 if env.get("SPMM_FORCE_KERNEL") == "0" else 1)
+    assert info["kernel"] == int(env["SPMM_FORCE_KERNEL"])
+    nblk = np.diff(A.h_ptr)
+    assert (nblk == 0).any() and (nblk % 2 == 1).any()
     B = A.device_b(p.B, padded=True)
     C = A.new_c(padded=True)
     C.fill_(float("nan"))

@@ -17,15 +17,16 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["status.cpp", "formats.cpp"]
-HIP_SOURCES = ["kernels.hip", "api.hip"]
-HEADERS = ["common.h", "kernels.h"]
+HEADERS = ["common.h", "kernels.h", "device.h"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
-# MFMA accumulators stay in ordinary VGPRs (the unified register file of gfx950),
-# which avoids AGPR<->VGPR copies around the software-pipelined loops.
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC,
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wall"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
+# kernels.hip: MFMA accumulators stay in ordinary VGPRs (the unified register
+# file of gfx950), which avoids copies around its two-waves-per-SIMD loops.
+# kernels_lds.hip runs one wave per SIMD and keeps them in accumulation registers.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+HIP_SOURCES = [("kernels.hip", VGPR_FORM), ("kernels_lds.hip", []), ("api.hip", [])]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wextra"]
 
 
@@ -47,9 +48,9 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD_DIR, src + ".o")
         _run(["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    for src in HIP_SOURCES:
+    for src, extra in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        _run([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        _run([HIPCC] + HIP_FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)

@@ -34,7 +34,9 @@ struct spmm_plan_s {
     int64_t grid;               // persistent work-groups of the generic kernel
     int64_t stored_entries;
     int V, waves_n, waves_k;
-    int kernel;                 // 0: generic tile kernel, 1: BCSR 64x64 with LDS-shared A
+    int kernel;                 // 0: generic tile kernel, 1: BCSR 64x64 with LDS-shared A,
+                                // 2: BCSR 64x64, LDS-shared A and a deep B ring
+    int ring_depth;             // kernel 2: half-blocks of B in flight per wave
     int64_t tile_cols, n_col_tiles;
     size_t workspace;
     int device;
@@ -249,8 +251,9 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.order = pl->order;
     p.lds_idx_ints = (int32_t)pl->lds_idx_ints;
     p.grid = pl->grid;
-    hipError_t e = pl->kernel == 1 ? launch_bcsr64_lds(pl->ab, p, st)
-                                   : launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, st);
+    hipError_t e = pl->kernel == 2   ? launch_bcsr64_ring(pl->ab, pl->ring_depth, p, st)
+                   : pl->kernel == 1 ? launch_bcsr64_lds(pl->ab, p, st)
+                                     : launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, st);
     if (e != hipSuccess)
         return hip_fail(e, "tile kernel launch");
     if (pl->n_merges > 0) {
@@ -567,10 +570,27 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
         free_plan(pl);
         return s;
     }
-    // 64x64 blocks and at least one full 256-column tile: the kernel that shares
-    // each A block through LDS walks whole block rows
-    pl->kernel = env_int("SPMM_FORCE_KERNEL", (b_row == 64 && b_col == 64 && N >= 256) ? 1 : 0);
-    if (pl->kernel == 1 && b_row == 64 && b_col == 64) {
+    // 64x64 blocks and wide N: kernels that share each A block through LDS and
+    // walk whole block rows.  Kernel 2 (one work-group per CU, a deep ring of B
+    // loads) holds a block row's block columns in one register: <= 64 blocks.
+    int max_blocks = 0;
+    for (int64_t w = 0; w < nbr; ++w)
+        max_blocks = std::max(max_blocks, h_block_row_ptr[w + 1] - h_block_row_ptr[w]);
+    const bool b64 = b_row == 64 && b_col == 64;
+    pl->kernel = env_int("SPMM_FORCE_KERNEL", b64 && N >= 256 ? 1 : 0);
+    if (pl->kernel == 2 && !(b64 && max_blocks <= 64))
+        pl->kernel = 0;
+    if (pl->kernel == 2) {
+        pl->n_items = nbr;
+        pl->V = 8;
+        pl->waves_n = 4;
+        pl->waves_k = 1;
+        pl->tile_cols = 512;
+        pl->n_col_tiles = ceil_div(N, pl->tile_cols);
+        pl->workspace = 0;
+        pl->ring_depth = env_int("SPMM_FORCE_RING_DEPTH", 5) == 3 ? 3 : 5;
+        pl->order = env_int("SPMM_FORCE_ORDER", 1) ? 1 : 0;
+    } else if (pl->kernel == 1 && b64) {
         const int nw = env_int("SPMM_FORCE_WAVES_N", 4) == 2 ? 2 : 4;
         pl->n_items = nbr;
         pl->V = 8;

@@ -63,5 +63,9 @@ hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stre
 // BCSR with 64x64 blocks, waves_n (2 or 4) waves x 128 columns per work-group, A
 // shared through LDS (requires waves_k = 1, V = 8, tile_cols = 128 * waves_n).
 hipError_t launch_bcsr64_lds(int ab_dtype, const TileParams &p, hipStream_t stream);
+// BCSR with 64x64 blocks, one work-group of 4 waves x 128 columns per CU, a ring
+// of depth (3 or 5) half-blocks of B loads in flight per wave; at most 64 blocks
+// per block row (tile_cols = 512).
+hipError_t launch_bcsr64_ring(int ab_dtype, int depth, const TileParams &p, hipStream_t stream);
 
 }  // namespace wspmm

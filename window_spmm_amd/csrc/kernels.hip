@@ -44,135 +44,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device.h"
 #include "kernels.h"
 
 namespace wspmm {
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-// Word 3 of a raw buffer resource on gfx9-class devices (no format conversion,
-// no swizzle): the value the ROCm libraries use for gfx90a/gfx94x/gfx950.
-constexpr int kRsrcWord3 = 0x00020000;
-// Offset used for "no data": beyond any resource size the host allows.
-constexpr uint32_t kOOB = 0xFFFFFFF0u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             kRsrcWord3);
-}
-
-// Cache-policy bits of buffer instructions: non-temporal.  (Measured: on the
-// generic kernel's A stream this is slower, the data then bypasses the MALL.)
-constexpr int kNT = 2;
-
-template <int DW, int POL = 0>
-__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *out)
-{
-    if constexpr (DW == 4) {
-        u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POL);
-        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
-    } else if constexpr (DW == 2) {
-        u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, POL);
-        out[0] = v[0]; out[1] = v[1];
-    } else {
-        out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, POL);
-    }
-}
-
-template <int AB>
-__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
-{
-    if constexpr (AB == SPMM_FP16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
-                                                      __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-// fp32 -> bfloat16 code, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f)
-{
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return 0x7fc0u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-// fp32 -> binary16 code (hardware conversion, round to nearest even).
-__device__ __forceinline__ uint32_t f32_to_f16(float f)
-{
-    return __builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
-// Stores V consecutive results of one row as c_dtype (NT: non-temporal stores).
-template <typename T>
-__device__ __forceinline__ void st(T *d, T x, bool nt)
-{
-    if (nt)
-        __builtin_nontemporal_store(x, d);
-    else
-        *d = x;
-}
-
-template <int V, bool NT = false>
-__device__ __forceinline__ void store_row(void *base, int64_t elem, int c_dtype, const float *v)
-{
-    if (c_dtype == SPMM_FP32) {
-        float *d = reinterpret_cast<float *>(base) + elem;
-        if constexpr (V >= 4) {
-#pragma unroll
-            for (int c = 0; c < V; c += 4)
-                st(reinterpret_cast<f32x4_t *>(d + c), f32x4_t{v[c], v[c + 1], v[c + 2], v[c + 3]}, NT);
-        } else {
-            st(reinterpret_cast<f32x2_t *>(d), f32x2_t{v[0], v[1]}, NT);
-        }
-    } else {
-        uint32_t w[V / 2];
-#pragma unroll
-        for (int c = 0; c < V; c += 2) {
-            uint32_t lo = c_dtype == SPMM_BF16 ? f32_to_bf16(v[c]) : f32_to_f16(v[c]);
-            uint32_t hi = c_dtype == SPMM_BF16 ? f32_to_bf16(v[c + 1]) : f32_to_f16(v[c + 1]);
-            w[c / 2] = lo | (hi << 16);
-        }
-        uint16_t *d = reinterpret_cast<uint16_t *>(base) + elem;
-        if constexpr (V == 8)
-            st(reinterpret_cast<u32x4_t *>(d), u32x4_t{w[0], w[1], w[2], w[3]}, NT);
-        else if constexpr (V == 4)
-            st(reinterpret_cast<u32x2_t *>(d), u32x2_t{w[0], w[1]}, NT);
-        else
-            st(reinterpret_cast<uint32_t *>(d), w[0], NT);
-    }
-}
-
-// Work-group id -> (work item, column tile), XCD-contiguous and column-tile major.
-__device__ __forceinline__ void tile_of(int64_t n_items, int64_t total, int order, int64_t &item,
-                                        int64_t &ctile)
-{
-    const int64_t i = blockIdx.x;
-    const int64_t q = total >> 3, rem = total & 7;
-    const int64_t xcd = i & 7, local = i >> 3;
-    const int64_t logical = order ? i : xcd * q + (xcd < rem ? xcd : rem) + local;
-    // (readfirstlane: tell the compiler these are wave-uniform, so that the
-    // loads they address become scalar loads)
-    ctile = __builtin_amdgcn_readfirstlane((int)(logical / n_items));
-    item = __builtin_amdgcn_readfirstlane((int)(logical - ctile * n_items));
-}
-
-// Waits until this wave's LDS operations are done, then joins the work-group
-// barrier.  Unlike __syncthreads() it does not wait for outstanding global
-// loads, so prefetched B rows stay in flight across the barrier.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
-    __builtin_amdgcn_s_barrier();
-}
 
 // One pipeline stage: the gathered B rows and the A fragments of one k' step.
 template <int MT, int DW>
@@ -195,10 +70,6 @@ constexpr int pipe_depth()
     constexpr int ring = (budget - acc) / stage;  // stages that fit
     return ring >= 4 ? 3 : ring >= 2 ? ring - 1 : 1;
 }
-
-// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: expcnt and lgkmcnt at
-// their maxima, vmcnt split over bits 3:0 and 15:14).
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Stores the V results of one row of one lane (V adjacent columns) at byte
 // offset `off` of r; kOOB drops the store.  For a given V both the fp32 and the
@@ -674,7 +545,7 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
         return q < nblk ? J : 0xFFFFFFFFu;
     };
     // B rows of k' step s of block column J (half s%2): J*64 + 32*(s%2) + 8g + j
-    auto issue_b = [&](int s, uint32_t J, Stage<MT, DW> &st) {
+    auto issue_b = [&](int s, uint32_t J, BStage<DW> &st) {
         const bool jv = J < nbc;
         const uint32_t r0 = (jv ? J : 0u) * BC + (uint32_t)(s & 1) * 32 + 8 * g;
 #pragma unroll
@@ -683,7 +554,7 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
             buf_load<DW>(rB, (jv & (r < k32)) ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
         }
     };
-    auto compute = [&](const Stage<MT, DW> &st, int buf, int half) {
+    auto compute = [&](const BStage<DW> &st, int buf, int half) {
         u32x4_t af[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -704,7 +575,7 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
 
     if (nblk > 0) {
         u32x4_t areg[CPT];
-        Stage<MT, DW> st0, st1;
+        BStage<DW> st0, st1;
         uint32_t Jcur = block_col(0);
         load_a(0, areg);
         issue_b(0, Jcur, st0);
