@@ -162,7 +162,8 @@ spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
                              size_t *workspace_bytes);
 
 /* Run: C = A * B, enqueued on `stream` (a hipStream_t; NULL = the null stream),
- * no host synchronisation.  d_B: k x N codes with leading dimension ldb; d_C:
+ * no host synchronisation.  d_B: k x N codes with leading dimension ldb (the
+ * kernels read no byte past element (k - 1) * ldb + N - 1); d_C:
  * m x N of c_dtype with leading dimension ldc.  Rows < m and columns < N of C
  * are overwritten (C is never read); rows without entries become 0.
  * Requirements (else UNSUPPORTED): d_B and d_C 16-byte aligned, ldb >= N and

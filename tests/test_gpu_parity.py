@@ -231,6 +231,63 @@ def test_ld_larger_than_n(ws):
     check(p, got[:, :64])
 
 
+@pytest.mark.parametrize("fmt", ["bcsr", "wcsr"])
+def test_b_extent_ends_at_last_element(ws, fmt):
+    """B with ldb > N in an allocation that ends right after element
+    (k - 1) * ldb + N - 1, NaN codes in every row's padding, k and N ragged with
+    respect to blocks and column tiles: nothing past N or past the end may reach C."""
+    m, k, N, ldb = 700, 650, 200, 264
+    if fmt == "bcsr":
+        p = synth.block_problem(m, k, N, 64, 64, 0.3, seed=41, ab_dtype="bf16", c_dtype="fp32")
+    else:
+        p = synth.random_problem(m, k, N, 0.03, seed=42, ab_dtype="fp16", c_dtype="fp32",
+                                 fmt="wcsr", b_row=16, b_col=8)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    nan_code = 0x7FC0 if p.ab_dtype == "bf16" else 0x7E00
+    flat = np.full((k - 1) * ldb + N, nan_code, dtype=np.uint16)
+    for r in range(k):
+        flat[r * ldb: r * ldb + N] = p.B[r]
+    dev = torch.from_numpy(flat.view(np.int16)).cuda()
+    B = torch.as_strided(dev, (k, N), (ldb, 1))
+    C = A.new_c()
+    C.fill_(float("nan"))
+    A.run(B, C)
+    torch.cuda.synchronize()
+    check(p, C.float().cpu().numpy().astype(np.float64))
+
+
+SWEEP_CASES = [
+    # m, k, N, block density, ab, c, ranges per XCD
+    (1280, 640, 4104, 0.25, "bf16", "bf16", 1),
+    (1280, 640, 4104, 0.25, "bf16", "fp32", 2),
+    (700, 600, 8192, 0.3, "fp16", "fp16", 1),
+    (640, 512, 4096, 0.95, "bf16", "bf16", 1),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bcsr64_sweep_kernel(ws, case, monkeypatch):
+    """The A-stationary 64x64 kernel: a ragged last column tile and empty column
+    ranges (N not a multiple of 8 tiles), one or two ranges per XCD, padded
+    leading dimensions, empty block rows and full (8-block) block rows."""
+    m, k, N, dens, ab, ct, H = case
+    monkeypatch.setenv("SPMM_FORCE_KERNEL", "3")
+    monkeypatch.setenv("SPMM_FORCE_RANGES_PER_XCD", str(H))
+    p = synth.block_problem(m, k, N, 64, 64, dens, seed=m + N + H, ab_dtype=ab, c_dtype=ct)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    assert A.plan.info()["kernel"] == 3
+    nblk = np.diff(A.h_ptr)
+    assert nblk.max() <= 8
+    B = A.device_b(p.B, padded=True)
+    C = A.new_c(padded=True)
+    C.fill_(float("nan"))
+    A.run(B, C)
+    torch.cuda.synchronize()
+    check(p, C.float().cpu().numpy().astype(np.float64))
+
+
 # --------------------------------------------------------------------------
 # the five workloads
 # --------------------------------------------------------------------------

@@ -35,7 +35,10 @@ struct spmm_plan_s {
     int64_t stored_entries;
     int V, waves_n, waves_k;
     int kernel;                 // 0: generic tile kernel, 1: BCSR 64x64 with LDS-shared A,
-                                // 2: BCSR 64x64, LDS-shared A and a deep B ring
+                                // 2: BCSR 64x64, LDS-shared A and a deep B ring,
+                                // 3: BCSR 64x64, A-stationary sweep over column ranges
+    int max_blocks;             // kernel 3: most blocks in a block row (LDS size)
+    int64_t n_ranges, range_tiles;  // kernel 3: column ranges (multiple of 8), tiles each
     int ring_depth;             // kernel 2: half-blocks of B in flight per wave
     int64_t tile_cols, n_col_tiles;
     size_t workspace;
@@ -198,7 +201,8 @@ spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int
         return fail(SPMM_ERR_UNSUPPORTED, "ldb must be below 2^23");
     if ((uint64_t)pl->k * (uint64_t)ldb * 2u >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "B (k * ldb * 2 bytes) must be smaller than 4 GiB - 256");
-    if (pl->kernel == 0 && (uint64_t)pl->b_row * (uint64_t)ldc * (pl->ct == SPMM_FP32 ? 4u : 2u) >= kMaxBBytes)
+    if ((pl->kernel == 0 || pl->kernel == 3) &&
+        (uint64_t)pl->b_row * (uint64_t)ldc * (pl->ct == SPMM_FP32 ? 4u : 2u) >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "b_row rows of C (b_row * ldc * element bytes) must be below 4 GiB");
     if (pl->workspace > 0 && (!ws || ((uintptr_t)ws & 15)))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "plan needs a 16-byte aligned workspace of %zu bytes",
@@ -237,7 +241,9 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.m = pl->m;
     p.k = pl->k;
     p.N = pl->N;
-    p.b_bytes = (uint64_t)pl->k * (uint64_t)ldb * 2u;
+    // the extent of B ends with column N - 1 of row k - 1: loads of columns past N
+    // in that row and of rows past k fall outside it and read zeros
+    p.b_bytes = pl->k > 0 ? ((uint64_t)(pl->k - 1) * (uint64_t)ldb + (uint64_t)pl->N) * 2u : 0u;
     p.n_items = pl->n_items;
     p.n_col_tiles = pl->n_col_tiles;
     p.b_col = pl->b_col;
@@ -251,7 +257,10 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.order = pl->order;
     p.lds_idx_ints = (int32_t)pl->lds_idx_ints;
     p.grid = pl->grid;
-    hipError_t e = pl->kernel == 2   ? launch_bcsr64_ring(pl->ab, pl->ring_depth, p, st)
+    p.n_ranges = pl->n_ranges;
+    p.range_tiles = pl->range_tiles;
+    hipError_t e = pl->kernel == 3   ? launch_bcsr64_sweep(pl->ab, pl->max_blocks, p, st)
+                   : pl->kernel == 2 ? launch_bcsr64_ring(pl->ab, pl->ring_depth, p, st)
                    : pl->kernel == 1 ? launch_bcsr64_lds(pl->ab, p, st)
                                      : launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, st);
     if (e != hipSuccess)
@@ -577,10 +586,37 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
     for (int64_t w = 0; w < nbr; ++w)
         max_blocks = std::max(max_blocks, h_block_row_ptr[w + 1] - h_block_row_ptr[w]);
     const bool b64 = b_row == 64 && b_col == 64;
-    pl->kernel = env_int("SPMM_FORCE_KERNEL", b64 && N >= 256 ? 1 : 0);
+    pl->max_blocks = max_blocks;
+    // Kernel 3 keeps a block row's A in LDS: two resident work-groups per CU
+    // (one per XCD slot pair) are what make each XCD's work-groups sweep the
+    // same B tiles together, so it needs every block row to fit twice per CU.
+    const int64_t tiles512 = ceil_div(N, 512);
+    const bool sweep_ok = b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 16 &&
+                          sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks)) >= 2;
+    pl->kernel = env_int("SPMM_FORCE_KERNEL", sweep_ok ? 3 : b64 && N >= 256 ? 1 : 0);
+    if (pl->kernel == 3 && !(b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 8))
+        pl->kernel = b64 && N >= 256 ? 1 : 0;
     if (pl->kernel == 2 && !(b64 && max_blocks <= 64))
         pl->kernel = 0;
-    if (pl->kernel == 2) {
+    if (pl->kernel == 3) {
+        pl->n_items = nbr;
+        pl->V = 8;
+        pl->waves_n = 4;
+        pl->waves_k = 1;
+        pl->tile_cols = 512;
+        pl->n_col_tiles = tiles512;
+        pl->workspace = 0;
+        pl->order = 0;
+        // Ranges of two column tiles: on the FFN shapes (N = 65536, 128 tiles)
+        // ranges of 1, 2, 4, 8 and 16 tiles measured 1540, 1430, 1660, 1730 and
+        // 1770 us (gate), 1530, 1410, 1580, 1620 and 1760 us (up); longer
+        // ranges amortise the A load over more tiles but let the work-groups of
+        // an XCD drift apart, so that fewer of them share each B tile in L2.
+        int64_t best_h = std::max<int64_t>(1, std::min<int64_t>(64, tiles512 / 16));
+        best_h = env_int("SPMM_FORCE_RANGES_PER_XCD", (int)best_h);
+        pl->n_ranges = 8 * std::max<int64_t>(1, best_h);
+        pl->range_tiles = ceil_div(tiles512, pl->n_ranges);
+    } else if (pl->kernel == 2) {
         pl->n_items = nbr;
         pl->V = 8;
         pl->waves_n = 4;
@@ -611,7 +647,7 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
             return s;
         }
     }
-    if (pl->n_items * pl->n_col_tiles > 0x7fffffff) {
+    if (pl->n_items * (pl->kernel == 3 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
     }
@@ -661,7 +697,7 @@ extern "C" spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
         free_plan(pl);
         return s;
     }
-    if (pl->n_items * pl->n_col_tiles > 0x7fffffff) {
+    if (pl->n_items * (pl->kernel == 3 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
     }

@@ -58,19 +58,18 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// fp32 -> bfloat16 code, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f)
-{
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return 0x7fc0u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-// fp32 -> binary16 code (hardware conversion, round to nearest even).
-__device__ __forceinline__ uint32_t f32_to_f16(float f)
+// Two fp32 results -> one word holding their 16-bit codes of type dt (low half
+// first), rounded to nearest even by the hardware conversions (gfx950 converts
+// a bfloat16 pair in one instruction; a NaN stays a NaN).
+__device__ __forceinline__ uint32_t pack2(int dt, float lo, float hi)
 {
-    return __builtin_bit_cast(uint16_t, (_Float16)f);
+    const f32x2_t v = {lo, hi};
+    if (dt == SPMM_BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
 }
 
 // Stores V consecutive results of one row as c_dtype (NT: non-temporal stores).
@@ -98,11 +97,8 @@ __device__ __forceinline__ void store_row(void *base, int64_t elem, int c_dtype,
     } else {
         uint32_t w[V / 2];
 #pragma unroll
-        for (int c = 0; c < V; c += 2) {
-            uint32_t lo = c_dtype == SPMM_BF16 ? f32_to_bf16(v[c]) : f32_to_f16(v[c]);
-            uint32_t hi = c_dtype == SPMM_BF16 ? f32_to_bf16(v[c + 1]) : f32_to_f16(v[c + 1]);
-            w[c / 2] = lo | (hi << 16);
-        }
+        for (int c = 0; c < V; c += 2)
+            w[c / 2] = pack2(c_dtype, v[c], v[c + 1]);
         uint16_t *d = reinterpret_cast<uint16_t *>(base) + elem;
         if constexpr (V == 8)
             st(reinterpret_cast<u32x4_t *>(d), u32x4_t{w[0], w[1], w[2], w[3]}, NT);

@@ -26,7 +26,7 @@ struct TileParams {
     int64_t ldc;
     float *partial;           // partial tiles [slot][R][N] (fp32)
     int64_t m, k, N;
-    uint64_t b_bytes;         // k * ldb * 2: bytes of B the kernel may read (< 2^32 - 256)
+    uint64_t b_bytes;         // ((k - 1) * ldb + N) * 2: bytes of B the kernel may read
     int64_t n_items;          // tasks (generic kernel) or block rows (LDS-A kernel)
     int64_t n_col_tiles;      // column tiles; work items = n_items * n_col_tiles
     int64_t grid;             // generic kernel: persistent work-groups
@@ -39,6 +39,8 @@ struct TileParams {
     int32_t order;            // LDS-A kernel: 0 XCD-contiguous, column-tile major; 1 launch order
     int32_t lds_idx_ints;     // generic kernel: ints of each LDS index buffer
     int32_t two_buffers;      // generic kernel: 0 if every work-group runs one entry (one buffer)
+    int64_t n_ranges;         // sweep kernel: column ranges (a multiple of 8)
+    int64_t range_tiles;      // sweep kernel: column tiles per range
 };
 
 struct MergeParams {
@@ -66,6 +68,15 @@ hipError_t launch_bcsr64_lds(int ab_dtype, const TileParams &p, hipStream_t stre
 // BCSR with 64x64 blocks, one work-group of 4 waves x 128 columns per CU, a ring
 // of depth (3 or 5) half-blocks of B loads in flight per wave; at most 64 blocks
 // per block row (tile_cols = 512).
+// Most blocks in a block row that the sweep kernel holds in LDS.
+constexpr int kSweepMaxBlocks = 8;
+// BCSR with 64x64 blocks, A-stationary: n_items block rows x n_ranges column
+// ranges of range_tiles tiles of 512 columns, 4 waves, every block of a block row
+// in LDS (max_blocks <= kSweepMaxBlocks, tile_cols = 512).
+hipError_t launch_bcsr64_sweep(int ab_dtype, int max_blocks, const TileParams &p, hipStream_t stream);
+size_t sweep_lds_bytes(int max_blocks);
+// Work-groups of the sweep kernel resident per CU (0 if the query fails).
+int sweep_blocks_per_cu(int ab_dtype, int max_blocks);
 hipError_t launch_bcsr64_ring(int ab_dtype, int depth, const TileParams &p, hipStream_t stream);
 
 }  // namespace wspmm

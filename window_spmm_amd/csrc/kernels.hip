@@ -71,6 +71,54 @@ constexpr int pipe_depth()
     return ring >= 4 ? 3 : ring >= 2 ? ring - 1 : 1;
 }
 
+// Stores the V results of one row of one lane at byte offset `off` of r as DT
+// (kOOB drops the store): V / 4 (fp32) or one (16-bit) store instructions,
+// non-temporal (C is written once; measured: it then displaces less of the B
+// rows that other work-groups still read from L2).
+template <int V, int DT>
+__device__ __forceinline__ void buf_store_row_dt(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *v)
+{
+    if constexpr (DT == SPMM_FP32) {
+#pragma unroll
+        for (int c = 0; c < V; c += 4)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4_t{__builtin_bit_cast(uint32_t, v[c]), __builtin_bit_cast(uint32_t, v[c + 1]),
+                        __builtin_bit_cast(uint32_t, v[c + 2]), __builtin_bit_cast(uint32_t, v[c + 3])},
+                r, (int)(off == kOOB ? kOOB : off + 4 * c), 0, kNT);
+    } else {
+        static_assert(V == 8, "16-bit rows of 8 values: one 16-byte store");
+        u32x4_t w;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            w[c] = pack2(DT, v[2 * c], v[2 * c + 1]);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, kNT);
+    }
+}
+
+// Stores a 64-row accumulator tile of one lane as DT through rC (whose record 0
+// is row row0 of C): rows 4g+q of each 16-row slice mt, V adjacent columns from
+// ncol.  Rows past m and columns past N get out-of-range offsets.
+template <int DT, int MT, int V>
+__device__ __forceinline__ void store_acc_rows(const f32x4_t (&acc)[MT][V], __amdgpu_buffer_rsrc_t rC,
+                                               int g, int64_t row0, int64_t m, int64_t ldc,
+                                               int64_t ncol, int64_t N)
+{
+    constexpr int esz = DT == SPMM_FP32 ? 4 : 2;
+    const bool col_ok = ncol < N;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = mt * 16 + 4 * g + q;
+            float v[V];
+#pragma unroll
+            for (int c = 0; c < V; ++c)
+                v[c] = acc[mt][c][q];
+            const bool ok = col_ok & (row0 + r < m);
+            buf_store_row_dt<V, DT>(rC, ok ? (uint32_t)((r * ldc + ncol) * esz) : kOOB, v);
+        }
+}
+
 // Stores the V results of one row of one lane (V adjacent columns) at byte
 // offset `off` of r; kOOB drops the store.  For a given V both the fp32 and the
 // 16-bit forms issue the same number of store instructions, so wait counts on
@@ -95,11 +143,8 @@ __device__ __forceinline__ void buf_store_row(__amdgpu_buffer_rsrc_t r, uint32_t
     } else {
         uint32_t w[V / 2];
 #pragma unroll
-        for (int c = 0; c < V; c += 2) {
-            const uint32_t lo = dt == SPMM_BF16 ? f32_to_bf16(v[c]) : f32_to_f16(v[c]);
-            const uint32_t hi = dt == SPMM_BF16 ? f32_to_bf16(v[c + 1]) : f32_to_f16(v[c + 1]);
-            w[c / 2] = lo | (hi << 16);
-        }
+        for (int c = 0; c < V; c += 2)
+            w[c / 2] = pack2(dt, v[c], v[c + 1]);
         if constexpr (V == 8) {
             __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[0], w[1], w[2], w[3]}, r, (int)off, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b32(0u, r, (int)kOOB, 0, 0);  // count filler
@@ -620,6 +665,156 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
     }
 }
 
+// BCSR with 64 x 64 blocks, wide N and at most kSweepMaxBlocks blocks per
+// block row: the A blocks stay put and the B tiles move.  A work-group loads
+// every block of its block row into padded LDS rows once, then sweeps a
+// contiguous range of column tiles (NW waves x 128 columns each) with no
+// further barrier: per tile it zeroes its accumulators, walks the blocks with
+// the same two-stage B pipeline as bcsr64_lds_kernel (the pipeline runs on
+// across tile boundaries) and stores the tile.  Launch order deals work-groups
+// to the XCDs in turn; XCD x runs the column ranges x, x + 8, ... and, inside a
+// range, the block rows in order, so the work-groups resident on one XCD sweep
+// the same column tiles at about the same time and share each tile's B rows in
+// that XCD's L2, and A is read once per (block row, range).
+template <int AB, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
+{
+    constexpr int R = 64, BC = 64, MT = 4, V = 8, DW = 4;
+    constexpr int NT = NW * 64;
+    constexpr int STRIDE = BC * 2 + 16;            // padded LDS row: conflict-free b128 reads
+    constexpr int ABUF = R * STRIDE;               // bytes of one block in LDS
+    constexpr int CPB = R * BC / 8;                // 16-byte chunks per block
+    constexpr int MAXC = kSweepMaxBlocks * CPB / NT;  // chunks per thread, fullest row
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_a[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int li = lane & 15;
+
+    const uint32_t xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const uint32_t h = local / (uint32_t)p.n_items;
+    const uint32_t item = __builtin_amdgcn_readfirstlane(local - h * (uint32_t)p.n_items);
+    const int64_t t_begin = (int64_t)(h * 8 + xcd) * p.range_tiles;
+    const int64_t t_end = t_begin + p.range_tiles < p.n_col_tiles ? t_begin + p.range_tiles
+                                                                  : p.n_col_tiles;
+    if (t_begin >= t_end)
+        return;  // the whole work-group
+    const int ntiles = (int)(t_end - t_begin);
+    const int64_t blk0 = p.row_ptr[item];
+    const int nblk = p.row_ptr[item + 1] - (int)blk0;  // <= kSweepMaxBlocks (the plan checks)
+    const int64_t row0 = (int64_t)item * R;
+
+    // the block row's A blocks -> LDS: every load in flight before the first store
+    {
+        const __amdgpu_buffer_rsrc_t rA =
+            make_rsrc(p.A + blk0 * R * BC, (uint32_t)(nblk * R * BC * 2));
+        const int nchunks = nblk * CPB;
+        u32x4_t v[MAXC];
+#pragma unroll
+        for (int t = 0; t < MAXC; ++t) {
+            const int c = threadIdx.x + t * NT;
+            v[t] = __builtin_amdgcn_raw_buffer_load_b128(rA, c < nchunks ? c * 16 : (int)kOOB, 0, kNT);
+        }
+#pragma unroll
+        for (int t = 0; t < MAXC; ++t) {
+            const int c = threadIdx.x + t * NT;
+            if (c < nchunks)
+                *reinterpret_cast<u32x4_t *>(lds_a + (c / CPB) * ABUF + ((c % CPB) >> 3) * STRIDE +
+                                             (c & 7) * 16) = v[t];
+        }
+    }
+    // block columns of the block row: lane q holds block q
+    const __amdgpu_buffer_rsrc_t rJ = make_rsrc(p.col_idx + blk0, (uint32_t)nblk * 4u);
+    const uint32_t vcols = __builtin_amdgcn_raw_buffer_load_b32(rJ, (uint32_t)lane * 4u, 0, 0);
+    __syncthreads();
+
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B, (uint32_t)p.b_bytes);
+    const uint32_t ldb2 = (uint32_t)p.ldb * 2;
+    const uint32_t k32 = (uint32_t)p.k;
+    const uint32_t nbc = (uint32_t)((p.k + BC - 1) / BC);
+    const uint32_t lane_col = (uint32_t)(wave * 16 * V + li * V);  // column inside a tile
+    const int64_t col_first = t_begin * p.tile_cols + lane_col;     // this lane, first tile
+    const uint32_t tile_bytes = (uint32_t)p.tile_cols * 2;
+    const int esz = p.c_dtype == SPMM_FP32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc((uint8_t *)p.C + row0 * p.ldc * esz, (uint32_t)(R * p.ldc * esz));
+
+    f32x4_t acc[MT][V];
+    // B rows of half `half` of block q in tile t: J*64 + 32*half + 8g + j; tile
+    // ntiles (past the range) loads nothing
+    auto issue_b = [&](int t, int q, int half, BStage<DW> &st) {
+        const uint32_t J = (uint32_t)__builtin_amdgcn_readlane((int)vcols, q);
+        const bool jv = (t < ntiles) & (J < nbc);
+        const uint32_t r0 = (jv ? J : 0u) * BC + (uint32_t)half * 32 + 8 * g;
+        const uint32_t base = r0 * ldb2 + (uint32_t)col_first * 2 + (uint32_t)t * tile_bytes;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            buf_load<DW>(rB, (jv & (r0 + j < k32)) ? base + (uint32_t)j * ldb2 : kOOB, st.b[j]);
+    };
+    auto compute = [&](const BStage<DW> &st, int q, int half) {
+        u32x4_t af[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            af[mt] = *reinterpret_cast<const u32x4_t *>(lds_a + q * ABUF + (mt * 16 + li) * STRIDE +
+                                                       (half * 32 + 8 * g) * 2);
+#pragma unroll
+        for (int c = 0; c < V; ++c) {
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            u32x4_t bf;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                bf[qq] = __builtin_amdgcn_perm(st.b[2 * qq + 1][c >> 1], st.b[2 * qq][c >> 1], sel);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt][c] = mfma16x16x32<AB>(af[mt], bf, acc[mt][c]);
+        }
+    };
+    // stores tile t (one branch on C's type per tile)
+    auto store_tile = [&](int t) {
+        const int64_t ncol = col_first + (int64_t)t * p.tile_cols;
+        if (p.c_dtype == SPMM_FP32)
+            store_acc_rows<SPMM_FP32>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
+        else if (p.c_dtype == SPMM_BF16)
+            store_acc_rows<SPMM_BF16>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
+        else
+            store_acc_rows<SPMM_FP16>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
+    };
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int c = 0; c < V; ++c)
+                acc[mt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    };
+
+    if (nblk == 0) {  // empty block row: zero tiles
+        zero_acc();
+        for (int t = 0; t < ntiles; ++t)
+            store_tile(t);
+        return;
+    }
+    BStage<DW> st0, st1;
+    issue_b(0, 0, 0, st0);
+    for (int t = 0; t < ntiles; ++t) {
+        zero_acc();
+        for (int q = 0; q < nblk; ++q) {
+            // first half of block q (in st0): prefetch its second half
+            issue_b(t, q, 1, st1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st0, q, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // second half: prefetch the first half of the next block (or tile)
+            const bool lastq = q + 1 == nblk;
+            issue_b(lastq ? t + 1 : t, lastq ? 0 : q + 1, 0, st0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st1, q, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        store_tile(t);
+    }
+}
+
 // One work-group per (merge record, chunk of 256*8 tile elements): adds the
 // partial tiles of a split window in slot order and writes C once.
 __global__ __launch_bounds__(256) void wcsr_merge_kernel(MergeParams p)
@@ -703,6 +898,34 @@ hipError_t launch_bcsr64_lds(int ab, const TileParams &p, hipStream_t stream)
     else
         launch_lds_nw<4>(ab, p, stream);
     return hipGetLastError();
+}
+
+size_t sweep_lds_bytes(int max_blocks)
+{
+    return (size_t)max_blocks * 64 * (64 * 2 + 16);
+}
+
+static const void *sweep_fn(int ab)
+{
+    return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4>)
+                           : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4>);
+}
+
+hipError_t launch_bcsr64_sweep(int ab, int max_blocks, const TileParams &p, hipStream_t stream)
+{
+    TileParams arg = p;
+    void *args[] = {&arg};
+    return hipLaunchKernel(sweep_fn(ab), dim3((unsigned)(p.n_items * p.n_ranges)), dim3(256), args,
+                           sweep_lds_bytes(max_blocks), stream);
+}
+
+int sweep_blocks_per_cu(int ab, int max_blocks)
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sweep_fn(ab), 256,
+                                                     sweep_lds_bytes(max_blocks)) != hipSuccess)
+        return 0;
+    return n;
 }
 
 hipError_t launch_tiles(int fmt, int R, int V, int ab, const TileParams &p, hipStream_t stream)
