@@ -116,6 +116,37 @@ spmm_status_t spmm_wcsr_split_count(int64_t n_windows, const int32_t *h_window_r
 spmm_status_t spmm_wcsr_split(int64_t n_windows, const int32_t *h_window_row_ptr,
                               int64_t split_cols, int32_t *h_tasks, int32_t *h_merges);
 
+/* Reordering before the formats are built (Section IV-A: each evaluation
+ * matrix is first reordered with reverse Cuthill-McKee, which clusters
+ * nonzeros near the diagonal; Cuthill and McKee, "Reducing the bandwidth of
+ * sparse symmetric matrices", 1969, with the numbering reversed).
+ *
+ * spmm_rcm_order: A is a square n x n CSR pattern (values not needed); the graph
+ * is pattern(A) + pattern(A)^T without self loops.  h_perm[n] receives the
+ * order: new position i holds old vertex h_perm[i].  The order is fixed by
+ * these rules: components are numbered one after another, each starting from
+ * the unplaced vertex of least degree (then least index), moved to a
+ * pseudo-peripheral vertex by George and Liu's search (repeatedly root a level
+ * structure at the least-degree, then least-index, vertex of the current last
+ * level while that makes the structure taller); inside a component, vertices
+ * are numbered breadth first and the unplaced neighbours of each vertex are
+ * numbered by increasing degree, then index; finally the whole numbering is
+ * reversed.  BAD_FORMAT / INVALID_ARGUMENT as for the builders;
+ * UNSUPPORTED if n >= 2^31.
+ *
+ * spmm_csr_permute: the symmetric permutation A' = P A P^T of a square CSR
+ * matrix: entry (h_perm[i], h_perm[j]) of A becomes entry (i, j) of A'.
+ * Outputs h_out_row_ptr[n+1], h_out_col_idx[nnz], h_out_values[nnz] (columns
+ * increasing in each row; codes copied bit-exactly).  With A' and B' = P B
+ * (row i of B' = row h_perm[i] of B), C' = A' B' = P C: row i of C' is row
+ * h_perm[i] of C.  INVALID_ARGUMENT if h_perm is not a permutation of 0..n-1. */
+spmm_status_t spmm_rcm_order(int64_t n, const int32_t *h_row_ptr, const int32_t *h_col_idx,
+                             int32_t *h_perm);
+spmm_status_t spmm_csr_permute(int64_t n, const int32_t *h_row_ptr, const int32_t *h_col_idx,
+                               const uint16_t *h_values, const int32_t *h_perm,
+                               int32_t *h_out_row_ptr, int32_t *h_out_col_idx,
+                               uint16_t *h_out_values);
+
 /* ---------------------------------------------------------------------------
  * Plans.  A plan validates the format's host row pointer, picks the kernel
  * configuration for (format, b_row, b_col, N, dtypes), copies the small

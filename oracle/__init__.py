@@ -19,6 +19,8 @@ Asynchronous GPU Architectures"):
   cut into fixed-size sub-tasks, and one task descriptor per thread block).
 * ``within_tolerance`` -- the acceptance test |C_gpu - C| <= tol * Bound.
 * ``dense_bruteforce`` -- a dense triple loop for tiny inputs.
+* ``rcm_order`` / ``permute_symmetric`` / ``bandwidth`` -- reverse
+  Cuthill-McKee reordering, the preprocessing of Section IV-A (``reorder.py``).
 """
 
 from .reference import (  # noqa: F401
@@ -35,3 +37,4 @@ from .reference import (  # noqa: F401
     wcsr_tasks,
     within_tolerance,
 )
+from .reorder import bandwidth, permute_symmetric, rcm_order  # noqa: F401,E402

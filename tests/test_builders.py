@@ -142,3 +142,84 @@ def test_builder_rejects_bad_csr():
 def test_split_rejects_bad_t():
     assert _err(lambda: ws.wcsr_split(np.array([0, 8], np.int32), 48)) == ws.ERR_INVALID_ARGUMENT
     assert _err(lambda: ws.wcsr_split(np.array([0, 8, 0], np.int32), 32)) == ws.ERR_BAD_FORMAT
+
+
+# --------------------------------------------------------------------------
+# reverse Cuthill-McKee and the symmetric permutation (Section IV-A)
+# --------------------------------------------------------------------------
+
+def _random_square(n, density, seed, components=1):
+    """Unsymmetric random pattern; with components > 1, block diagonal (no
+    edges between the parts) plus a few isolated vertices."""
+    rng = np.random.default_rng(seed)
+    dense = np.zeros((n, n), bool)
+    cuts = np.linspace(0, n - 3 if n > 6 else n, components + 1).astype(int)
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        dense[a:b, a:b] = rng.random((b - a, b - a)) < density
+    rows, cols = np.nonzero(dense)
+    row_ptr = np.searchsorted(rows, np.arange(n + 1)).astype(np.int32)
+    vals = rng.integers(1, 0x7BFF, size=rows.size).astype(np.uint16)
+    return row_ptr, cols.astype(np.int32), vals
+
+
+@pytest.mark.parametrize("n,density,seed,parts", [(1, 0.5, 0, 1), (9, 0.3, 1, 1), (200, 0.02, 2, 1),
+                                                  (500, 0.01, 3, 4), (1500, 0.004, 4, 2),
+                                                  (800, 0.0005, 5, 1)])
+def test_rcm_matches_oracle(n, density, seed, parts):
+    rp, ci, v = _random_square(n, density, seed, parts)
+    perm = ws.rcm_order(n, rp, ci)
+    assert np.array_equal(perm, oracle.rcm_order(n, rp, ci))
+    got = ws.csr_permute(n, rp, ci, v, perm)
+    want = oracle.permute_symmetric(n, rp, ci, v, perm)
+    assert _same(got, want)
+
+
+def test_rcm_hand_example_through_the_abi():
+    # path 1-2-3-4-5-6 with 0 hanging off 3 (worked by hand in the oracle pins)
+    rp = np.array([0, 1, 2, 3, 4, 5, 6, 6], np.int32)
+    ci = np.array([3, 2, 3, 4, 5, 6], np.int32)
+    assert ws.rcm_order(7, rp, ci).tolist() == [1, 2, 0, 3, 4, 5, 6]
+
+
+def test_rcm_recovers_a_shuffled_band_and_raises_wcsr_fill():
+    # banded pattern (half-width 1% of n, like the banded half of the SuiteSparse
+    # stand-ins), relabelled at random: RCM brings the union width per window
+    # back down (the effect the paper reorders for)
+    n, half = 4096, 40
+    rng = np.random.default_rng(11)
+    i = np.repeat(np.arange(n), 2 * half + 1)
+    j = i + np.tile(np.arange(-half, half + 1), n)
+    keep = (j >= 0) & (j < n) & (rng.random(i.size) < 0.25)
+    i, j = i[keep], j[keep]
+    orp = np.searchsorted(i, np.arange(n + 1)).astype(np.int32)
+    original = ws.csr_to_wcsr(n, n, orp, j.astype(np.int32), np.ones(j.size, np.uint16), 16, 8)[0][-1]
+    lab = rng.permutation(n)
+    dense_rows, dense_cols = lab[i], lab[j]
+    order = np.lexsort((dense_cols, dense_rows))
+    r, c = dense_rows[order], dense_cols[order]
+    rp = np.searchsorted(r, np.arange(n + 1)).astype(np.int32)
+    ci = c.astype(np.int32)
+    v = np.ones(ci.size, np.uint16) * 0x3C00
+    before = ws.csr_to_wcsr(n, n, rp, ci, v, 16, 8)[0][-1]
+    perm = ws.rcm_order(n, rp, ci)
+    prp, pci, pv = ws.csr_permute(n, rp, ci, v, perm)
+    after = ws.csr_to_wcsr(n, n, prp, pci, pv, 16, 8)[0][-1]
+    # shuffled, a window's union is nearly all of its rows' entries; after RCM it
+    # is about the original band's union again
+    assert after * 3 < before
+    assert after <= 1.25 * original
+    assert oracle.bandwidth(n, prp, pci) <= 4 * half
+
+
+def test_rcm_and_permute_reject_bad_input():
+    rp = np.array([0, 2, 1], np.int32)
+    with pytest.raises(ws.SpmmError, match="BAD_FORMAT"):
+        ws.rcm_order(2, rp, np.array([0, 1], np.int32))
+    rp = np.array([0, 1, 2], np.int32)
+    ci = np.array([1, 0], np.int32)
+    v = np.ones(2, np.uint16)
+    with pytest.raises(ws.SpmmError, match="INVALID_ARGUMENT"):
+        ws.csr_permute(2, rp, ci, v, np.array([0, 0], np.int32))
+    with pytest.raises(ws.SpmmError, match="INVALID_ARGUMENT"):
+        ws.csr_permute(2, rp, ci, v, np.array([0, 2], np.int32))
+    assert ws.rcm_order(0, np.zeros(1, np.int32), np.zeros(0, np.int32)).size == 0

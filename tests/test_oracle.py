@@ -347,3 +347,140 @@ def test_padding_arithmetic_printed_in_section_iv_c():
     assert round((1056 - 1024) / 1024, 2) == 0.03
     # 64-wide blocks take 64 / 16 = 4 k16 steps (Section III-A)
     assert 64 // 16 == 4
+
+
+# --------------------------------------------------------------------------
+# reverse Cuthill-McKee (Section IV-A preprocessing)
+# --------------------------------------------------------------------------
+
+def _csr_from_edges(n, edges):
+    rows = [set() for _ in range(n)]
+    for a, b in edges:
+        rows[a].add(b)
+    row_ptr = np.zeros(n + 1, np.int32)
+    cols = []
+    for i in range(n):
+        c = sorted(rows[i])
+        cols += c
+        row_ptr[i + 1] = row_ptr[i] + len(c)
+    return row_ptr, np.asarray(cols, np.int32)
+
+
+def _relabelled(n, edges, seed):
+    lab = np.random.default_rng(seed).permutation(n)
+    return [(int(lab[a]), int(lab[b])) for a, b in edges]
+
+
+def _bandwidth_after(n, row_ptr, col_idx, perm):
+    inv = np.empty(n, np.int64)
+    inv[perm] = np.arange(n)
+    bw = 0
+    for i in range(n):
+        for e in range(row_ptr[i], row_ptr[i + 1]):
+            bw = max(bw, abs(int(inv[i]) - int(inv[col_idx[e]])))
+    return bw
+
+
+def _is_permutation(perm, n):
+    return sorted(perm.tolist()) == list(range(n))
+
+
+def test_rcm_path_graph_gets_bandwidth_one():
+    # a path, relabelled at random and stored one-sided (upper entries only):
+    # any level-structure numbering from an end vertex is the path itself
+    n = 40
+    edges = _relabelled(n, [(i, i + 1) for i in range(n - 1)], seed=1)
+    rp, ci = _csr_from_edges(n, edges)
+    perm = oracle.rcm_order(n, rp, ci)
+    assert _is_permutation(perm, n)
+    assert _bandwidth_after(n, rp, ci, perm) == 1
+
+
+def test_rcm_cycle_gets_bandwidth_two():
+    # breadth-first levels of a cycle hold two vertices (one at the ends), and a
+    # cycle is not a path: the bandwidth is exactly 2
+    n = 33
+    edges = _relabelled(n, [(i, (i + 1) % n) for i in range(n)], seed=2)
+    edges += [(b, a) for a, b in edges]
+    rp, ci = _csr_from_edges(n, edges)
+    perm = oracle.rcm_order(n, rp, ci)
+    assert _is_permutation(perm, n)
+    assert _bandwidth_after(n, rp, ci, perm) == 2
+
+
+def test_rcm_full_band_is_recovered():
+    # full band of half-width b, relabelled: levels from an end vertex hold b
+    # consecutive original vertices, so the numbering's bandwidth is <= 2b - 1
+    n, b = 300, 7
+    edges = [(i, j) for i in range(n) for j in range(i + 1, min(n, i + b + 1))]
+    edges = _relabelled(n, edges, seed=3)
+    edges += [(q, p) for p, q in edges]
+    rp, ci = _csr_from_edges(n, edges)
+    perm = oracle.rcm_order(n, rp, ci)
+    assert _bandwidth_after(n, rp, ci, perm) <= 2 * b - 1
+
+
+def test_rcm_hand_examples():
+    # orders worked out by hand from the rules in oracle/reorder.py
+    # star with centre 3: start at leaf 0, then centre, then leaves by index; reversed
+    rp, ci = _csr_from_edges(6, [(3, v) for v in (0, 1, 2, 4, 5)])
+    assert oracle.rcm_order(6, rp, ci).tolist() == [5, 4, 2, 1, 3, 0]
+    # isolated 2 and 3 first, then component {0, 5} from 0, then path 4-1-6 from 4
+    rp, ci = _csr_from_edges(7, [(4, 1), (1, 6), (0, 5)])
+    assert oracle.rcm_order(7, rp, ci).tolist() == [6, 1, 4, 5, 0, 3, 2]
+    # path 1-2-3-4-5-6 with vertex 0 hanging off 3: the search starts at 0
+    # (height 4), moves to 6 (height 5), and 1 is no taller, so numbering starts
+    # at 6; at vertex 3 the neighbours go by degree: 0 (1) before 2 (2)
+    rp, ci = _csr_from_edges(7, [(1, 2), (2, 3), (3, 4), (4, 5), (5, 6), (0, 3)])
+    assert oracle.rcm_order(7, rp, ci).tolist() == [1, 2, 0, 3, 4, 5, 6]
+
+
+def test_rcm_numbering_is_breadth_first():
+    # reversed back, the numbering of each component lists its vertices level by
+    # level (distances from the first vertex never decrease), and every vertex
+    # after the first is adjacent to an earlier one
+    rng = np.random.default_rng(5)
+    n = 120
+    edges = [(int(a), int(b)) for a, b in rng.integers(0, n, size=(150, 2)) if a != b]
+    rp, ci = _csr_from_edges(n, edges)
+    adj = oracle.reorder.symmetric_adjacency(n, rp, ci)
+    order = oracle.rcm_order(n, rp, ci)[::-1].tolist()
+    seen = set()
+    i = 0
+    while i < n:
+        root = order[i]
+        dist = oracle.reorder._level_structure(adj, root)
+        comp = order[i:i + len(dist)]
+        assert set(comp) == set(dist)
+        d = [dist[v] for v in comp]
+        assert d == sorted(d)
+        for v in comp[1:]:
+            assert any(w in seen or w == root for w in adj[v] if dist[w] < dist[v])
+            seen.add(v)
+        seen.add(root)
+        i += len(dist)
+
+
+def test_symmetric_permutation_keeps_the_product():
+    # P9: with A' = P A P^T and B' = P B, C' = A' B' is P C (fp64, integer data: exact)
+    rng = np.random.default_rng(6)
+    n, N = 50, 6
+    dense = (rng.random((n, n)) < 0.08) * rng.integers(-3, 4, size=(n, n))
+    rows, cols = np.nonzero(dense)
+    row_ptr = np.searchsorted(rows, np.arange(n + 1)).astype(np.int32)
+    vals = np.asarray([oracle_encode16(float(dense[r, c])) for r, c in zip(rows, cols)], np.uint16)
+    B = rng.integers(-3, 4, size=(n, N)).astype(np.float16).view(np.uint16)
+    perm = oracle.rcm_order(n, row_ptr, cols.astype(np.int32))
+    p_ptr, p_col, p_val = oracle.permute_symmetric(n, row_ptr, cols, vals, perm)
+    C, _ = oracle.spmm(n, n, N, rows, cols, vals, B, "fp16")
+    prow = np.repeat(np.arange(n), np.diff(p_ptr))
+    Cp, _ = oracle.spmm(n, n, N, prow, p_col, p_val, np.ascontiguousarray(B[perm]), "fp16")
+    assert np.array_equal(Cp, C[perm])
+    # and the permuted pattern is the relabelled one
+    D = np.zeros((n, n))
+    D[prow, p_col] = oracle.decode16(p_val, "fp16")
+    assert np.array_equal(D, dense[np.ix_(perm, perm)])
+
+
+def oracle_encode16(x: float) -> int:
+    return int(np.asarray(x, np.float16).view(np.uint16))

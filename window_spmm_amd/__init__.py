@@ -35,7 +35,8 @@ EXPORTED = [
     "spmm_csr_to_bcsr_count", "spmm_csr_to_bcsr", "spmm_csr_to_wcsr_count", "spmm_csr_to_wcsr",
     "spmm_wcsr_split_count", "spmm_wcsr_split", "spmm_bcsr_plan", "spmm_wcsr_plan",
     "spmm_bcsr_run", "spmm_wcsr_run", "spmm_plan_info", "spmm_plan_destroy",
-    "spmm_status_string", "spmm_last_error", "spmm_recommended_ld",
+    "spmm_status_string", "spmm_last_error", "spmm_recommended_ld", "spmm_rcm_order",
+    "spmm_csr_permute",
 ]
 
 
@@ -62,6 +63,8 @@ _sigs = {
     "spmm_csr_to_wcsr": [_i64, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp],
     "spmm_wcsr_split_count": [_i64, _vp, _i64, _P64, _P64],
     "spmm_wcsr_split": [_i64, _vp, _i64, _vp, _vp],
+    "spmm_rcm_order": [_i64, _vp, _vp, _vp],
+    "spmm_csr_permute": [_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "spmm_bcsr_plan": [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                        ctypes.c_int, ctypes.c_int, _Psz],
     "spmm_wcsr_plan": [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
@@ -162,6 +165,28 @@ def wcsr_split(window_row_ptr, split_cols: int):
     merges = np.empty((nm.value, 3), np.int32)
     _check(_lib.spmm_wcsr_split(nw, _hp(wrp), split_cols, _hp(tasks), _hp(merges)), "spmm_wcsr_split")
     return tasks, merges
+
+
+def rcm_order(n: int, row_ptr, col_idx) -> np.ndarray:
+    """Reverse Cuthill-McKee order of a square CSR pattern: ``perm`` (int32[n]),
+    new position i holds old vertex perm[i] (rules in the C header)."""
+    rp, ci = _host(row_ptr, np.int32), _host(col_idx, np.int32)
+    perm = np.empty(n, np.int32)
+    _check(_lib.spmm_rcm_order(n, _hp(rp), _hp(ci), _hp(perm)), "spmm_rcm_order")
+    return perm
+
+
+def csr_permute(n: int, row_ptr, col_idx, values, perm):
+    """Symmetric permutation P A P^T of a square CSR matrix:
+    ``(row_ptr, col_idx, values)`` with entry (perm[i], perm[j]) moved to (i, j)."""
+    rp, ci = _host(row_ptr, np.int32), _host(col_idx, np.int32)
+    v, pm = _host(values, np.uint16), _host(perm, np.int32)
+    orp = np.empty(n + 1, np.int32)
+    oci = np.empty(ci.size, np.int32)
+    ov = np.empty(ci.size, np.uint16)
+    _check(_lib.spmm_csr_permute(n, _hp(rp), _hp(ci), _hp(v), _hp(pm), _hp(orp), _hp(oci), _hp(ov)),
+           "spmm_csr_permute")
+    return orp, oci, ov
 
 
 # --------------------------------------------------------------------------

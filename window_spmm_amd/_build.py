@@ -16,7 +16,7 @@ LIB = os.path.join(PKG, "libwindow_spmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["status.cpp", "formats.cpp"]
+HOST_SOURCES = ["status.cpp", "formats.cpp", "reorder.cpp"]
 HEADERS = ["common.h", "kernels.h", "device.h"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.

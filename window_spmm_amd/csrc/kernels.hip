@@ -830,13 +830,28 @@ __global__ __launch_bounds__(256) void wcsr_merge_kernel(MergeParams p)
     if (row >= p.m)
         return;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int t = 0; t < mr.z; ++t) {
-        const float *src = p.partial + ((int64_t)(mr.y + t) * p.R + r) * p.N + col;
-        f32x4_t a = *reinterpret_cast<const f32x4_t *>(src);
-        f32x4_t b = *reinterpret_cast<const f32x4_t *>(src + 4);
+    const float *src = p.partial + ((int64_t)mr.y * p.R + r) * p.N + col;
+    const int64_t slot_stride = (int64_t)p.R * p.N;
+    auto add = [&](const f32x4_t &a, const f32x4_t &b) {
         s[0] += a[0]; s[1] += a[1]; s[2] += a[2]; s[3] += a[3];
         s[4] += b[0]; s[5] += b[1]; s[6] += b[2]; s[7] += b[3];
+    };
+    // four slots' loads in flight at a time; the adds stay in slot order
+    int t = 0;
+    for (; t + 4 <= mr.z; t += 4) {
+        f32x4_t a[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            a[u] = *reinterpret_cast<const f32x4_t *>(src + (t + u) * slot_stride);
+            b[u] = *reinterpret_cast<const f32x4_t *>(src + (t + u) * slot_stride + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            add(a[u], b[u]);
     }
+    for (; t < mr.z; ++t)
+        add(*reinterpret_cast<const f32x4_t *>(src + t * slot_stride),
+            *reinterpret_cast<const f32x4_t *>(src + t * slot_stride + 4));
     store_row<8>(p.C, row * p.ldc + col, p.c_dtype, s);
 }
 
