@@ -238,7 +238,7 @@ def main():
     roof["traffic"] = measured_traffic(key)
     roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["kernel_us"] = t_kernel * 1e6
-    roof["kernels"] = {1: "bcsr64_lds_kernel", 2: "bcsr64_ring_kernel", 3: "bcsr64_sweep_kernel"}.get(info["kernel"], "spmm_tile_kernel") + \
+    roof["kernels"] = {1: "bcsr64_lds_kernel", 2: "bcsr64_sweep_kernel"}.get(info["kernel"], "spmm_tile_kernel") + \
         (" + wcsr_merge_kernel" if info["n_merges"] else "")
 
     value = alg["flops_true"] / (ms_step / 1e3) / 1e12

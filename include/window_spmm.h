@@ -52,7 +52,8 @@ typedef struct {
     int32_t waves_n;         /* waves splitting the tile's columns */
     int32_t waves_k;         /* waves splitting the reduction (packed columns) */
     int32_t cols_per_lane;   /* adjacent C columns each lane accumulates (V) */
-    int32_t kernel;          /* 0: generic tile kernel; 1: BCSR 64x64 kernel with LDS-shared A */
+    int32_t kernel;          /* 0: generic tile kernel; 1: BCSR 64x64 kernel with LDS-shared A;
+                                2: BCSR 64x64 A-stationary sweep kernel */
     int32_t reserved;
     int64_t split_cols;      /* sub-task size T in packed columns (0: whole block rows) */
     int64_t n_tasks;         /* tasks (= work-groups per column tile; 0: whole block rows) */

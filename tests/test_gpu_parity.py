@@ -290,12 +290,12 @@ def test_bcsr64_sweep_kernel(ws, case, monkeypatch):
     ranges (N not a multiple of 8 tiles), one or two ranges per XCD, padded
     leading dimensions, empty block rows and full (8-block) block rows."""
     m, k, N, dens, ab, ct, H = case
-    monkeypatch.setenv("SPMM_FORCE_KERNEL", "3")
+    monkeypatch.setenv("SPMM_FORCE_KERNEL", "2")
     monkeypatch.setenv("SPMM_FORCE_RANGES_PER_XCD", str(H))
     p = synth.block_problem(m, k, N, 64, 64, dens, seed=m + N + H, ab_dtype=ab, c_dtype=ct)
     A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
                         p.ab_dtype, p.c_dtype)
-    assert A.plan.info()["kernel"] == 3
+    assert A.plan.info()["kernel"] == 2
     nblk = np.diff(A.h_ptr)
     assert nblk.max() <= 8
     B = A.device_b(p.B, padded=True)
@@ -358,18 +358,15 @@ def test_config5_sampled(ws):
     check(p, got, rows=rows)
 
 
-@pytest.mark.parametrize("env", [{"SPMM_FORCE_KERNEL": "2", "SPMM_FORCE_RING_DEPTH": "5"},
-                                 {"SPMM_FORCE_KERNEL": "2", "SPMM_FORCE_RING_DEPTH": "3"},
-                                 {"SPMM_FORCE_KERNEL": "2", "SPMM_FORCE_ORDER": "0"},
-                                 {"SPMM_FORCE_KERNEL": "1", "SPMM_FORCE_WAVES_N": "2"},
+@pytest.mark.parametrize("env", [{"SPMM_FORCE_KERNEL": "1", "SPMM_FORCE_WAVES_N": "2"},
                                  {"SPMM_FORCE_KERNEL": "1", "SPMM_FORCE_WAVES_N": "4"},
+                                 {"SPMM_FORCE_KERNEL": "1", "SPMM_FORCE_ORDER": "1"},
                                  {"SPMM_FORCE_KERNEL": "0"}],
                          ids=lambda e: "-".join("%s%s" % (k[11:].lower(), v) for k, v in e.items()))
 def test_bcsr64_kernel_variants_padded_ld(ws, env, monkeypatch):
-    """The 64x64-block kernels (the deep-ring kernel at both depths and both
-    work-group orders, the LDS-shared-A kernel at 2 or 4 waves, the generic one)
-    on a wide N with padded leading dimensions, a partial last column tile,
-    empty block rows and odd block counts."""
+    """The 64x64-block kernels (the LDS-shared-A kernel at 2 or 4 waves and in
+    launch order, the generic one) on a wide N with padded leading dimensions,
+    a partial last column tile, empty block rows and odd block counts."""
     for k_, v_ in env.items():
         monkeypatch.setenv(k_, v_)
     p = synth.block_problem(1280, 640, 1288, 64, 64, 0.25, seed=31, ab_dtype="bf16", c_dtype="bf16")

@@ -24,9 +24,8 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-I", INCLU
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
 # kernels.hip: MFMA accumulators stay in ordinary VGPRs (the unified register
 # file of gfx950), which avoids copies around its two-waves-per-SIMD loops.
-# kernels_lds.hip runs one wave per SIMD and keeps them in accumulation registers.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-HIP_SOURCES = [("kernels.hip", VGPR_FORM), ("kernels_lds.hip", []), ("api.hip", [])]
+HIP_SOURCES = [("kernels.hip", VGPR_FORM), ("api.hip", [])]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wextra"]
 
 

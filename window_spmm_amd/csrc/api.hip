@@ -35,11 +35,9 @@ struct spmm_plan_s {
     int64_t stored_entries;
     int V, waves_n, waves_k;
     int kernel;                 // 0: generic tile kernel, 1: BCSR 64x64 with LDS-shared A,
-                                // 2: BCSR 64x64, LDS-shared A and a deep B ring,
-                                // 3: BCSR 64x64, A-stationary sweep over column ranges
-    int max_blocks;             // kernel 3: most blocks in a block row (LDS size)
-    int64_t n_ranges, range_tiles;  // kernel 3: column ranges (multiple of 8), tiles each
-    int ring_depth;             // kernel 2: half-blocks of B in flight per wave
+                                // 2: BCSR 64x64, A-stationary sweep over column ranges
+    int max_blocks;             // kernel 2: most blocks in a block row (LDS size)
+    int64_t n_ranges, range_tiles;  // kernel 2: column ranges (multiple of 8), tiles each
     int64_t tile_cols, n_col_tiles;
     size_t workspace;
     int device;
@@ -201,7 +199,7 @@ spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int
         return fail(SPMM_ERR_UNSUPPORTED, "ldb must be below 2^23");
     if ((uint64_t)pl->k * (uint64_t)ldb * 2u >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "B (k * ldb * 2 bytes) must be smaller than 4 GiB - 256");
-    if ((pl->kernel == 0 || pl->kernel == 3) &&
+    if ((pl->kernel == 0 || pl->kernel == 1 || pl->kernel == 2) &&
         (uint64_t)pl->b_row * (uint64_t)ldc * (pl->ct == SPMM_FP32 ? 4u : 2u) >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "b_row rows of C (b_row * ldc * element bytes) must be below 4 GiB");
     if (pl->workspace > 0 && (!ws || ((uintptr_t)ws & 15)))
@@ -259,8 +257,7 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.grid = pl->grid;
     p.n_ranges = pl->n_ranges;
     p.range_tiles = pl->range_tiles;
-    hipError_t e = pl->kernel == 3   ? launch_bcsr64_sweep(pl->ab, pl->max_blocks, p, st)
-                   : pl->kernel == 2 ? launch_bcsr64_ring(pl->ab, pl->ring_depth, p, st)
+    hipError_t e = pl->kernel == 2   ? launch_bcsr64_sweep(pl->ab, pl->max_blocks, p, st)
                    : pl->kernel == 1 ? launch_bcsr64_lds(pl->ab, p, st)
                                      : launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, st);
     if (e != hipSuccess)
@@ -580,25 +577,22 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
         return s;
     }
     // 64x64 blocks and wide N: kernels that share each A block through LDS and
-    // walk whole block rows.  Kernel 2 (one work-group per CU, a deep ring of B
-    // loads) holds a block row's block columns in one register: <= 64 blocks.
+    // walk whole block rows.
     int max_blocks = 0;
     for (int64_t w = 0; w < nbr; ++w)
         max_blocks = std::max(max_blocks, h_block_row_ptr[w + 1] - h_block_row_ptr[w]);
     const bool b64 = b_row == 64 && b_col == 64;
     pl->max_blocks = max_blocks;
-    // Kernel 3 keeps a block row's A in LDS: two resident work-groups per CU
+    // Kernel 2 keeps a block row's A in LDS: two resident work-groups per CU
     // (one per XCD slot pair) are what make each XCD's work-groups sweep the
     // same B tiles together, so it needs every block row to fit twice per CU.
     const int64_t tiles512 = ceil_div(N, 512);
     const bool sweep_ok = b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 16 &&
                           sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks)) >= 2;
-    pl->kernel = env_int("SPMM_FORCE_KERNEL", sweep_ok ? 3 : b64 && N >= 256 ? 1 : 0);
-    if (pl->kernel == 3 && !(b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 8))
+    pl->kernel = env_int("SPMM_FORCE_KERNEL", sweep_ok ? 2 : b64 && N >= 256 ? 1 : 0);
+    if (pl->kernel == 2 && !(b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 8))
         pl->kernel = b64 && N >= 256 ? 1 : 0;
-    if (pl->kernel == 2 && !(b64 && max_blocks <= 64))
-        pl->kernel = 0;
-    if (pl->kernel == 3) {
+    if (pl->kernel == 2) {
         pl->n_items = nbr;
         pl->V = 8;
         pl->waves_n = 4;
@@ -616,16 +610,6 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
         best_h = env_int("SPMM_FORCE_RANGES_PER_XCD", (int)best_h);
         pl->n_ranges = 8 * std::max<int64_t>(1, best_h);
         pl->range_tiles = ceil_div(tiles512, pl->n_ranges);
-    } else if (pl->kernel == 2) {
-        pl->n_items = nbr;
-        pl->V = 8;
-        pl->waves_n = 4;
-        pl->waves_k = 1;
-        pl->tile_cols = 512;
-        pl->n_col_tiles = ceil_div(N, pl->tile_cols);
-        pl->workspace = 0;
-        pl->ring_depth = env_int("SPMM_FORCE_RING_DEPTH", 5) == 3 ? 3 : 5;
-        pl->order = env_int("SPMM_FORCE_ORDER", 1) ? 1 : 0;
     } else if (pl->kernel == 1 && b64) {
         const int nw = env_int("SPMM_FORCE_WAVES_N", 4) == 2 ? 2 : 4;
         pl->n_items = nbr;
@@ -647,7 +631,7 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
             return s;
         }
     }
-    if (pl->n_items * (pl->kernel == 3 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
+    if (pl->n_items * (pl->kernel == 2 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
     }
@@ -697,7 +681,7 @@ extern "C" spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
         free_plan(pl);
         return s;
     }
-    if (pl->n_items * (pl->kernel == 3 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
+    if (pl->n_items * (pl->kernel == 2 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
     }

@@ -65,9 +65,6 @@ hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stre
 // BCSR with 64x64 blocks, waves_n (2 or 4) waves x 128 columns per work-group, A
 // shared through LDS (requires waves_k = 1, V = 8, tile_cols = 128 * waves_n).
 hipError_t launch_bcsr64_lds(int ab_dtype, const TileParams &p, hipStream_t stream);
-// BCSR with 64x64 blocks, one work-group of 4 waves x 128 columns per CU, a ring
-// of depth (3 or 5) half-blocks of B loads in flight per wave; at most 64 blocks
-// per block row (tile_cols = 512).
 // Most blocks in a block row that the sweep kernel holds in LDS.
 constexpr int kSweepMaxBlocks = 8;
 // BCSR with 64x64 blocks, A-stationary: n_items block rows x n_ranges column
@@ -77,6 +74,5 @@ hipError_t launch_bcsr64_sweep(int ab_dtype, int max_blocks, const TileParams &p
 size_t sweep_lds_bytes(int max_blocks);
 // Work-groups of the sweep kernel resident per CU (0 if the query fails).
 int sweep_blocks_per_cu(int ab_dtype, int max_blocks);
-hipError_t launch_bcsr64_ring(int ab_dtype, int depth, const TileParams &p, hipStream_t stream);
 
 }  // namespace wspmm

@@ -646,23 +646,17 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
         }
     }
 
-    // epilogue (non-temporal stores: C is written once)
+    // epilogue: one branch on C's type, non-temporal stores
     const int64_t ncol = col0 + li * V;
-    if (ncol >= p.N)
-        return;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = mt * 16 + 4 * g + q;
-            float v[V];
-#pragma unroll
-            for (int c = 0; c < V; ++c)
-                v[c] = acc[mt][c][q];
-            if (row0 + r < p.m)
-                store_row<V, true>(p.C, (row0 + r) * p.ldc + ncol, p.c_dtype, v);
-        }
-    }
+    const int esz = p.c_dtype == SPMM_FP32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc((uint8_t *)p.C + row0 * p.ldc * esz, (uint32_t)(R * p.ldc * esz));
+    if (p.c_dtype == SPMM_FP32)
+        store_acc_rows<SPMM_FP32>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
+    else if (p.c_dtype == SPMM_BF16)
+        store_acc_rows<SPMM_BF16>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
+    else
+        store_acc_rows<SPMM_FP16>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
 }
 
 // BCSR with 64 x 64 blocks, wide N and at most kSweepMaxBlocks blocks per
