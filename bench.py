@@ -144,6 +144,79 @@ def cpu_baseline(p, budget_s: float):
                       "%.2f s each" % (n_rows - 1, r.size, p.N, reps, t)}
 
 
+def sweep_candidates(p):
+    """Plan options to time: the 64x64 kernels' variants, then the generic
+    kernel's tile shapes (columns per lane x waves across N x waves along the
+    packed columns) with both ways of handing out tasks."""
+    cands = []
+    if p.fmt == "bcsr" and p.b_row == 64 and p.b_col == 64:
+        cands += [{"kernel": 1, "waves_n": wn, "order": o} for wn in (2, 4) for o in (0, 1)]
+        cands += [{"kernel": 2, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16)]
+    for V in (2, 4, 8):
+        if V == 8 and p.b_row >= 32:
+            continue
+        for wn, wk in ((1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (4, 1)):
+            for dist in (0, 1):
+                cands.append({"kernel": 0, "cols_per_lane": V, "waves_n": wn, "waves_k": wk,
+                              "distribution": dist})
+    return cands
+
+
+def run_sweep(p, A, B, C, alg, workload):
+    """Times every candidate plan on the resident input (HIP events on the launch
+    stream), checks its C against the default plan's, prints a table and one
+    JSON summary line.  The measurement behind choosing a tile width, like the
+    paper's sweep over WGMMA_N (Section IV-C, Fig. 7)."""
+    import torch
+    import window_spmm_amd as ws
+    stream = torch.cuda.current_stream()
+
+    def time_plan(n):
+        for _ in range(3):
+            A.run(B, C, stream)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(n):
+            A.run(B, C, stream)
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n * 1e3
+
+    base_us = time_plan(20)
+    C_ref = C.float().clone()
+    scale = float(C_ref.abs().max()) or 1.0
+    rows = [("default", A.plan.info(), base_us, True)]
+    for opts in sweep_candidates(p):
+        try:
+            A.replan(opts)
+        except ws.SpmmError as exc:
+            rows.append((opts, None, None, str(exc).split(":")[1].strip()))
+            continue
+        us = time_plan(max(5, min(50, int(2e5 / max(base_us, 1.0)))))
+        same = bool(torch.allclose(C.float(), C_ref, rtol=1e-2, atol=1e-3 * scale))
+        rows.append((opts, A.plan.info(), us, same))
+    A.replan(None)
+    print("%-64s %6s %10s %9s %7s %s" % ("options", "tile", "us", "TFLOP/s", "frac", "C"))
+    best = None
+    for opts, info, us, same in rows:
+        if info is None:
+            print("%-64s %6s %10s %9s %7s %s" % (json.dumps(opts), "-", "-", "-", "-", same))
+            continue
+        tf = alg["flops_true"] / (us * 1e-6) / 1e12
+        t_roof = max(alg["flops_stored"] / (PEAK_MFMA_TFLOPS * 1e12), alg["bytes_alg"] / (PEAK_HBM_GBS * 1e9))
+        print("%-64s %6d %10.1f %9.1f %7.3f %s" % (json.dumps(opts) if opts != "default" else
+                                                  "default (kernel %d)" % info["kernel"],
+                                                  info["tile_cols"], us, tf, t_roof / (us * 1e-6),
+                                                  "same" if same is True else "DIFFERS"))
+        if same is True and opts != "default" and (best is None or us < best[1]):
+            best = (opts, us)
+    print(json.dumps({"sweep": workload, "default_us": base_us,
+                      "best_options": best[0] if best else None,
+                      "best_us": best[1] if best else None}))
+    if any(r[3] is False for r in rows):
+        raise SystemExit("a candidate plan's C differs from the default plan's")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +234,8 @@ def main():
     ap.add_argument("--no-pad", action="store_true", help="B and C with leading dimension N")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the kernel / tile-shape options on this workload instead")
     args = ap.parse_args()
 
     if args.copy_probe:
@@ -189,6 +264,9 @@ def main():
     B = A.device_b(p.B, dev, padded=not args.no_pad)
     C = A.new_c(dev, padded=not args.no_pad)
     alg = algorithmic(p, A)
+    if args.sweep:
+        run_sweep(p, A, B, C, alg, workload)
+        return
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):

@@ -54,7 +54,7 @@ typedef struct {
     int32_t cols_per_lane;   /* adjacent C columns each lane accumulates (V) */
     int32_t kernel;          /* 0: generic tile kernel; 1: BCSR 64x64 kernel with LDS-shared A;
                                 2: BCSR 64x64 A-stationary sweep kernel */
-    int32_t reserved;
+    int32_t ranges_per_xcd;  /* kernel 2: column ranges per XCD (0 otherwise) */
     int64_t split_cols;      /* sub-task size T in packed columns (0: whole block rows) */
     int64_t n_tasks;         /* tasks (= work-groups per column tile; 0: whole block rows) */
     int64_t n_merges;        /* row tiles split into more than one task */
@@ -169,6 +169,35 @@ spmm_status_t spmm_csr_permute(int64_t n, const int32_t *h_row_ptr, const int32_
  * none).
  * ------------------------------------------------------------------------- */
 
+/* Plan options.  The kernel and tile shape are normally chosen by the plan;
+ * these fields let a caller pin them, for a tile-width / wave-count sweep (the
+ * measurement behind the paper's choice of tile width, Section IV-C, Fig. 7)
+ * or to keep a configuration an autotuner found.  Each field's "auto" value
+ * leaves that choice to the plan; spmm_plan_options_default() sets all of them.
+ * A value outside its range is INVALID_ARGUMENT; a kernel that cannot run the
+ * problem (see each kernel) is UNSUPPORTED. */
+typedef struct {
+    int32_t kernel;          /* -1 auto; 0 generic tile kernel (any format and shape);
+                                1 BCSR 64x64 with LDS-shared A (b_row = b_col = 64, N >= 256);
+                                2 BCSR 64x64 A-stationary sweep (b_row = b_col = 64,
+                                  N >= 4096, at most 8 blocks in every block row) */
+    int32_t cols_per_lane;   /* 0 auto; kernel 0: 2, 4 or 8 adjacent C columns per lane
+                                (8 only with b_row = 16) */
+    int32_t waves_n;         /* 0 auto; kernel 0: 1, 2 or 4 waves across the tile's
+                                columns; kernel 1: 2 or 4 */
+    int32_t waves_k;         /* 0 auto; kernel 0: 1, 2 or 4 waves splitting the packed
+                                columns, waves_n * waves_k <= 4 */
+    int32_t distribution;    /* -1 auto; kernel 0: 0 planned per-work-group task lists,
+                                1 one work-group per task (hardware dispatch) */
+    int32_t row_order;       /* -1 auto; kernel 0 with distribution 1: 0 longest task
+                                first, 1 row order with a contiguous range per XCD */
+    int32_t order;           /* -1 auto; kernel 1: 0 column-tile major with a contiguous
+                                range per XCD, 1 launch order */
+    int32_t ranges_per_xcd;  /* 0 auto; kernel 2: column ranges per XCD, 1 to 64 */
+} spmm_plan_options_t;
+
+void spmm_plan_options_default(spmm_plan_options_t *opt);
+
 /* BCSR plan.  h_block_row_ptr[ceil(m/b_row)+1] (host, read during the call);
  * d_block_col_idx[nnz_blocks], d_blocks[nnz_blocks*b_row*b_col] (device).
  * Block-column indices are not read on the host; an index whose block lies
@@ -180,6 +209,12 @@ spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
                              int32_t b_col, const int32_t *h_block_row_ptr,
                              const int32_t *d_block_col_idx, const void *d_blocks,
                              spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype, size_t *workspace_bytes);
+/* The same with options (NULL: all automatic, as spmm_bcsr_plan). */
+spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
+                                int32_t b_col, const int32_t *h_block_row_ptr,
+                                const int32_t *d_block_col_idx, const void *d_blocks,
+                                spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
+                                const spmm_plan_options_t *options, size_t *workspace_bytes);
 
 /* WCSR plan.  h_window_row_ptr[ceil(m/b_row)+1] (host; every window width a
  * multiple of b_col, else BAD_FORMAT); d_window_col_idx[P], d_values[b_row*P]
@@ -192,6 +227,13 @@ spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
                              const int32_t *d_window_col_idx, const void *d_values,
                              spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype, int64_t split_cols,
                              size_t *workspace_bytes);
+/* The same with options (NULL: all automatic, as spmm_wcsr_plan); kernel must
+ * be -1 or 0. */
+spmm_status_t spmm_wcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
+                                int32_t b_col, const int32_t *h_window_row_ptr,
+                                const int32_t *d_window_col_idx, const void *d_values,
+                                spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype, int64_t split_cols,
+                                const spmm_plan_options_t *options, size_t *workspace_bytes);
 
 /* Run: C = A * B, enqueued on `stream` (a hipStream_t; NULL = the null stream),
  * no host synchronisation.  d_B: k x N codes with leading dimension ldb (the

@@ -18,7 +18,7 @@ def _declared():
     for fn in os.listdir(os.path.join(ROOT, "include")):
         if fn.endswith(".h"):
             text = open(os.path.join(ROOT, "include", fn)).read()
-            names |= set(re.findall(r"^\s*(?:spmm_status_t|const char \*|int64_t)\s*(spmm_\w+)\s*\(", text, re.M))
+            names |= set(re.findall(r"^\s*(?:spmm_status_t|const char \*|int64_t|void)\s*(spmm_\w+)\s*\(", text, re.M))
     return names
 
 
@@ -90,3 +90,24 @@ def test_recommended_ld():
     assert ws.recommended_ld(1000, 2) == 1000
     assert ws.recommended_ld(1001, 2) == 1008
     assert ws.recommended_ld(0, 2) == 0
+
+
+def test_plan_options_default_and_checks():
+    """Option fields are range-checked before any device work (CPU-only
+    check: these plans fail with INVALID_ARGUMENT, not a HIP error)."""
+    o = ws.PlanOptions()
+    ws._lib.spmm_plan_options_default(ctypes.byref(o))
+    assert {n: getattr(o, n) for n, _ in o._fields_} == ws.PlanOptions.AUTO
+    rp = np.array([0, 1], np.int32)
+    bad = [{"kernel": 3}, {"kernel": -2}, {"cols_per_lane": 3}, {"waves_n": 3},
+           {"waves_n": 4, "waves_k": 2}, {"distribution": 2}, {"order": -3},
+           {"ranges_per_xcd": 65}, {"row_order": 5}]
+    for opts in bad:
+        with pytest.raises(ws.SpmmError, match="INVALID_ARGUMENT"):
+            ws.bcsr_plan(64, 64, 64, 64, 64, rp, 16, 32, "bf16", "fp32", options=opts)
+    # WCSR has only the generic kernel
+    with pytest.raises(ws.SpmmError, match="INVALID_ARGUMENT"):
+        ws.wcsr_plan(16, 64, 64, 16, 8, np.array([0, 8], np.int32), 16, 32, "fp16", "fp32",
+                     options={"kernel": 1})
+    with pytest.raises(ValueError):
+        ws.PlanOptions.of({"tile": 3})

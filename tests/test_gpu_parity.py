@@ -208,12 +208,12 @@ def test_wcsr_split_invariance_and_determinism(ws):
 
 @pytest.mark.parametrize("source", ["lists", "spread"])
 @pytest.mark.parametrize("fmt", ["wcsr", "bcsr"])
-def test_work_sources_repeated_launches(ws, fmt, source, monkeypatch):
+def test_work_sources_repeated_launches(ws, fmt, source):
     """Both ways of handing tasks to the work-groups (a list of several tasks
     per persistent work-group, or one task per work-group left to the hardware
     dispatcher) give the oracle's result and the same bits on every one of
     many launches of one plan."""
-    monkeypatch.setenv("SPMM_FORCE_SPREAD", "1" if source == "spread" else "0")
+    opts = {"distribution": 1 if source == "spread" else 0}
     if fmt == "wcsr":
         p = synth.random_problem(1500, 5000, 136, 0.03, seed=21, ab_dtype="fp16", c_dtype="fp32",
                                  fmt="wcsr", b_row=16, b_col=8)
@@ -223,7 +223,7 @@ def test_work_sources_repeated_launches(ws, fmt, source, monkeypatch):
                                  fmt="bcsr", b_row=32, b_col=16)
         split = 0
     A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
-                        p.ab_dtype, p.c_dtype, split_cols=split)
+                        p.ab_dtype, p.c_dtype, split_cols=split, options=opts)
     outs = run_gpu(ws, p, A=A, repeats=12)
     assert all(np.array_equal(o, outs[0]) for o in outs[1:])
     check(p, outs[0])
@@ -285,17 +285,16 @@ SWEEP_CASES = [
 
 
 @pytest.mark.parametrize("case", SWEEP_CASES, ids=lambda c: "x".join(map(str, c)))
-def test_bcsr64_sweep_kernel(ws, case, monkeypatch):
+def test_bcsr64_sweep_kernel(ws, case):
     """The A-stationary 64x64 kernel: a ragged last column tile and empty column
     ranges (N not a multiple of 8 tiles), one or two ranges per XCD, padded
     leading dimensions, empty block rows and full (8-block) block rows."""
     m, k, N, dens, ab, ct, H = case
-    monkeypatch.setenv("SPMM_FORCE_KERNEL", "2")
-    monkeypatch.setenv("SPMM_FORCE_RANGES_PER_XCD", str(H))
     p = synth.block_problem(m, k, N, 64, 64, dens, seed=m + N + H, ab_dtype=ab, c_dtype=ct)
     A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
-                        p.ab_dtype, p.c_dtype)
-    assert A.plan.info()["kernel"] == 2
+                        p.ab_dtype, p.c_dtype, options={"kernel": 2, "ranges_per_xcd": H})
+    info = A.plan.info()
+    assert info["kernel"] == 2 and info["ranges_per_xcd"] == H
     nblk = np.diff(A.h_ptr)
     assert nblk.max() <= 8
     B = A.device_b(p.B, padded=True)
@@ -358,22 +357,25 @@ def test_config5_sampled(ws):
     check(p, got, rows=rows)
 
 
-@pytest.mark.parametrize("env", [{"SPMM_FORCE_KERNEL": "1", "SPMM_FORCE_WAVES_N": "2"},
-                                 {"SPMM_FORCE_KERNEL": "1", "SPMM_FORCE_WAVES_N": "4"},
-                                 {"SPMM_FORCE_KERNEL": "1", "SPMM_FORCE_ORDER": "1"},
-                                 {"SPMM_FORCE_KERNEL": "0"}],
-                         ids=lambda e: "-".join("%s%s" % (k[11:].lower(), v) for k, v in e.items()))
-def test_bcsr64_kernel_variants_padded_ld(ws, env, monkeypatch):
+@pytest.mark.parametrize("opts", [{"kernel": 1, "waves_n": 2}, {"kernel": 1, "waves_n": 4},
+                                  {"kernel": 1, "order": 1}, {"kernel": 0},
+                                  {"kernel": 0, "waves_n": 1, "waves_k": 4},
+                                  {"kernel": 0, "cols_per_lane": 2, "waves_n": 4}],
+                         ids=lambda e: "-".join("%s%s" % (k, v) for k, v in e.items()))
+def test_bcsr64_kernel_variants_padded_ld(ws, opts):
     """The 64x64-block kernels (the LDS-shared-A kernel at 2 or 4 waves and in
-    launch order, the generic one) on a wide N with padded leading dimensions,
-    a partial last column tile, empty block rows and odd block counts."""
-    for k_, v_ in env.items():
-        monkeypatch.setenv(k_, v_)
+    launch order, the generic one at several tile shapes, all chosen through
+    plan options) on a wide N with padded leading dimensions, a partial last
+    column tile, empty block rows and odd block counts."""
     p = synth.block_problem(1280, 640, 1288, 64, 64, 0.25, seed=31, ab_dtype="bf16", c_dtype="bf16")
     A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
-                        p.ab_dtype, p.c_dtype)
+                        p.ab_dtype, p.c_dtype, options=opts)
     info = A.plan.info()
-    assert info["kernel"] == int(env["SPMM_FORCE_KERNEL"])
+    for name, value in opts.items():
+        if name in ("kernel", "waves_n", "waves_k"):
+            assert info[name] == value, (name, info)
+        if name == "cols_per_lane":
+            assert info["cols_per_lane"] == value
     nblk = np.diff(A.h_ptr)
     assert (nblk == 0).any() and (nblk % 2 == 1).any()
     B = A.device_b(p.B, padded=True)
@@ -382,3 +384,40 @@ def test_bcsr64_kernel_variants_padded_ld(ws, env, monkeypatch):
     A.run(B, C)
     torch.cuda.synchronize()
     check(p, C.float().cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("kind", ["wcsr16", "bcsr64", "bcsr32"])
+def test_every_sweep_candidate_matches_oracle(ws, kind):
+    """Every plan option set that `bench.py --sweep` times gives the oracle's
+    result (or is refused with UNSUPPORTED before anything runs)."""
+    import bench
+    if kind == "wcsr16":
+        p = synth.random_problem(400, 1500, 136, 0.03, seed=51, ab_dtype="fp16", c_dtype="fp32",
+                                 fmt="wcsr", b_row=16, b_col=8)
+    elif kind == "bcsr64":
+        p = synth.block_problem(330, 520, 4104, 64, 64, 0.3, seed=52, ab_dtype="bf16",
+                                c_dtype="bf16")
+    else:
+        p = synth.block_problem(300, 400, 200, 32, 16, 0.3, seed=53, ab_dtype="fp16",
+                                c_dtype="fp32")
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    ref, bound = oracle.spmm(p.m, p.k, p.N, p.coo_rows(), p.col_idx, p.vals, p.B, p.ab_dtype)
+    B = _device_b(p)
+    ran = 0
+    for opts in bench.sweep_candidates(p):
+        try:
+            A.replan(opts)
+        except ws.SpmmError as exc:
+            assert exc.code == ws.ERR_UNSUPPORTED, (opts, str(exc))
+            continue
+        _say("   options", opts)
+        C = A.new_c()
+        C.fill_(float("nan"))
+        A.run(B, C)
+        torch.cuda.synchronize()
+        got = C.float().cpu().numpy().astype(np.float64)
+        ok, worst, at = oracle.within_tolerance(got, ref, bound, TOL, out_dtype=p.c_dtype)
+        assert ok, (opts, worst, at)
+        ran += 1
+    assert ran >= 10

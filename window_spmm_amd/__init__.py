@@ -36,7 +36,7 @@ EXPORTED = [
     "spmm_wcsr_split_count", "spmm_wcsr_split", "spmm_bcsr_plan", "spmm_wcsr_plan",
     "spmm_bcsr_run", "spmm_wcsr_run", "spmm_plan_info", "spmm_plan_destroy",
     "spmm_status_string", "spmm_last_error", "spmm_recommended_ld", "spmm_rcm_order",
-    "spmm_csr_permute",
+    "spmm_csr_permute", "spmm_plan_options_default", "spmm_bcsr_plan_ex", "spmm_wcsr_plan_ex",
 ]
 
 
@@ -44,13 +44,34 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
                 ("tile_cols", ctypes.c_int32), ("waves_n", ctypes.c_int32),
                 ("waves_k", ctypes.c_int32), ("cols_per_lane", ctypes.c_int32),
-                ("kernel", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("kernel", ctypes.c_int32), ("ranges_per_xcd", ctypes.c_int32),
                 ("split_cols", ctypes.c_int64), ("n_tasks", ctypes.c_int64),
                 ("n_merges", ctypes.c_int64), ("n_slots", ctypes.c_int64),
                 ("stored_entries", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class PlanOptions(ctypes.Structure):
+    """spmm_plan_options_t: -1 / 0 = let the plan choose (see the C header)."""
+    _fields_ = [("kernel", ctypes.c_int32), ("cols_per_lane", ctypes.c_int32),
+                ("waves_n", ctypes.c_int32), ("waves_k", ctypes.c_int32),
+                ("distribution", ctypes.c_int32), ("row_order", ctypes.c_int32),
+                ("order", ctypes.c_int32), ("ranges_per_xcd", ctypes.c_int32)]
+
+    AUTO = {"kernel": -1, "cols_per_lane": 0, "waves_n": 0, "waves_k": 0, "distribution": -1,
+            "row_order": -1, "order": -1, "ranges_per_xcd": 0}
+
+    @classmethod
+    def of(cls, options=None):
+        """From a dict of the fields to pin (others automatic), or None."""
+        o = cls(**cls.AUTO)
+        for name, value in (options or {}).items():
+            if name not in cls.AUTO:
+                raise ValueError("unknown plan option %r" % name)
+            setattr(o, name, int(value))
+        return o
 
 
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
@@ -69,6 +90,10 @@ _sigs = {
                        ctypes.c_int, ctypes.c_int, _Psz],
     "spmm_wcsr_plan": [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                        ctypes.c_int, ctypes.c_int, _i64, _Psz],
+    "spmm_bcsr_plan_ex": [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                          ctypes.c_int, ctypes.c_int, ctypes.POINTER(PlanOptions), _Psz],
+    "spmm_wcsr_plan_ex": [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                          ctypes.c_int, ctypes.c_int, _i64, ctypes.POINTER(PlanOptions), _Psz],
     "spmm_bcsr_run": [_vp, _vp, _i64, _vp, _i64, _vp, _vp],
     "spmm_wcsr_run": [_vp, _vp, _i64, _vp, _i64, _vp, _vp],
     "spmm_plan_info": [_vp, ctypes.POINTER(PlanInfo)],
@@ -84,6 +109,8 @@ _lib.spmm_last_error.argtypes = []
 _lib.spmm_last_error.restype = ctypes.c_char_p
 _lib.spmm_recommended_ld.argtypes = [ctypes.c_int64, ctypes.c_int32]
 _lib.spmm_recommended_ld.restype = ctypes.c_int64
+_lib.spmm_plan_options_default.argtypes = [ctypes.POINTER(PlanOptions)]
+_lib.spmm_plan_options_default.restype = None
 
 
 def recommended_ld(N: int, elem_bytes: int) -> int:
@@ -227,24 +254,30 @@ class Plan:
 
 
 def bcsr_plan(m, k, N, b_row, b_col, h_block_row_ptr, d_block_col_idx, d_blocks,
-              ab_dtype="bf16", c_dtype="fp32") -> Plan:
+              ab_dtype="bf16", c_dtype="fp32", options=None) -> Plan:
+    """spmm_bcsr_plan_ex; ``options``: dict of PlanOptions fields to pin."""
     rp = _host(h_block_row_ptr, np.int32)
     h = ctypes.c_void_p(0)
     ws = ctypes.c_size_t(0)
-    _check(_lib.spmm_bcsr_plan(ctypes.byref(h), m, k, N, b_row, b_col, _hp(rp), _dp(d_block_col_idx),
-                               _dp(d_blocks), DTYPES[ab_dtype], DTYPES[c_dtype], ctypes.byref(ws)),
-           "spmm_bcsr_plan")
+    opt = PlanOptions.of(options)
+    _check(_lib.spmm_bcsr_plan_ex(ctypes.byref(h), m, k, N, b_row, b_col, _hp(rp),
+                                  _dp(d_block_col_idx), _dp(d_blocks), DTYPES[ab_dtype],
+                                  DTYPES[c_dtype], ctypes.byref(opt), ctypes.byref(ws)),
+           "spmm_bcsr_plan_ex")
     return Plan(h, "bcsr", ws.value, (d_block_col_idx, d_blocks))
 
 
 def wcsr_plan(m, k, N, b_row, b_col, h_window_row_ptr, d_window_col_idx, d_values,
-              ab_dtype="fp16", c_dtype="fp32", split_cols=0) -> Plan:
+              ab_dtype="fp16", c_dtype="fp32", split_cols=0, options=None) -> Plan:
+    """spmm_wcsr_plan_ex; ``options``: dict of PlanOptions fields to pin."""
     rp = _host(h_window_row_ptr, np.int32)
     h = ctypes.c_void_p(0)
     ws = ctypes.c_size_t(0)
-    _check(_lib.spmm_wcsr_plan(ctypes.byref(h), m, k, N, b_row, b_col, _hp(rp), _dp(d_window_col_idx),
-                               _dp(d_values), DTYPES[ab_dtype], DTYPES[c_dtype], int(split_cols),
-                               ctypes.byref(ws)), "spmm_wcsr_plan")
+    opt = PlanOptions.of(options)
+    _check(_lib.spmm_wcsr_plan_ex(ctypes.byref(h), m, k, N, b_row, b_col, _hp(rp),
+                                  _dp(d_window_col_idx), _dp(d_values), DTYPES[ab_dtype],
+                                  DTYPES[c_dtype], int(split_cols), ctypes.byref(opt),
+                                  ctypes.byref(ws)), "spmm_wcsr_plan_ex")
     return Plan(h, "wcsr", ws.value, (d_window_col_idx, d_values))
 
 
@@ -287,7 +320,8 @@ class DeviceSparse:
     the device, makes the plan and a workspace.  ``run(B, C)`` enqueues C = A*B."""
 
     def __init__(self, fmt: str, m: int, k: int, N: int, row_ptr, col_idx, values, b_row: int,
-                 b_col: int, ab_dtype: str, c_dtype: str, device="cuda", split_cols: int = 0):
+                 b_col: int, ab_dtype: str, c_dtype: str, device="cuda", split_cols: int = 0,
+                 options=None):
         import torch
         self.fmt, self.m, self.k, self.N = fmt, int(m), int(k), int(N)
         self.ab_dtype, self.c_dtype = ab_dtype, c_dtype
@@ -303,15 +337,26 @@ class DeviceSparse:
             torch.empty(4, dtype=torch.int32, device=device)
         self.d_vals = torch.from_numpy(vals.view(np.int16).copy()).to(device) if vals.size else \
             torch.empty(8, dtype=torch.int16, device=device)
-        if fmt == "bcsr":
-            self.plan = bcsr_plan(m, k, N, b_row, b_col, ptr, self.d_idx, self.d_vals, ab_dtype,
-                                  c_dtype)
+        self.device, self.split_cols = device, int(split_cols)
+        self.replan(options)
+
+    def replan(self, options=None):
+        """(Re)makes the plan, with ``options`` (dict of PlanOptions fields to
+        pin, None: automatic), and its workspace."""
+        import torch
+        if getattr(self, "plan", None) is not None:
+            self.plan.destroy()
+        if self.fmt == "bcsr":
+            self.plan = bcsr_plan(self.m, self.k, self.N, self.b_row, self.b_col, self.h_ptr,
+                                  self.d_idx, self.d_vals, self.ab_dtype, self.c_dtype, options)
         else:
-            self.plan = wcsr_plan(m, k, N, b_row, b_col, ptr, self.d_idx, self.d_vals, ab_dtype,
-                                  c_dtype, split_cols)
+            self.plan = wcsr_plan(self.m, self.k, self.N, self.b_row, self.b_col, self.h_ptr,
+                                  self.d_idx, self.d_vals, self.ab_dtype, self.c_dtype,
+                                  self.split_cols, options)
         nbytes = self.plan.workspace_bytes
         self.workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32,
-                                     device=device) if nbytes else None
+                                     device=self.device) if nbytes else None
+        return self
 
     @property
     def stored_entries(self) -> int:

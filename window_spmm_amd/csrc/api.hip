@@ -37,6 +37,7 @@ struct spmm_plan_s {
     int kernel;                 // 0: generic tile kernel, 1: BCSR 64x64 with LDS-shared A,
                                 // 2: BCSR 64x64, A-stationary sweep over column ranges
     int max_blocks;             // kernel 2: most blocks in a block row (LDS size)
+    spmm_plan_options_t opt;    // the caller's choices (auto fields: the plan's)
     int64_t n_ranges, range_tiles;  // kernel 2: column ranges (multiple of 8), tiles each
     int64_t tile_cols, n_col_tiles;
     size_t workspace;
@@ -50,10 +51,24 @@ namespace {
 // this bound as "read zero".
 constexpr uint64_t kMaxBBytes = 0xFFFFFF00ull;
 
-int env_int(const char *name, int dflt)
+// Range checks of plan options that do not depend on the matrix.
+spmm_status_t check_options(const spmm_plan_options_t &o, bool bcsr)
 {
-    const char *s = std::getenv(name);
-    return (s && *s) ? std::atoi(s) : dflt;
+    if (o.kernel < -1 || o.kernel > 2 || (!bcsr && o.kernel > 0))
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "options.kernel %d is not a kernel of this format",
+                    o.kernel);
+    if (o.cols_per_lane != 0 && o.cols_per_lane != 2 && o.cols_per_lane != 4 && o.cols_per_lane != 8)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "options.cols_per_lane must be 0, 2, 4 or 8");
+    if (o.waves_n < 0 || o.waves_n > 4 || o.waves_n == 3 || o.waves_k < 0 || o.waves_k > 4 ||
+        o.waves_k == 3 || std::max(1, o.waves_n) * std::max(1, o.waves_k) > 4)
+        return fail(SPMM_ERR_INVALID_ARGUMENT,
+                    "options.waves_n and waves_k must be 0, 1, 2 or 4 with a product of at most 4");
+    if (o.distribution < -1 || o.distribution > 1 || o.row_order < -1 || o.row_order > 1 ||
+        o.order < -1 || o.order > 1)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "options.distribution, row_order and order must be -1, 0 or 1");
+    if (o.ranges_per_xcd < 0 || o.ranges_per_xcd > 64)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "options.ranges_per_xcd must be in [0, 64]");
+    return SPMM_OK;
 }
 
 spmm_status_t hip_fail(hipError_t e, const char *what)
@@ -126,31 +141,37 @@ spmm_status_t check_common(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, i
 }
 
 // Tile shape: V columns per lane (wave width 16V), waves along N, waves along k'.
-void choose_config(spmm_plan_s *pl, double mean_kprime, int n_cu)
+spmm_status_t choose_config(spmm_plan_s *pl, double mean_kprime, int n_cu)
 {
+    const spmm_plan_options_t &o = pl->opt;
     int V = pl->N >= 128 ? 8 : (pl->N >= 64 ? 4 : 2);
-    V = env_int("SPMM_FORCE_V", V);
-    if (V != 2 && V != 4 && V != 8)
-        V = 8;
     if (pl->b_row >= 32 && V > 4)
         V = 4;  // taller tiles: the accumulators at V = 8 leave no room for the ring
                 // (the kernel has no such instantiation)
+    if (o.cols_per_lane > 0) {
+        if (pl->b_row >= 32 && o.cols_per_lane > 4)
+            return fail(SPMM_ERR_UNSUPPORTED, "8 columns per lane need b_row = 16");
+        V = o.cols_per_lane;
+    }
     const int64_t wave_cols = 16 * V;
     const int64_t col_waves = ceil_div(pl->N, wave_cols);
-    int wn = (pl->b_row == 64 && col_waves >= 2) ? 2 : 1;
-    wn = std::max(1, std::min(4, env_int("SPMM_FORCE_WAVES_N", wn)));
+    int wn = o.waves_n > 0 ? o.waves_n : (pl->b_row == 64 && col_waves >= 2) ? 2 : 1;
     const int64_t col_tiles = std::max<int64_t>(1, ceil_div(pl->N, wave_cols * wn));
     // add reduction waves while the grid is small and the items are long
     const int64_t waves = std::max<int64_t>(1, pl->n_items * col_tiles * wn);
     int wk = 1;
     while (wn * wk * 2 <= 4 && waves * wk < int64_t(16) * n_cu && mean_kprime >= 64.0 * wk * 2)
         wk *= 2;
-    wk = std::max(1, std::min(4 / wn, env_int("SPMM_FORCE_WAVES_K", wk)));
+    if (o.waves_k > 0)
+        wk = o.waves_k;
+    if (wn * wk > 4)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "waves_n * waves_k must be at most 4");
     pl->V = V;
     pl->waves_n = wn;
     pl->waves_k = wk;
     pl->tile_cols = wave_cols * wn;
     pl->n_col_tiles = pl->N > 0 ? ceil_div(pl->N, pl->tile_cols) : 0;
+    return SPMM_OK;
 }
 
 template <typename T>
@@ -305,11 +326,7 @@ int64_t auto_split(int64_t n_rows, const std::function<int64_t(int64_t)> &start,
     const int64_t share = ceil_div(total, std::max<int64_t>(1, slots));
     int64_t T = longest <= share ? longest : share;
     T = std::max<int64_t>(512, ceil_div(T, align) * align);
-    T = std::min<int64_t>(T, kMaxSplit);
-    const int64_t forced = env_int("SPMM_FORCE_SPLIT", 0);
-    if (forced > 0 && forced % align == 0 && forced <= kMaxSplit)
-        T = forced;
-    return T;
+    return std::min<int64_t>(T, kMaxSplit);
 }
 
 // Work of an item for the assignment: its packed columns plus a fixed share
@@ -374,7 +391,7 @@ spmm_status_t make_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
         const int64_t n_ct = pl->n_col_tiles;
         const int64_t groups =
             (n_ct > 1 && n_ct <= 8 && 8 % n_ct == 0) ? n_ct : (n_ct > 8 && n_ct % 8 == 0) ? 8 : 1;
-        const int64_t xcd_groups = env_int("SPMM_FORCE_XCD_GROUPS", 1) ? groups : 1;
+        const int64_t xcd_groups = groups;
         std::vector<int64_t> order(n_work);
         for (int64_t i = 0; i < n_work; ++i)
             order[i] = i;
@@ -397,7 +414,7 @@ spmm_status_t make_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
         }
         // SIMD-sharing level of work-group g: 0 for the first waves on each SIMD
         const int waves_wg = pl->waves_n * pl->waves_k;
-        const int64_t late10 = env_int("SPMM_FORCE_SLOT_COST10", (int)kLateSlotCost10);
+        const int64_t late10 = kLateSlotCost10;
         const auto weight10 = [&](int64_t g) -> int64_t {
             return ((g / n_cu) * waves_wg) / 4 > 0 ? late10 : 10;
         };
@@ -497,15 +514,17 @@ spmm_status_t plan_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
 {
     const int64_t total = start(n_rows) - start(0);
     pl->n_items = n_rows;
-    choose_config(pl, n_rows > 0 ? (double)total / (double)n_rows : 0.0, n_cu);
+    spmm_status_t s = choose_config(pl, n_rows > 0 ? (double)total / (double)n_rows : 0.0, n_cu);
+    if (s != SPMM_OK)
+        return s;
     const int threads = 64 * pl->waves_n * pl->waves_k;
     // work-groups per CU that registers allow
     const size_t lds0 = tile_lds_bytes(0, pl->b_row, pl->V, pl->waves_n, pl->waves_k, true);
     const int per_cu_regs = std::max(1, tiles_blocks_per_cu(pl->fmt, pl->b_row, pl->V, pl->ab,
                                                             threads, lds0));
     const int64_t slots = (int64_t)n_cu * per_cu_regs;
-    const bool spread =
-        env_int("SPMM_FORCE_SPREAD", n_rows * pl->n_col_tiles >= kSpreadItems * slots ? 1 : 0) != 0;
+    const bool spread = pl->opt.distribution >= 0 ? pl->opt.distribution == 1
+                                                   : n_rows * pl->n_col_tiles >= kSpreadItems * slots;
     if (split_cols == 0) {
         // the index buffers of every resident work-group must fit its share of
         // the LDS, which caps the task length
@@ -513,13 +532,12 @@ spmm_status_t plan_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
         int64_t cap = ((buf_max - 256) / 256 * 256) << shift;
         cap = std::max<int64_t>(512, cap / align * align);
         split_cols = auto_split(n_rows, start, align, slots / std::max<int64_t>(1, pl->n_col_tiles));
-        if (env_int("SPMM_FORCE_SPLIT", 0) == 0)
-            split_cols = std::min(split_cols, std::max<int64_t>(align, cap));
+        split_cols = std::min(split_cols, std::max<int64_t>(align, cap));
     }
     // Spread work-groups run in row order when B is much larger than an L2 and
     // the pattern is banded (neighbouring row tiles then share B rows);
     // otherwise longest first, which balances better.
-    int local = env_int("SPMM_FORCE_LOCAL", -1);
+    int local = pl->opt.row_order;
     if (local < 0)
         local = spread && pl->k * pl->N * 2 > 2 * std::max<int64_t>(1, l2_bytes) &&
                 banded_pattern(n_rows, h_ptr, pl->col_idx, pl->fmt == 0 ? pl->b_col : 1, pl->k,
@@ -547,6 +565,20 @@ spmm_plan_s *new_plan(int fmt, int64_t m, int64_t k, int64_t N, int32_t b_row, i
 }  // namespace
 }  // namespace wspmm
 
+extern "C" void spmm_plan_options_default(spmm_plan_options_t *opt)
+{
+    if (!opt)
+        return;
+    opt->kernel = -1;
+    opt->cols_per_lane = 0;
+    opt->waves_n = 0;
+    opt->waves_k = 0;
+    opt->distribution = -1;
+    opt->row_order = -1;
+    opt->order = -1;
+    opt->ranges_per_xcd = 0;
+}
+
 extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
                                         int32_t b_row, int32_t b_col,
                                         const int32_t *h_block_row_ptr,
@@ -554,11 +586,29 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
                                         spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
                                         size_t *workspace_bytes)
 {
+    return spmm_bcsr_plan_ex(plan, m, k, N, b_row, b_col, h_block_row_ptr, d_block_col_idx,
+                             d_blocks, ab_dtype, c_dtype, nullptr, workspace_bytes);
+}
+
+extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
+                                           int32_t b_row, int32_t b_col,
+                                           const int32_t *h_block_row_ptr,
+                                           const int32_t *d_block_col_idx, const void *d_blocks,
+                                           spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
+                                           const spmm_plan_options_t *options,
+                                           size_t *workspace_bytes)
+{
     spmm_status_t s = check_common(plan, m, k, N, b_row, b_col, h_block_row_ptr, d_block_col_idx,
                                    d_blocks, ab_dtype, c_dtype, workspace_bytes, true);
     if (s != SPMM_OK)
         return s;
     *plan = nullptr;
+    spmm_plan_options_t opt;
+    spmm_plan_options_default(&opt);
+    if (options)
+        opt = *options;
+    if ((s = check_options(opt, true)) != SPMM_OK)
+        return s;
     const int64_t nbr = ceil_div(m, b_row);
     const int64_t nnzb = h_block_row_ptr[nbr];
     if (nnzb * b_col >= (int64_t(1) << 31))
@@ -571,6 +621,7 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
                                d_block_col_idx, dev);
     if (!pl)
         return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+    pl->opt = opt;
     pl->stored_entries = nnzb * b_row * b_col;
     if ((s = upload(h_block_row_ptr, nbr + 1, &pl->d_row_ptr)) != SPMM_OK) {
         free_plan(pl);
@@ -584,14 +635,21 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
     const bool b64 = b_row == 64 && b_col == 64;
     pl->max_blocks = max_blocks;
     // Kernel 2 keeps a block row's A in LDS: two resident work-groups per CU
-    // (one per XCD slot pair) are what make each XCD's work-groups sweep the
-    // same B tiles together, so it needs every block row to fit twice per CU.
+    // are what make each XCD's work-groups sweep the same B tiles together, so
+    // it needs every block row to fit twice per CU.
     const int64_t tiles512 = ceil_div(N, 512);
-    const bool sweep_ok = b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 16 &&
-                          sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks)) >= 2;
-    pl->kernel = env_int("SPMM_FORCE_KERNEL", sweep_ok ? 2 : b64 && N >= 256 ? 1 : 0);
-    if (pl->kernel == 2 && !(b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 8))
-        pl->kernel = b64 && N >= 256 ? 1 : 0;
+    const bool lds_ok = b64 && N >= 256;
+    const bool sweep_fits = b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 8 &&
+                            sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks)) >= 2;
+    const bool sweep_auto = sweep_fits && tiles512 >= 16;
+    pl->kernel = opt.kernel >= 0 ? opt.kernel : sweep_auto ? 2 : lds_ok ? 1 : 0;
+    if ((pl->kernel == 1 && !lds_ok) || (pl->kernel == 2 && !sweep_fits)) {
+        free_plan(pl);
+        return fail(SPMM_ERR_UNSUPPORTED,
+                    "kernel %d cannot run this problem (b_row %d, b_col %d, N %lld, %d blocks in "
+                    "the longest block row)",
+                    opt.kernel, b_row, b_col, (long long)N, max_blocks);
+    }
     if (pl->kernel == 2) {
         pl->n_items = nbr;
         pl->V = 8;
@@ -606,12 +664,17 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
         // 1770 us (gate), 1530, 1410, 1580, 1620 and 1760 us (up); longer
         // ranges amortise the A load over more tiles but let the work-groups of
         // an XCD drift apart, so that fewer of them share each B tile in L2.
-        int64_t best_h = std::max<int64_t>(1, std::min<int64_t>(64, tiles512 / 16));
-        best_h = env_int("SPMM_FORCE_RANGES_PER_XCD", (int)best_h);
-        pl->n_ranges = 8 * std::max<int64_t>(1, best_h);
+        const int64_t h = opt.ranges_per_xcd > 0
+                              ? opt.ranges_per_xcd
+                              : std::max<int64_t>(1, std::min<int64_t>(64, tiles512 / 16));
+        pl->n_ranges = 8 * h;
         pl->range_tiles = ceil_div(tiles512, pl->n_ranges);
-    } else if (pl->kernel == 1 && b64) {
-        const int nw = env_int("SPMM_FORCE_WAVES_N", 4) == 2 ? 2 : 4;
+    } else if (pl->kernel == 1) {
+        if (opt.waves_n != 0 && opt.waves_n != 2 && opt.waves_n != 4) {
+            free_plan(pl);
+            return fail(SPMM_ERR_UNSUPPORTED, "kernel 1 runs 2 or 4 waves across N");
+        }
+        const int nw = opt.waves_n > 0 ? opt.waves_n : 4;
         pl->n_items = nbr;
         pl->V = 8;
         pl->waves_n = nw;
@@ -619,9 +682,8 @@ extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
         pl->tile_cols = 128 * nw;
         pl->n_col_tiles = ceil_div(N, pl->tile_cols);
         pl->workspace = 0;
-        pl->order = env_int("SPMM_FORCE_ORDER", 0) ? 1 : 0;
+        pl->order = opt.order > 0 ? 1 : 0;
     } else {
-        pl->kernel = 0;
         const auto start = [&](int64_t w) { return (int64_t)h_block_row_ptr[w] * b_col; };
         int shift = 0;
         while ((1 << shift) < b_col)
@@ -647,12 +709,30 @@ extern "C" spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
                                         spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
                                         int64_t split_cols, size_t *workspace_bytes)
 {
+    return spmm_wcsr_plan_ex(plan, m, k, N, b_row, b_col, h_window_row_ptr, d_window_col_idx,
+                             d_values, ab_dtype, c_dtype, split_cols, nullptr, workspace_bytes);
+}
+
+extern "C" spmm_status_t spmm_wcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
+                                           int32_t b_row, int32_t b_col,
+                                           const int32_t *h_window_row_ptr,
+                                           const int32_t *d_window_col_idx, const void *d_values,
+                                           spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
+                                           int64_t split_cols, const spmm_plan_options_t *options,
+                                           size_t *workspace_bytes)
+{
     spmm_status_t s = check_common(plan, m, k, N, b_row, b_col, h_window_row_ptr,
                                    d_window_col_idx, d_values, ab_dtype, c_dtype, workspace_bytes,
                                    false);
     if (s != SPMM_OK)
         return s;
     *plan = nullptr;
+    spmm_plan_options_t opt;
+    spmm_plan_options_default(&opt);
+    if (options)
+        opt = *options;
+    if ((s = check_options(opt, false)) != SPMM_OK)
+        return s;
     if (split_cols < 0 || split_cols % 32 != 0 || split_cols > kMaxSplit)
         return fail(SPMM_ERR_INVALID_ARGUMENT,
                     "split_cols must be 0 or a positive multiple of 32 up to %lld",
@@ -668,6 +748,7 @@ extern "C" spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k,
                                d_window_col_idx, dev);
     if (!pl)
         return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+    pl->opt = opt;
     pl->stored_entries = P * b_row;
     int64_t widest = 0;
     for (int64_t w = 0; w < nw; ++w)
@@ -714,6 +795,7 @@ extern "C" spmm_status_t spmm_plan_info(spmm_plan_t pl, spmm_plan_info_t *info)
     info->waves_k = pl->waves_k;
     info->cols_per_lane = pl->V;
     info->kernel = pl->kernel;
+    info->ranges_per_xcd = pl->kernel == 2 ? (int32_t)(pl->n_ranges / 8) : 0;
     info->split_cols = pl->kernel == 0 ? pl->split_cols : 0;
     info->n_tasks = pl->kernel == 0 ? pl->n_tasks : 0;
     info->n_merges = pl->n_merges;
