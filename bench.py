@@ -162,7 +162,7 @@ def sweep_candidates(p):
     return cands
 
 
-def run_sweep(p, A, B, C, alg, workload):
+def run_sweep(p, A, B, C, alg, workload, base=None):
     """Times every candidate plan on the resident input (HIP events on the launch
     stream), checks its C against the default plan's, prints a table and one
     JSON summary line.  The measurement behind choosing a tile width, like the
@@ -187,6 +187,7 @@ def run_sweep(p, A, B, C, alg, workload):
     scale = float(C_ref.abs().max()) or 1.0
     rows = [("default", A.plan.info(), base_us, True)]
     for opts in sweep_candidates(p):
+        opts = dict(opts, **(base or {}))
         try:
             A.replan(opts)
         except ws.SpmmError as exc:
@@ -195,7 +196,7 @@ def run_sweep(p, A, B, C, alg, workload):
         us = time_plan(max(5, min(50, int(2e5 / max(base_us, 1.0)))))
         same = bool(torch.allclose(C.float(), C_ref, rtol=1e-2, atol=1e-3 * scale))
         rows.append((opts, A.plan.info(), us, same))
-    A.replan(None)
+    A.replan(base)
     print("%-64s %6s %10s %9s %7s %s" % ("options", "tile", "us", "TFLOP/s", "frac", "C"))
     best = None
     for opts, info, us, same in rows:
@@ -236,6 +237,9 @@ def main():
                     help="only run a 256 MiB device copy (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the kernel / tile-shape options on this workload instead")
+    ap.add_argument("--col-major", action="store_true",
+                    help="BCSR 64x64: B and C column-major (B^T: N x k, C^T: N x m), the "
+                         "token-major activation layout")
     args = ap.parse_args()
 
     if args.copy_probe:
@@ -257,15 +261,28 @@ def main():
     p, workload = make_problem(args.config, args)
     print("bench: building format and plan", file=sys.stderr, flush=True)
     A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
-                        p.ab_dtype, p.c_dtype, device=dev, split_cols=args.split)
+                        p.ab_dtype, p.c_dtype, device=dev, split_cols=args.split,
+                        options={"col_major": 1} if args.col_major else None)
     info = A.plan.info()
-    # B and C rows padded to the library's recommended leading dimension (only
-    # differs from N when the row pitch is a multiple of 4 KiB, e.g. N = 65536)
-    B = A.device_b(p.B, dev, padded=not args.no_pad)
-    C = A.new_c(dev, padded=not args.no_pad)
+    if args.col_major:
+        # B^T (N x k) and C^T (N x m), rows padded like the row-major operands
+        ldb = p.k if args.no_pad else ws.recommended_ld(p.k, 2)
+        ldc = p.m if args.no_pad else ws.recommended_ld(p.m, E_C[p.c_dtype])
+        bt = np.zeros((p.N, ldb), dtype=np.uint16)
+        bt[:, :p.k] = p.B.T
+        B = torch.from_numpy(bt.view(np.int16)).to(dev)[:, :p.k]
+        del bt
+        cdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[p.c_dtype]
+        C = torch.empty((p.N, ldc), dtype=cdt, device=dev)[:, :p.m]
+        workload += " [column-major B^T, C^T]"
+    else:
+        # B and C rows padded to the library's recommended leading dimension (only
+        # differs from N when the row pitch is a multiple of 4 KiB, e.g. N = 65536)
+        B = A.device_b(p.B, dev, padded=not args.no_pad)
+        C = A.new_c(dev, padded=not args.no_pad)
     alg = algorithmic(p, A)
     if args.sweep:
-        run_sweep(p, A, B, C, alg, workload)
+        run_sweep(p, A, B, C, alg, workload, {"col_major": 1} if args.col_major else None)
         return
 
     stream = torch.cuda.current_stream()
@@ -312,7 +329,8 @@ def main():
                 "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     key = "config%d" % args.config + ("_" + args.which if args.config == 4 else "") + \
-          ("_m%d_n%d" % (args.member, args.n3) if args.config == 3 else "")
+          ("_m%d_n%d" % (args.member, args.n3) if args.config == 3 else "") + \
+          ("_colmajor" if args.col_major else "")
     roof["traffic"] = measured_traffic(key)
     roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["kernel_us"] = t_kernel * 1e6

@@ -55,6 +55,8 @@ typedef struct {
     int32_t kernel;          /* 0: generic tile kernel; 1: BCSR 64x64 kernel with LDS-shared A;
                                 2: BCSR 64x64 A-stationary sweep kernel */
     int32_t ranges_per_xcd;  /* kernel 2: column ranges per XCD (0 otherwise) */
+    int32_t col_major;       /* 1 if the plan takes B^T and C^T (spmm_plan_options_t) */
+    int32_t reserved;
     int64_t split_cols;      /* sub-task size T in packed columns (0: whole block rows) */
     int64_t n_tasks;         /* tasks (= work-groups per column tile; 0: whole block rows) */
     int64_t n_merges;        /* row tiles split into more than one task */
@@ -194,6 +196,12 @@ typedef struct {
     int32_t order;           /* -1 auto; kernel 1: 0 column-tile major with a contiguous
                                 range per XCD, 1 launch order */
     int32_t ranges_per_xcd;  /* 0 auto; kernel 2: column ranges per XCD, 1 to 64 */
+    int32_t col_major;       /* 0: B is k x N and C is m x N, row-major (the default);
+                                1: column-major, the layout of activations stored token by
+                                token: d_B holds B^T (N rows of k, leading dimension ldb >= k)
+                                and d_C holds C^T (N rows of m, ldc >= m).  BCSR with
+                                b_row = b_col = 64, N >= 256, m and k multiples of 8, kernels 1
+                                and 2 only (UNSUPPORTED otherwise); INVALID_ARGUMENT for WCSR. */
 } spmm_plan_options_t;
 
 void spmm_plan_options_default(spmm_plan_options_t *opt);
@@ -243,7 +251,11 @@ spmm_status_t spmm_wcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t
  * Requirements (else UNSUPPORTED): d_B and d_C 16-byte aligned, ldb >= N and
  * ldc >= N, both multiples of 8, ldb < 2^23, k * ldb * 2 < 2^32 - 256 and
  * b_row * ldc * (C element bytes) < 2^32 - 256 (B and a tile's rows of C are
- * addressed through 32-bit buffer offsets).  d_workspace: at least workspace_bytes of
+ * addressed through 32-bit buffer offsets).  A plan made with col_major = 1
+ * takes d_B = B^T (N rows of k, ldb >= k) and d_C = C^T (N rows of m, ldc >= m):
+ * ldb, ldc multiples of 8, ldb < 2^23, N * ldb * 2 and (N + 1024) * ldc * (C
+ * element bytes) below 2^32 - 256; the kernels read no byte of B^T past element
+ * (N - 1) * ldb + k - 1.  d_workspace: at least workspace_bytes of
  * device memory (16-byte aligned) when workspace_bytes > 0, else ignored.
  * Device-side faults surface at the caller's next synchronisation. */
 spmm_status_t spmm_bcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void *d_C, int64_t ldc,

@@ -421,3 +421,50 @@ def test_every_sweep_candidate_matches_oracle(ws, kind):
         assert ok, (opts, worst, at)
         ran += 1
     assert ran >= 10
+
+
+COL_MAJOR_CASES = [
+    # m, k, N, block density, ab, c, options
+    (1000, 520, 1288, 0.3, "bf16", "bf16", {"kernel": 1, "waves_n": 4}),
+    (1000, 520, 1288, 0.3, "fp16", "fp32", {"kernel": 1, "waves_n": 2}),
+    (1280, 640, 4104, 0.25, "bf16", "bf16", {"kernel": 2, "ranges_per_xcd": 1}),
+    (704, 576, 8200, 0.3, "bf16", "fp16", {"kernel": 2, "ranges_per_xcd": 2}),
+    (640, 512, 4096, 0.95, "fp16", "fp32", {"kernel": 2}),
+]
+
+
+@pytest.mark.parametrize("case", COL_MAJOR_CASES, ids=lambda c: "x".join(map(str, c[:6])) + "-k%d" % c[6]["kernel"])
+def test_bcsr64_col_major(ws, case):
+    """Column-major B and C (B^T: N rows of k, C^T: N rows of m), the layout of
+    token-major activations: both 64x64 kernels, N ragged against the column
+    tiles, m and k ragged against the blocks, padded leading dimensions with NaN
+    codes in B^T's padding; C^T's padding must stay untouched."""
+    m, k, N, dens, ab, ct, opts = case
+    p = synth.block_problem(m, k, N, 64, 64, dens, seed=m + k + N, ab_dtype=ab, c_dtype=ct)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options=dict(opts, col_major=1))
+    info = A.plan.info()
+    assert info["col_major"] == 1 and info["kernel"] == opts["kernel"]
+    ldb, ldc = k + 24, m + 40
+    nan_code = 0x7FC0 if ab == "bf16" else 0x7E00
+    bt = np.full((N, ldb), nan_code, dtype=np.uint16)
+    bt[:, :k] = p.B.T
+    Bt = torch.from_numpy(bt.view(np.int16)).cuda()[:, :k]
+    Ct_full = torch.full((N, ldc), float("nan"), device="cuda",
+                         dtype={"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[ct])
+    A.run(Bt, Ct_full[:, :m])
+    torch.cuda.synchronize()
+    got = Ct_full.float().cpu().numpy().astype(np.float64)
+    assert np.isnan(got[:, m:]).all()
+    check(p, np.ascontiguousarray(got[:, :m].T))
+
+
+def test_col_major_rejected_where_unsupported(ws):
+    p = synth.block_problem(200, 150, 72, 32, 16, 0.3, seed=1, ab_dtype="bf16", c_dtype="fp32")
+    with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):
+        ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"col_major": 1})
+    p = synth.block_problem(200, 150, 512, 64, 64, 0.3, seed=2, ab_dtype="bf16", c_dtype="fp32")
+    with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):   # m, k not multiples of 8
+        ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"col_major": 1})

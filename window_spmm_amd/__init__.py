@@ -45,6 +45,7 @@ class PlanInfo(ctypes.Structure):
                 ("tile_cols", ctypes.c_int32), ("waves_n", ctypes.c_int32),
                 ("waves_k", ctypes.c_int32), ("cols_per_lane", ctypes.c_int32),
                 ("kernel", ctypes.c_int32), ("ranges_per_xcd", ctypes.c_int32),
+                ("col_major", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("split_cols", ctypes.c_int64), ("n_tasks", ctypes.c_int64),
                 ("n_merges", ctypes.c_int64), ("n_slots", ctypes.c_int64),
                 ("stored_entries", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
@@ -58,10 +59,11 @@ class PlanOptions(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("cols_per_lane", ctypes.c_int32),
                 ("waves_n", ctypes.c_int32), ("waves_k", ctypes.c_int32),
                 ("distribution", ctypes.c_int32), ("row_order", ctypes.c_int32),
-                ("order", ctypes.c_int32), ("ranges_per_xcd", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("ranges_per_xcd", ctypes.c_int32),
+                ("col_major", ctypes.c_int32)]
 
     AUTO = {"kernel": -1, "cols_per_lane": 0, "waves_n": 0, "waves_k": 0, "distribution": -1,
-            "row_order": -1, "order": -1, "ranges_per_xcd": 0}
+            "row_order": -1, "order": -1, "ranges_per_xcd": 0, "col_major": 0}
 
     @classmethod
     def of(cls, options=None):

@@ -68,6 +68,8 @@ spmm_status_t check_options(const spmm_plan_options_t &o, bool bcsr)
         return fail(SPMM_ERR_INVALID_ARGUMENT, "options.distribution, row_order and order must be -1, 0 or 1");
     if (o.ranges_per_xcd < 0 || o.ranges_per_xcd > 64)
         return fail(SPMM_ERR_INVALID_ARGUMENT, "options.ranges_per_xcd must be in [0, 64]");
+    if (o.col_major < 0 || o.col_major > 1 || (!bcsr && o.col_major))
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "options.col_major must be 0 or 1 (0 for WCSR)");
     return SPMM_OK;
 }
 
@@ -214,12 +216,21 @@ spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int
         return fail(SPMM_ERR_INVALID_ARGUMENT, "null B or C");
     if (((uintptr_t)B | (uintptr_t)C) & 15)
         return fail(SPMM_ERR_UNSUPPORTED, "B and C must be 16-byte aligned");
-    if (ldb < pl->N || ldc < pl->N || ldb % 8 || ldc % 8)
-        return fail(SPMM_ERR_UNSUPPORTED, "ldb/ldc must be >= N and multiples of 8");
+    const bool cm = pl->opt.col_major != 0;
+    const uint64_t esz = pl->ct == SPMM_FP32 ? 4u : 2u;
+    if (cm ? (ldb < pl->k || ldc < pl->m) : (ldb < pl->N || ldc < pl->N))
+        return fail(SPMM_ERR_UNSUPPORTED, cm ? "column-major: ldb must be >= k and ldc >= m"
+                                             : "ldb/ldc must be >= N");
+    if (ldb % 8 || ldc % 8)
+        return fail(SPMM_ERR_UNSUPPORTED, "ldb/ldc must be multiples of 8");
     if (ldb >= (int64_t(1) << 23))
         return fail(SPMM_ERR_UNSUPPORTED, "ldb must be below 2^23");
-    if ((uint64_t)pl->k * (uint64_t)ldb * 2u >= kMaxBBytes)
-        return fail(SPMM_ERR_UNSUPPORTED, "B (k * ldb * 2 bytes) must be smaller than 4 GiB - 256");
+    if ((uint64_t)(cm ? pl->N : pl->k) * (uint64_t)ldb * 2u >= kMaxBBytes)
+        return fail(SPMM_ERR_UNSUPPORTED, "B must be smaller than 4 GiB - 256 bytes");
+    // (the last column tile's lanes address up to 511 columns past N; their
+    // 32-bit store offsets must stay past the end of C^T without wrapping)
+    if (cm && (uint64_t)(pl->N + 1024) * (uint64_t)ldc * esz >= kMaxBBytes)
+        return fail(SPMM_ERR_UNSUPPORTED, "C^T ((N + 1024) * ldc * element bytes) must be below 4 GiB - 256");
     if ((pl->kernel == 0 || pl->kernel == 1 || pl->kernel == 2) &&
         (uint64_t)pl->b_row * (uint64_t)ldc * (pl->ct == SPMM_FP32 ? 4u : 2u) >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "b_row rows of C (b_row * ldc * element bytes) must be below 4 GiB");
@@ -262,7 +273,10 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.N = pl->N;
     // the extent of B ends with column N - 1 of row k - 1: loads of columns past N
     // in that row and of rows past k fall outside it and read zeros
-    p.b_bytes = pl->k > 0 ? ((uint64_t)(pl->k - 1) * (uint64_t)ldb + (uint64_t)pl->N) * 2u : 0u;
+    p.b_bytes = pl->opt.col_major
+                    ? ((uint64_t)(pl->N - 1) * (uint64_t)ldb + (uint64_t)pl->k) * 2u
+                    : pl->k > 0 ? ((uint64_t)(pl->k - 1) * (uint64_t)ldb + (uint64_t)pl->N) * 2u : 0u;
+    p.col_major = pl->opt.col_major;
     p.n_items = pl->n_items;
     p.n_col_tiles = pl->n_col_tiles;
     p.b_col = pl->b_col;
@@ -577,6 +591,7 @@ extern "C" void spmm_plan_options_default(spmm_plan_options_t *opt)
     opt->row_order = -1;
     opt->order = -1;
     opt->ranges_per_xcd = 0;
+    opt->col_major = 0;
 }
 
 extern "C" spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
@@ -640,8 +655,15 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
     const int64_t tiles512 = ceil_div(N, 512);
     const bool lds_ok = b64 && N >= 256;
     const bool sweep_fits = b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 8 &&
-                            sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks)) >= 2;
+                            sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks),
+                                                opt.col_major != 0) >= 2;
     const bool sweep_auto = sweep_fits && tiles512 >= 16;
+    if (opt.col_major && (!lds_ok || m % 8 || k % 8 || opt.kernel == 0)) {
+        free_plan(pl);
+        return fail(SPMM_ERR_UNSUPPORTED,
+                    "column-major B and C need b_row = b_col = 64, N >= 256, m and k multiples "
+                    "of 8 and kernel 1 or 2");
+    }
     pl->kernel = opt.kernel >= 0 ? opt.kernel : sweep_auto ? 2 : lds_ok ? 1 : 0;
     if ((pl->kernel == 1 && !lds_ok) || (pl->kernel == 2 && !sweep_fits)) {
         free_plan(pl);
@@ -651,12 +673,14 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
                     opt.kernel, b_row, b_col, (long long)N, max_blocks);
     }
     if (pl->kernel == 2) {
+        // column-major: 4 columns per lane (a whole block of B^T per ring stage)
+        const int cm_v = opt.col_major ? 4 : 8;
         pl->n_items = nbr;
-        pl->V = 8;
+        pl->V = cm_v;
         pl->waves_n = 4;
         pl->waves_k = 1;
-        pl->tile_cols = 512;
-        pl->n_col_tiles = tiles512;
+        pl->tile_cols = 64 * cm_v;
+        pl->n_col_tiles = ceil_div(N, pl->tile_cols);
         pl->workspace = 0;
         pl->order = 0;
         // Ranges of two column tiles: on the FFN shapes (N = 65536, 128 tiles)
@@ -666,9 +690,9 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         // an XCD drift apart, so that fewer of them share each B tile in L2.
         const int64_t h = opt.ranges_per_xcd > 0
                               ? opt.ranges_per_xcd
-                              : std::max<int64_t>(1, std::min<int64_t>(64, tiles512 / 16));
+                              : std::max<int64_t>(1, std::min<int64_t>(64, pl->n_col_tiles / 16));
         pl->n_ranges = 8 * h;
-        pl->range_tiles = ceil_div(tiles512, pl->n_ranges);
+        pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
     } else if (pl->kernel == 1) {
         if (opt.waves_n != 0 && opt.waves_n != 2 && opt.waves_n != 4) {
             free_plan(pl);
@@ -796,6 +820,7 @@ extern "C" spmm_status_t spmm_plan_info(spmm_plan_t pl, spmm_plan_info_t *info)
     info->cols_per_lane = pl->V;
     info->kernel = pl->kernel;
     info->ranges_per_xcd = pl->kernel == 2 ? (int32_t)(pl->n_ranges / 8) : 0;
+    info->col_major = pl->opt.col_major;
     info->split_cols = pl->kernel == 0 ? pl->split_cols : 0;
     info->n_tasks = pl->kernel == 0 ? pl->n_tasks : 0;
     info->n_merges = pl->n_merges;

@@ -41,6 +41,7 @@ struct TileParams {
     int32_t two_buffers;      // generic kernel: 0 if every work-group runs one entry (one buffer)
     int64_t n_ranges;         // sweep kernel: column ranges (a multiple of 8)
     int64_t range_tiles;      // sweep kernel: column tiles per range
+    int32_t col_major;        // 64x64 kernels: B holds B^T (N rows of k), C holds C^T (N rows of m)
 };
 
 struct MergeParams {
@@ -63,16 +64,17 @@ hipError_t launch_tiles(int fmt, int R, int V, int ab_dtype, const TileParams &p
 int tiles_blocks_per_cu(int fmt, int R, int V, int ab_dtype, int threads, size_t lds_bytes);
 hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stream);
 // BCSR with 64x64 blocks, waves_n (2 or 4) waves x 128 columns per work-group, A
-// shared through LDS (requires waves_k = 1, V = 8, tile_cols = 128 * waves_n).
+// shared through LDS (requires waves_k = 1, V = 8, tile_cols = 128 * waves_n);
+// p.col_major selects column-major B and C.
 hipError_t launch_bcsr64_lds(int ab_dtype, const TileParams &p, hipStream_t stream);
 // Most blocks in a block row that the sweep kernel holds in LDS.
 constexpr int kSweepMaxBlocks = 8;
 // BCSR with 64x64 blocks, A-stationary: n_items block rows x n_ranges column
-// ranges of range_tiles tiles of 512 columns, 4 waves, every block of a block row
-// in LDS (max_blocks <= kSweepMaxBlocks, tile_cols = 512).
+// ranges of range_tiles tiles of 512 columns (256 with col_major), 4 waves,
+// every block of a block row in LDS (max_blocks <= kSweepMaxBlocks).
 hipError_t launch_bcsr64_sweep(int ab_dtype, int max_blocks, const TileParams &p, hipStream_t stream);
 size_t sweep_lds_bytes(int max_blocks);
 // Work-groups of the sweep kernel resident per CU (0 if the query fails).
-int sweep_blocks_per_cu(int ab_dtype, int max_blocks);
+int sweep_blocks_per_cu(int ab_dtype, int max_blocks, bool col_major);
 
 }  // namespace wspmm

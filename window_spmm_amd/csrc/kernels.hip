@@ -119,6 +119,57 @@ __device__ __forceinline__ void store_acc_rows(const f32x4_t (&acc)[MT][V], __am
         }
 }
 
+// Column-major operands (B^T: N rows of k, C^T: N rows of m).  Lane (g, i) of
+// MFMA column tile c holds column n = 16c + i of its tile; its results are rows
+// 4g .. 4g+3 of each 16-row slice mt, four adjacent elements of C^T row n.
+// rC starts at a C^T row and ends `size` bytes later, after the last column
+// (< N) the work-group may write, so columns past N fall outside it; tile_off
+// (wave-uniform) is the byte offset of this tile's first C^T row inside rC.
+// Rows past m (m is a multiple of 4: all four or none) are sent to offset
+// size + ..., also outside (the host keeps (N + 1024) * ldc * esz below 2^32,
+// so no offset wraps).
+// Stores as DT, non-temporal.
+template <int DT, int MT, int V>
+__device__ __forceinline__ void store_acc_cm(const f32x4_t (&acc)[MT][V], __amdgpu_buffer_rsrc_t rC,
+                                             uint32_t size, uint32_t tile_off, int g, int li,
+                                             int64_t row0, int64_t m, int64_t ldc)
+{
+    constexpr int esz = DT == SPMM_FP32 ? 4 : 2;
+    const uint32_t ldcb = (uint32_t)ldc * esz;
+    const uint32_t lane_off = tile_off + (uint32_t)li * ldcb + (uint32_t)(row0 + 4 * g) * esz;
+    const int32_t nrows = (int32_t)(m - row0 < (1 << 30) ? m - row0 : (1 << 30)) - 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t vo = 16 * mt < nrows ? lane_off + (uint32_t)(16 * mt * esz) : size;
+#pragma unroll
+        for (int c = 0; c < V; ++c) {
+            const uint32_t off = vo + (uint32_t)(16 * c) * ldcb;
+            if constexpr (DT == SPMM_FP32) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[mt][c]), rC,
+                                                       (int)off, 0, kNT);
+            } else {
+                const f32x4_t v = acc[mt][c];
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack2(DT, v[0], v[1]), pack2(DT, v[2], v[3])},
+                                                      rC, (int)off, 0, kNT);
+            }
+        }
+    }
+}
+
+template <int MT, int V>
+__device__ __forceinline__ void store_tile_cm(int dt, const f32x4_t (&acc)[MT][V],
+                                              __amdgpu_buffer_rsrc_t rC, uint32_t size,
+                                              uint32_t tile_off, int g, int li, int64_t row0,
+                                              int64_t m, int64_t ldc)
+{
+    if (dt == SPMM_FP32)
+        store_acc_cm<SPMM_FP32>(acc, rC, size, tile_off, g, li, row0, m, ldc);
+    else if (dt == SPMM_BF16)
+        store_acc_cm<SPMM_BF16>(acc, rC, size, tile_off, g, li, row0, m, ldc);
+    else
+        store_acc_cm<SPMM_FP16>(acc, rC, size, tile_off, g, li, row0, m, ldc);
+}
+
 // Stores the V results of one row of one lane (V adjacent columns) at byte
 // offset `off` of r; kOOB drops the store.  For a given V both the fp32 and the
 // 16-bit forms issue the same number of store instructions, so wait counts on
@@ -526,8 +577,10 @@ __global__ __launch_bounds__(256, 2) void spmm_tile_kernel(TileParams p)
 // shared: the work-group loads each 64 x 64 block once (non-temporal, it is
 // streamed) into one of two padded LDS buffers, and every wave reads its A
 // fragments from there.  Block-column indices are work-group uniform and come
-// through scalar loads.  One LDS barrier per block.
-template <int AB, int NW>
+// through scalar loads.  One LDS barrier per block.  CM: column-major B and C
+// (B^T and C^T row-major): each lane's 16-byte load of a B^T row already is
+// its MFMA B operand, no register transpose.
+template <int AB, int NW, bool CM>
 __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
                                                              const int32_t *__restrict__ block_cols)
 {
@@ -551,9 +604,10 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
     const __amdgpu_buffer_rsrc_t rA =
         make_rsrc(p.A + blk0 * R * BC, (uint32_t)((int64_t)nblk * R * BC * 2));
     const int64_t col0 = ctile * p.tile_cols + wave * 16 * V;
-    const uint64_t b_skip = (uint64_t)col0 * 2;
-    const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc(p.B + col0, (uint32_t)(p.b_bytes > b_skip ? p.b_bytes - b_skip : 0));
+    // row-major: B + col0 (column col0 of every row); CM: B^T row col0
+    const uint64_t b_skip = CM ? (uint64_t)col0 * p.ldb * 2 : (uint64_t)col0 * 2;
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+        p.B + (CM ? col0 * p.ldb : col0), (uint32_t)(p.b_bytes > b_skip ? p.b_bytes - b_skip : 0));
     const uint32_t ldb2 = (uint32_t)p.ldb * 2;
     const uint32_t lane_col_bytes = (uint32_t)li * V * 2;
     const uint32_t k32 = (uint32_t)p.k;
@@ -589,14 +643,23 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
         const uint32_t J = (uint32_t)block_cols[at];
         return q < nblk ? J : 0xFFFFFFFFu;
     };
-    // B rows of k' step s of block column J (half s%2): J*64 + 32*(s%2) + 8g + j
+    // k' step s of block column J (half s%2): row-major, B rows J*64 + 32*(s%2) +
+    // 8g + j; CM, columns 16c + i of B^T rows from k = J*64 + 32*(s%2) + 8g (k is
+    // a multiple of 8: a lane's eight values are all inside B or all past it)
     auto issue_b = [&](int s, uint32_t J, BStage<DW> &st) {
         const bool jv = J < nbc;
         const uint32_t r0 = (jv ? J : 0u) * BC + (uint32_t)(s & 1) * 32 + 8 * g;
+        if constexpr (CM) {
+            const uint32_t base = (uint32_t)li * ldb2 + r0 * 2;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t r = r0 + j;
-            buf_load<DW>(rB, (jv & (r < k32)) ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
+            for (int c = 0; c < V; ++c)
+                buf_load<DW>(rB, (jv & (r0 < k32)) ? base + (uint32_t)(16 * c) * ldb2 : kOOB, st.b[c]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t r = r0 + j;
+                buf_load<DW>(rB, (jv & (r < k32)) ? r * ldb2 + lane_col_bytes : kOOB, st.b[j]);
+            }
         }
     };
     auto compute = [&](const BStage<DW> &st, int buf, int half) {
@@ -607,11 +670,15 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
                                                        (half * 32 + 8 * g) * 2);
 #pragma unroll
         for (int c = 0; c < V; ++c) {
-            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
             u32x4_t bf;
+            if constexpr (CM) {
+                bf = u32x4_t{st.b[c][0], st.b[c][1], st.b[c][2], st.b[c][3]};
+            } else {
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                bf[q] = __builtin_amdgcn_perm(st.b[2 * q + 1][c >> 1], st.b[2 * q][c >> 1], sel);
+                for (int q = 0; q < 4; ++q)
+                    bf[q] = __builtin_amdgcn_perm(st.b[2 * q + 1][c >> 1], st.b[2 * q][c >> 1], sel);
+            }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 acc[mt][c] = mfma16x16x32<AB>(af[mt], bf, acc[mt][c]);
@@ -647,8 +714,15 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
     }
 
     // epilogue: one branch on C's type, non-temporal stores
-    const int64_t ncol = col0 + li * V;
     const int esz = p.c_dtype == SPMM_FP32 ? 4 : 2;
+    if constexpr (CM) {
+        const int64_t n_end = col0 + 16 * V < p.N ? col0 + 16 * V : p.N;
+        const uint32_t size = n_end > col0 ? (uint32_t)((n_end - col0) * p.ldc * esz) : 0u;
+        const __amdgpu_buffer_rsrc_t rCt = make_rsrc((uint8_t *)p.C + col0 * p.ldc * esz, size);
+        store_tile_cm(p.c_dtype, acc, rCt, size, 0u, g, li, row0, p.m, p.ldc);
+        return;
+    }
+    const int64_t ncol = col0 + li * V;
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc((uint8_t *)p.C + row0 * p.ldc * esz, (uint32_t)(R * p.ldc * esz));
     if (p.c_dtype == SPMM_FP32)
@@ -669,11 +743,14 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
 // to the XCDs in turn; XCD x runs the column ranges x, x + 8, ... and, inside a
 // range, the block rows in order, so the work-groups resident on one XCD sweep
 // the same column tiles at about the same time and share each tile's B rows in
-// that XCD's L2, and A is read once per (block row, range).
-template <int AB, int NW>
+// that XCD's L2, and A is read once per (block row, range).  CM: column-major B
+// and C, as in bcsr64_lds_kernel.
+template <int AB, int NW, bool CM>
 __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
 {
-    constexpr int R = 64, BC = 64, MT = 4, V = 8, DW = 4;
+    // CM: 4 columns per lane, so that a whole block of B^T (both halves) fits
+    // one ring stage
+    constexpr int R = 64, BC = 64, MT = 4, V = CM ? 4 : 8, DW = 4;
     constexpr int NT = NW * 64;
     constexpr int STRIDE = BC * 2 + 16;            // padded LDS row: conflict-free b128 reads
     constexpr int ABUF = R * STRIDE;               // bytes of one block in LDS
@@ -727,38 +804,68 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
     const uint32_t ldb2 = (uint32_t)p.ldb * 2;
     const uint32_t k32 = (uint32_t)p.k;
     const uint32_t nbc = (uint32_t)((p.k + BC - 1) / BC);
-    const uint32_t lane_col = (uint32_t)(wave * 16 * V + li * V);  // column inside a tile
-    const int64_t col_first = t_begin * p.tile_cols + lane_col;     // this lane, first tile
+    // this lane's first column in the first tile: row-major li*V + c, CM 16c + li
+    const uint32_t lane_col = (uint32_t)(wave * 16 * V + (CM ? li : li * V));
+    const int64_t col_first = t_begin * p.tile_cols + lane_col;
     const uint32_t tile_bytes = (uint32_t)p.tile_cols * 2;
     const int esz = p.c_dtype == SPMM_FP32 ? 4 : 2;
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc((uint8_t *)p.C + row0 * p.ldc * esz, (uint32_t)(R * p.ldc * esz));
+    // CM: one resource over the C^T rows this wave writes in the whole range
+    const int64_t cm_n0 = t_begin * p.tile_cols + wave * 16 * V;
+    const int64_t cm_n1 = (t_end - 1) * p.tile_cols + wave * 16 * V + 16 * V;
+    const int64_t cm_end = cm_n1 < p.N ? cm_n1 : p.N;
+    const uint32_t cm_size = CM && cm_end > cm_n0 ? (uint32_t)((cm_end - cm_n0) * p.ldc * esz) : 0u;
+    const __amdgpu_buffer_rsrc_t rCt = make_rsrc((uint8_t *)p.C + (CM ? cm_n0 * p.ldc * esz : 0), cm_size);
 
     f32x4_t acc[MT][V];
     // B rows of half `half` of block q in tile t: J*64 + 32*half + 8g + j; tile
     // ntiles (past the range) loads nothing
     auto issue_b = [&](int t, int q, int half, BStage<DW> &st) {
         const uint32_t J = (uint32_t)__builtin_amdgcn_readlane((int)vcols, q);
-        const bool jv = (t < ntiles) & (J < nbc);
+        const bool jv = (t < ntiles) & (q < nblk) & (J < nbc);
         const uint32_t r0 = (jv ? J : 0u) * BC + (uint32_t)half * 32 + 8 * g;
-        const uint32_t base = r0 * ldb2 + (uint32_t)col_first * 2 + (uint32_t)t * tile_bytes;
+        if constexpr (CM) {
+            // the whole block: B^T rows n = col_first + t*tile_cols + 16c, 32 bytes
+            // from k = J*64 + 16g (both halves of a 128-byte line arrive together);
+            // st.b[2c + hh] feeds half hh (`half` is unused)
+            const uint32_t k0 = (jv ? J : 0u) * BC + 16 * g;
+            const uint32_t base =
+                ((uint32_t)col_first + (uint32_t)t * (uint32_t)p.tile_cols) * ldb2 + k0 * 2;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            buf_load<DW>(rB, (jv & (r0 + j < k32)) ? base + (uint32_t)j * ldb2 : kOOB, st.b[j]);
+            for (int c = 0; c < V; ++c)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    buf_load<DW>(rB, (jv & (k0 + 8 * hh < k32)) ? base + (uint32_t)(16 * c) * ldb2 + 16 * hh : kOOB,
+                                 st.b[2 * c + hh]);
+        } else {
+            const uint32_t base = r0 * ldb2 + (uint32_t)col_first * 2 + (uint32_t)t * tile_bytes;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                buf_load<DW>(rB, (jv & (r0 + j < k32)) ? base + (uint32_t)j * ldb2 : kOOB, st.b[j]);
+        }
     };
     auto compute = [&](const BStage<DW> &st, int q, int half) {
         u32x4_t af[MT];
+        // CM: lane group g, half `half` holds k = 16g + 8*half .. +7 (row-major:
+        // 32*half + 8g .. +7); A is read with the same permutation of k
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            af[mt] = *reinterpret_cast<const u32x4_t *>(lds_a + q * ABUF + (mt * 16 + li) * STRIDE +
-                                                       (half * 32 + 8 * g) * 2);
+            af[mt] = *reinterpret_cast<const u32x4_t *>(
+                lds_a + q * ABUF + (mt * 16 + li) * STRIDE +
+                (CM ? 16 * g + 8 * half : half * 32 + 8 * g) * 2);
 #pragma unroll
         for (int c = 0; c < V; ++c) {
-            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
             u32x4_t bf;
+            if constexpr (CM) {
+                const int e = 2 * c + half;
+                bf = u32x4_t{st.b[e][0], st.b[e][1], st.b[e][2], st.b[e][3]};
+            } else {
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-                bf[qq] = __builtin_amdgcn_perm(st.b[2 * qq + 1][c >> 1], st.b[2 * qq][c >> 1], sel);
+                for (int qq = 0; qq < 4; ++qq)
+                    bf[qq] = __builtin_amdgcn_perm(st.b[2 * qq + 1][c >> 1], st.b[2 * qq][c >> 1], sel);
+            }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 acc[mt][c] = mfma16x16x32<AB>(af[mt], bf, acc[mt][c]);
@@ -766,13 +873,18 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
     };
     // stores tile t (one branch on C's type per tile)
     auto store_tile = [&](int t) {
-        const int64_t ncol = col_first + (int64_t)t * p.tile_cols;
-        if (p.c_dtype == SPMM_FP32)
-            store_acc_rows<SPMM_FP32>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
-        else if (p.c_dtype == SPMM_BF16)
-            store_acc_rows<SPMM_BF16>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
-        else
-            store_acc_rows<SPMM_FP16>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
+        if constexpr (CM) {
+            const uint32_t tile_off = (uint32_t)t * (uint32_t)p.tile_cols * (uint32_t)(p.ldc * esz);
+            store_tile_cm(p.c_dtype, acc, rCt, cm_size, tile_off, g, li, row0, p.m, p.ldc);
+        } else {
+            const int64_t ncol = col_first + (int64_t)t * p.tile_cols;
+            if (p.c_dtype == SPMM_FP32)
+                store_acc_rows<SPMM_FP32>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
+            else if (p.c_dtype == SPMM_BF16)
+                store_acc_rows<SPMM_BF16>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
+            else
+                store_acc_rows<SPMM_FP16>(acc, rC, g, row0, p.m, p.ldc, ncol, p.N);
+        }
     };
     auto zero_acc = [&]() {
 #pragma unroll
@@ -790,6 +902,31 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
     }
     BStage<DW> st0, st1;
     issue_b(0, 0, 0, st0);
+    if constexpr (CM) {
+        // whole-block stages, two blocks per iteration: st0 holds block q, st1
+        // block q + 1 (past the row's end, an odd count: zeros, not computed).
+        // Every path issues the same loads, which keeps the wait counts exact.
+        for (int t = 0; t < ntiles; ++t) {
+            zero_acc();
+            for (int q = 0; q < nblk; q += 2) {
+                issue_b(t, q + 1, 0, st1);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(st0, q, 0);
+                compute(st0, q, 1);
+                __builtin_amdgcn_sched_barrier(0);
+                const bool last = q + 2 >= nblk;
+                issue_b(last ? t + 1 : t, last ? 0 : q + 2, 0, st0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q + 1 < nblk) {
+                    compute(st1, q + 1, 0);
+                    compute(st1, q + 1, 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            store_tile(t);
+        }
+        return;
+    }
     for (int t = 0; t < ntiles; ++t) {
         zero_acc();
         for (int q = 0; q < nblk; ++q) {
@@ -888,24 +1025,24 @@ size_t tile_lds_bytes(int64_t buf_ints, int R, int V, int waves_n, int waves_k, 
     return (size_t)((two_buffers ? 2 : 1) * buf_ints + 256 + red) * sizeof(int32_t);
 }
 
-template <int NW>
+template <int NW, bool CM>
 static void launch_lds_nw(int ab, const TileParams &p, hipStream_t stream)
 {
     dim3 grid((unsigned)(p.n_items * p.n_col_tiles));
     if (ab == SPMM_FP16)
-        hipLaunchKernelGGL((bcsr64_lds_kernel<SPMM_FP16, NW>), grid, dim3(NW * 64), 0, stream, p,
-                           p.col_idx);
+        hipLaunchKernelGGL((bcsr64_lds_kernel<SPMM_FP16, NW, CM>), grid, dim3(NW * 64), 0, stream,
+                           p, p.col_idx);
     else
-        hipLaunchKernelGGL((bcsr64_lds_kernel<SPMM_BF16, NW>), grid, dim3(NW * 64), 0, stream, p,
-                           p.col_idx);
+        hipLaunchKernelGGL((bcsr64_lds_kernel<SPMM_BF16, NW, CM>), grid, dim3(NW * 64), 0, stream,
+                           p, p.col_idx);
 }
 
 hipError_t launch_bcsr64_lds(int ab, const TileParams &p, hipStream_t stream)
 {
-    if (p.waves_n == 2)
-        launch_lds_nw<2>(ab, p, stream);
+    if (p.col_major)
+        p.waves_n == 2 ? launch_lds_nw<2, true>(ab, p, stream) : launch_lds_nw<4, true>(ab, p, stream);
     else
-        launch_lds_nw<4>(ab, p, stream);
+        p.waves_n == 2 ? launch_lds_nw<2, false>(ab, p, stream) : launch_lds_nw<4, false>(ab, p, stream);
     return hipGetLastError();
 }
 
@@ -914,24 +1051,27 @@ size_t sweep_lds_bytes(int max_blocks)
     return (size_t)max_blocks * 64 * (64 * 2 + 16);
 }
 
-static const void *sweep_fn(int ab)
+static const void *sweep_fn(int ab, bool cm)
 {
-    return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4>)
-                           : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4>);
+    if (cm)
+        return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4, true>)
+                               : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4, true>);
+    return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4, false>)
+                           : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4, false>);
 }
 
 hipError_t launch_bcsr64_sweep(int ab, int max_blocks, const TileParams &p, hipStream_t stream)
 {
     TileParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel(sweep_fn(ab), dim3((unsigned)(p.n_items * p.n_ranges)), dim3(256), args,
-                           sweep_lds_bytes(max_blocks), stream);
+    return hipLaunchKernel(sweep_fn(ab, p.col_major != 0), dim3((unsigned)(p.n_items * p.n_ranges)),
+                           dim3(256), args, sweep_lds_bytes(max_blocks), stream);
 }
 
-int sweep_blocks_per_cu(int ab, int max_blocks)
+int sweep_blocks_per_cu(int ab, int max_blocks, bool col_major)
 {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sweep_fn(ab), 256,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sweep_fn(ab, col_major), 256,
                                                      sweep_lds_bytes(max_blocks)) != hipSuccess)
         return 0;
     return n;
