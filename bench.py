@@ -45,7 +45,7 @@ def make_problem(cfg: int, args):
         return p, "cfg3 member %d: WCSR m=k=%d, N=%d, %s" % (
             args.member, p.m, p.N, "banded" if p.meta["banded"] else "uniform")
     if cfg == 4:
-        p = synth.config4(args.which)
+        p = synth.config4(args.which, N=args.n4)
         return p, "cfg4 %s: BCSR %dx%d bf16, 64x64 blocks, 90%% block sparse, N=65536, bf16 out" % (
             args.which, p.m, p.k)
     if cfg == 5:
@@ -218,6 +218,87 @@ def run_sweep(p, A, B, C, alg, workload, base=None):
         raise SystemExit("a candidate plan's C differs from the default plan's")
 
 
+def run_ffn_table():
+    """Kernel-level analog of the paper's gate_proj table (Section IV-D, Table
+    III): the 18944 x 3584 gate_proj weight at 80, 90, 95 and 99 % random block
+    sparsity (64 x 64 blocks, the same number per block row) times dense
+    activations of N = 1K, 4K, 16K and 64K tokens, bf16, against the dense
+    product of the same shape through torch.mm (hipBLASLt).  Latency averaged
+    over 100 runs after 10 warm-up runs, as in the paper.  At N = 1K each sparse
+    result is checked against torch.mm of its densified weight (fp32).  Each
+    measurement starts after a 2 s pause (the GPU's clocks drop after long
+    full-power runs such as the dense GEMM), sparse cases before the dense one."""
+    import torch
+    import synth
+    import window_spmm_amd as ws
+    dev = torch.device("cuda:0")
+    m, k = 18944, 3584
+    sparsities = (0.80, 0.90, 0.95, 0.99)
+
+    def timed(fn, warm=10, n=100):
+        torch.cuda.synchronize()
+        time.sleep(2.0)
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(n):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n
+
+    rows = []
+    for N in (1024, 4096, 16384, 65536):
+        g = torch.Generator(device=dev)
+        g.manual_seed(N)
+        Bf = torch.randn((k, N), generator=g, device=dev).to(torch.bfloat16)
+        ld = ws.recommended_ld(N, 2)
+        Bp = torch.empty((k, ld), dtype=torch.int16, device=dev)
+        Bp[:, :N] = Bf.view(torch.int16)
+        B = Bp[:, :N]
+        row = {"N": N}
+        for sp in sparsities:
+            p = synth.config4("gate", N=N, with_b=False, density=1.0 - sp)
+            A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row,
+                                p.b_col, p.ab_dtype, p.c_dtype, device=dev)
+            C = A.new_c(dev, padded=True)
+            t_sp = timed(lambda: A.run(B, C))
+            check = None
+            if N == 1024:
+                W = torch.zeros((m, k), dtype=torch.float32)
+                rr = torch.from_numpy(np.repeat(np.arange(m), np.diff(p.row_ptr)))
+                W[rr, torch.from_numpy(p.col_idx.astype(np.int64))] = \
+                    torch.from_numpy(p.vals.view(np.int16).copy()).view(torch.bfloat16).float()
+                ref = torch.mm(W.to(dev), Bf.float())
+                err = (C.float() - ref).abs().max().item()
+                check = err <= 2e-2 * max(1.0, ref.abs().max().item())
+                del W, ref
+            row["s%d" % round(sp * 100)] = {"ms": t_sp,
+                                             "kernel": A.plan.info()["kernel"],
+                                             "blocks_per_row": p.meta["blocks_per_row"],
+                                             "checked": check}
+            del A, C
+        Wd = (torch.randn((m, k), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        Cd = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+        t_dense = timed(lambda: torch.mm(Wd, Bf, out=Cd))
+        del Wd
+        row["dense_ms"] = t_dense
+        for sp in sparsities:
+            row["s%d" % round(sp * 100)]["speedup"] = t_dense / row["s%d" % round(sp * 100)]["ms"]
+        rows.append(row)
+        print("N=%6d dense %.3f ms | " % (N, t_dense) + " | ".join(
+            "%d%%: %.3f ms (%.2fx, k%d)" % (round(sp * 100), row["s%d" % round(sp * 100)]["ms"],
+                                             row["s%d" % round(sp * 100)]["speedup"],
+                                             row["s%d" % round(sp * 100)]["kernel"])
+            for sp in sparsities), flush=True)
+        del Bf, Bp, B, Cd
+    print(json.dumps({"ffn_gate_table": rows}))
+    if any(r[k_]["checked"] is False for r in rows for k_ in r if k_.startswith("s")):
+        raise SystemExit("a sparse result disagrees with torch.mm of its densified weight")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +308,7 @@ def main():
     ap.add_argument("--which", default="gate", help="config 4 weight: gate, up or down")
     ap.add_argument("--member", type=int, default=0, help="config 3 matrix index")
     ap.add_argument("--n3", type=int, default=128, help="config 3 N")
+    ap.add_argument("--n4", type=int, default=65536, help="config 4 N (tokens)")
     ap.add_argument("--width", type=int, default=1, help="config 5 line width in blocks")
     ap.add_argument("--split", type=int, default=0, help="WCSR sub-task size (0 = plan's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -237,6 +319,9 @@ def main():
                     help="only run a 256 MiB device copy (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the kernel / tile-shape options on this workload instead")
+    ap.add_argument("--ffn-table", action="store_true",
+                    help="gate_proj latency at 80-99%% block sparsity x N = 1K..64K against "
+                         "dense torch.mm (the paper's Table III, kernel level)")
     ap.add_argument("--col-major", action="store_true",
                     help="BCSR 64x64: B and C column-major (B^T: N x k, C^T: N x m), the "
                          "token-major activation layout")
@@ -244,6 +329,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.ffn_table:
+        run_ffn_table()
         return
 
     if args.gpus != 1:

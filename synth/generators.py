@@ -340,15 +340,17 @@ def config3_matrix(j: int, N: int, seed: int = 0, with_b: bool = True) -> Proble
 _CFG4_SHAPES = {"gate": (18944, 3584, 0), "up": (18944, 3584, 1), "down": (3584, 18944, 2)}
 
 
-def config4(which: str = "gate", N: int = 65536, seed: int = 0, with_b: bool = True) -> Problem:
+def config4(which: str = "gate", N: int = 65536, seed: int = 0, with_b: bool = True,
+            density: float = 0.1) -> Problem:
     """Qwen2.5-7B MLP weight shapes (gate/up 18944x3584, down 3584x18944), bf16
-    N(0, 0.02), 64x64 blocks, each block row keeps round(0.1 * block columns)
-    blocks chosen uniformly without replacement; activations K x N bf16 N(0,1);
-    bf16 output."""
+    N(0, 0.02), 64x64 blocks, each block row keeps round(density * block
+    columns) blocks (at least one) chosen uniformly without replacement;
+    activations K x N bf16 N(0,1); bf16 output.  density = 0.1 is the 90 %
+    block sparsity of the workload; other values serve the sparsity sweep."""
     m, k, mid = _CFG4_SHAPES[which]
     br = bc = 64
     nbr, nbc = m // br, k // bc
-    keep = int(round(0.1 * nbc))
+    keep = max(1, int(round(density * nbc)))
     g = rng_for(4, mid, 0, seed)
     sel = _sample_rows(g, np.full(nbr, nbc), np.full(nbr, keep)).reshape(nbr, keep)
     ptr, cols = _block_rows_to_csr(nbr, br, bc, m, k, list(sel))
