@@ -29,8 +29,10 @@ if ROOT not in sys.path:
 
 METRIC = "effective SpMM TFLOP/s (2·nnz·N) BCSR & WCSR; % of MFMA/HBM roofline"
 PEAK_MFMA_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA
+PEAK_MFMA_TFLOPS_FP8 = 5000.0  # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 E_C = {"fp32": 4, "bf16": 2, "fp16": 2}
+E_AB = {"bf16": 2, "fp16": 2, "fp8": 1}
 
 
 def make_problem(cfg: int, args):
@@ -45,9 +47,9 @@ def make_problem(cfg: int, args):
         return p, "cfg3 member %d: WCSR m=k=%d, N=%d, %s" % (
             args.member, p.m, p.N, "banded" if p.meta["banded"] else "uniform")
     if cfg == 4:
-        p = synth.config4(args.which, N=args.n4)
-        return p, "cfg4 %s: BCSR %dx%d bf16, 64x64 blocks, 90%% block sparse, N=65536, bf16 out" % (
-            args.which, p.m, p.k)
+        p = synth.config4(args.which, N=args.n4, ab_dtype="fp8" if args.fp8 else "bf16")
+        return p, "cfg4 %s: BCSR %dx%d %s, 64x64 blocks, 90%% block sparse, N=%d, bf16 out" % (
+            args.which, p.m, p.k, p.ab_dtype, p.N)
     if cfg == 5:
         p = synth.config5(width=args.width)
         return p, "cfg5: BCSR P*V 65536x65536 bf16, 64x64 blocks (diag + 4 vertical + 8 slash%s), " \
@@ -69,7 +71,8 @@ def algorithmic(p, A):
         P = A.h_idx.size
         brows = int(np.unique(A.h_idx[A.h_idx >= 0]).size)
         meta = 4 * P + 4 * A.h_ptr.size
-    bytes_alg = 2 * stored + meta + 2 * N * brows + E_C[p.c_dtype] * p.m * N
+    e = E_AB[p.ab_dtype]
+    bytes_alg = e * stored + meta + e * N * brows + E_C[p.c_dtype] * p.m * N
     return {"flops_true": 2.0 * p.nnz * N, "flops_stored": 2.0 * stored * N,
             "bytes_alg": float(bytes_alg), "b_rows_referenced": brows}
 
@@ -204,7 +207,8 @@ def run_sweep(p, A, B, C, alg, workload, base=None):
             print("%-64s %6s %10s %9s %7s %s" % (json.dumps(opts), "-", "-", "-", "-", same))
             continue
         tf = alg["flops_true"] / (us * 1e-6) / 1e12
-        t_roof = max(alg["flops_stored"] / (PEAK_MFMA_TFLOPS * 1e12), alg["bytes_alg"] / (PEAK_HBM_GBS * 1e9))
+        peak = PEAK_MFMA_TFLOPS_FP8 if p.ab_dtype == "fp8" else PEAK_MFMA_TFLOPS
+        t_roof = max(alg["flops_stored"] / (peak * 1e12), alg["bytes_alg"] / (PEAK_HBM_GBS * 1e9))
         print("%-64s %6d %10.1f %9.1f %7.3f %s" % (json.dumps(opts) if opts != "default" else
                                                   "default (kernel %d)" % info["kernel"],
                                                   info["tile_cols"], us, tf, t_roof / (us * 1e-6),
@@ -322,10 +326,14 @@ def main():
     ap.add_argument("--ffn-table", action="store_true",
                     help="gate_proj latency at 80-99%% block sparsity x N = 1K..64K against "
                          "dense torch.mm (the paper's Table III, kernel level)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="config 4 with FP8 E4M3 weights and activations")
     ap.add_argument("--col-major", action="store_true",
                     help="BCSR 64x64: B and C column-major (B^T: N x k, C^T: N x m), the "
                          "token-major activation layout")
     args = ap.parse_args()
+    if args.fp8 and args.config != 4:
+        raise SystemExit("--fp8 applies to config 4")
 
     if args.copy_probe:
         copy_probe()
@@ -407,18 +415,19 @@ def main():
         cold = float(np.mean(cms)) / 1e3
         del flush
 
-    t_roof_mfma = alg["flops_stored"] / (PEAK_MFMA_TFLOPS * 1e12)
+    peak_mfma = PEAK_MFMA_TFLOPS_FP8 if p.ab_dtype == "fp8" else PEAK_MFMA_TFLOPS
+    t_roof_mfma = alg["flops_stored"] / (peak_mfma * 1e12)
     t_roof_hbm = alg["bytes_alg"] / (PEAK_HBM_GBS * 1e9)
     if t_roof_hbm >= t_roof_mfma:
         roof = {"bound": "hbm", "achieved": alg["bytes_alg"] / t_kernel / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     else:
         roof = {"bound": "mfma", "achieved": alg["flops_stored"] / t_kernel / 1e12,
-                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"}
+                "peak": peak_mfma, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     key = "config%d" % args.config + ("_" + args.which if args.config == 4 else "") + \
           ("_m%d_n%d" % (args.member, args.n3) if args.config == 3 else "") + \
-          ("_colmajor" if args.col_major else "")
+          ("_colmajor" if args.col_major else "") + ("_fp8" if args.fp8 else "")
     roof["traffic"] = measured_traffic(key)
     roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["kernel_us"] = t_kernel * 1e6

@@ -40,7 +40,10 @@ typedef enum {
     SPMM_ERR_HIP = 5               /* HIP runtime / launch error, or no usable gfx950 device */
 } spmm_status_t;
 
-typedef enum { SPMM_FP16 = 0, SPMM_BF16 = 1, SPMM_FP32 = 2 } spmm_dtype_t;
+/* Element types.  SPMM_FP8_E4M3: OCP FP8 E4M3 (1 sign, 4 exponent bits with
+ * bias 7, 3 fraction bits, no infinities), the format of gfx950's fp8 MFMA;
+ * A and B only (BCSR), the paper's first future direction (Section V). */
+typedef enum { SPMM_FP16 = 0, SPMM_BF16 = 1, SPMM_FP32 = 2, SPMM_FP8_E4M3 = 3 } spmm_dtype_t;
 
 typedef struct spmm_plan_s *spmm_plan_t;
 
@@ -89,6 +92,12 @@ spmm_status_t spmm_csr_to_bcsr(int64_t m, int64_t k, const int32_t *h_row_ptr,
                                const int32_t *h_col_idx, const uint16_t *h_values, int32_t b_row,
                                int32_t b_col, int32_t *h_block_row_ptr, int32_t *h_block_col_idx,
                                uint16_t *h_blocks);
+/* The same for 8-bit codes (SPMM_FP8_E4M3 values): blocks[nnz_blocks*b_row*b_col]
+ * bytes, absent entries 0x00 (+0). */
+spmm_status_t spmm_csr_to_bcsr8(int64_t m, int64_t k, const int32_t *h_row_ptr,
+                                const int32_t *h_col_idx, const uint8_t *h_values, int32_t b_row,
+                                int32_t b_col, int32_t *h_block_row_ptr, int32_t *h_block_col_idx,
+                                uint8_t *h_blocks);
 
 /* WCSR (Section II-C "Window Compressed Sparse Row", Fig. 2): rows are grouped
  * into windows of b_row rows; window w keeps the sorted union of its rows'
@@ -161,7 +170,9 @@ spmm_status_t spmm_csr_permute(int64_t n, const int32_t *h_row_ptr, const int32_
  *
  * Supported: b_row in {16, 32, 64}; b_col a multiple of 8 (BCSR: a power of two
  * in [8, 256]);
- * ab_dtype FP16 or BF16 (A and B alike); c_dtype FP32, BF16 or FP16; N a
+ * ab_dtype FP16 or BF16 (A and B alike), or FP8_E4M3 for BCSR on kernel 2
+ * (b_row = b_col = 64, N >= 4096, row-major B and C; values built with
+ * spmm_csr_to_bcsr8, B one byte per element); c_dtype FP32, BF16 or FP16; N a
  * multiple of 8 (m = 0 or N = 0 gives a plan whose runs do nothing); k < 2^24
  * (B row numbers are multiplied in 24-bit arithmetic); device index and value
  * arrays 16-byte aligned.  Otherwise UNSUPPORTED.
@@ -266,8 +277,8 @@ spmm_status_t spmm_wcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void
 spmm_status_t spmm_plan_info(spmm_plan_t plan, spmm_plan_info_t *info);
 
 /* Leading dimension (elements) to allocate for a dense operand with N columns of
- * elem_bytes-byte elements: N rounded up to 8, plus 64 when the row pitch would
- * be a multiple of 4 KiB.  With power-of-two pitches the rows that one column
+ * elem_bytes-byte elements: N rounded up to 8, plus 64 (128 for 1-byte elements)
+ * when the row pitch would be a multiple of 4 KiB.  With power-of-two pitches the rows that one column
  * tile gathers from B all fall into the same L2 sets; the pad spreads them.
  * Any ldb/ldc >= N that is a multiple of 8 is valid; this only affects speed.
  * Returns N unchanged for N <= 0 or elem_bytes <= 0. */

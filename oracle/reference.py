@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 ORACLE_SRC = os.path.join(_HERE, "spmm_oracle.c")
 ORACLE_LIB = os.path.join(_HERE, "liboracle.so")
 
-_DTYPES = {"fp16": 0, "bf16": 1}
+_DTYPES = {"fp16": 0, "bf16": 1, "fp8": 3}
 
 
 def build_oracle(force: bool = False) -> str:

@@ -26,14 +26,35 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_FP16 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_FP16 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 3 };
 
-/* Exact value of a 16-bit floating-point code.
+/* Exact value of an OCP FP8 E4M3 code (the low byte): 1 sign, 4 exponent bits
+ * (bias 7), 3 fraction bits; exponent field 0 = zero/subnormal; no infinities,
+ * exponent and fraction all ones = NaN. */
+static double decode_fp8_e4m3(uint16_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 15;
+    int f = code & 7;
+    double v;
+    if (e == 15 && f == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)f, 1 - 7 - 3);          /* 0.f * 2^(1 - bias) */
+    else
+        v = ldexp((double)(8 + f), e - 7 - 3);    /* 1.f * 2^(e - bias) */
+    return sign ? -v : v;
+}
+
+/* Exact value of a 16-bit floating-point code (or, for ORACLE_FP8_E4M3, of the
+ * FP8 code in its low byte).
  * binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits.
  * bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits (the upper half of
  * an IEEE single). Exponent field 0 = zero/subnormal, all ones = inf/NaN. */
 double oracle_decode16(uint16_t code, int dtype)
 {
+    if (dtype == ORACLE_FP8_E4M3)
+        return decode_fp8_e4m3(code);
     int ebits = (dtype == ORACLE_BF16) ? 8 : 5;
     int fbits = (dtype == ORACLE_BF16) ? 7 : 10;
     int bias = (1 << (ebits - 1)) - 1;

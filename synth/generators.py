@@ -53,11 +53,35 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes of ``x`` (1 sign, 4 exponent bits with bias 7, 3
+    mantissa bits, subnormals down to 2^-9, no infinities), round to nearest
+    even, magnitudes past 448 saturated to 448; returned as uint16 (0..255)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    sign = np.signbit(np.asarray(x, dtype=np.float64)).astype(np.uint16) << 7
+    out = np.zeros(a.shape, dtype=np.uint16)
+    sub = a < 2.0 ** -6
+    # subnormal: m * 2^-9 with m = 0..8 (m = 8 is the code of 2^-6, the smallest normal)
+    out[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.uint16)
+    mant, ex = np.frexp(a[~sub])            # a = mant * 2^ex, mant in [0.5, 1)
+    e = ex.astype(np.int64) - 1             # a = (2 mant) * 2^e
+    q = np.rint((2.0 * mant - 1.0) * 8.0).astype(np.int64)   # 3 fraction bits, 0..8
+    e = np.where(q == 8, e + 1, e)
+    q = np.where(q == 8, 0, q)
+    big = (e > 8) | ((e == 8) & (q > 6))
+    e = np.where(big, 8, e)
+    q = np.where(big, 6, q)
+    out[~sub] = (((e + 7) << 3) | q).astype(np.uint16)
+    return out | sign
+
+
 def _bits(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "fp16":
         return fp16_bits(x)
     if dtype == "bf16":
         return bf16_bits(x)
+    if dtype == "fp8":
+        return fp8_e4m3_bits(x)
     raise ValueError(dtype)
 
 
@@ -65,8 +89,9 @@ def _nonzero_values(rng: np.random.Generator, n: int, dtype: str, draw) -> np.nd
     """``n`` value bits from ``draw(rng, size)``; draws that round to +-0 are redrawn,
     so every structural entry holds a nonzero value."""
     bits = _bits(draw(rng, n), dtype)
+    mag = 0x7F if dtype == "fp8" else 0x7FFF
     while True:
-        z = np.flatnonzero((bits & 0x7FFF) == 0)
+        z = np.flatnonzero((bits & mag) == 0)
         if z.size == 0:
             return bits
         bits[z] = _bits(draw(rng, z.size), dtype)
@@ -341,12 +366,15 @@ _CFG4_SHAPES = {"gate": (18944, 3584, 0), "up": (18944, 3584, 1), "down": (3584,
 
 
 def config4(which: str = "gate", N: int = 65536, seed: int = 0, with_b: bool = True,
-            density: float = 0.1) -> Problem:
+            density: float = 0.1, ab_dtype: str = "bf16") -> Problem:
     """Qwen2.5-7B MLP weight shapes (gate/up 18944x3584, down 3584x18944), bf16
     N(0, 0.02), 64x64 blocks, each block row keeps round(density * block
     columns) blocks (at least one) chosen uniformly without replacement;
     activations K x N bf16 N(0,1); bf16 output.  density = 0.1 is the 90 %
-    block sparsity of the workload; other values serve the sparsity sweep."""
+    block sparsity of the workload; other values serve the sparsity sweep.
+    ab_dtype = "fp8": the same pattern with FP8 E4M3 weights and activations,
+    weights drawn N(0, 1) (as if pre-multiplied by a per-tensor scale of 50,
+    which keeps them clear of the E4M3 subnormals)."""
     m, k, mid = _CFG4_SHAPES[which]
     br = bc = 64
     nbr, nbc = m // br, k // bc
@@ -354,11 +382,15 @@ def config4(which: str = "gate", N: int = 65536, seed: int = 0, with_b: bool = T
     g = rng_for(4, mid, 0, seed)
     sel = _sample_rows(g, np.full(nbr, nbc), np.full(nbr, keep)).reshape(nbr, keep)
     ptr, cols = _block_rows_to_csr(nbr, br, bc, m, k, list(sel))
-    vals = _nonzero_values(rng_for(4, mid, 1, seed), cols.size, "bf16",
-                           lambda r, n: r.normal(0.0, 0.02, n))
-    B = make_dense_b(rng_for(4, mid, 2, seed), k, N, "bf16") if with_b else np.zeros((0, N), np.uint16)
-    return _finish(f"cfg4_bcsr_{which}", m, k, N, ptr, cols, vals, B, "bf16", "bf16", "bcsr",
-                   br, bc, which=which, blocks_per_row=keep)
+    if ab_dtype not in ("bf16", "fp8"):
+        raise ValueError(ab_dtype)
+    sd = 0.02 if ab_dtype == "bf16" else 1.0
+    vals = _nonzero_values(rng_for(4, mid, 1, seed), cols.size, ab_dtype,
+                           lambda r, n: r.normal(0.0, sd, n))
+    B = make_dense_b(rng_for(4, mid, 2, seed), k, N, ab_dtype) if with_b else np.zeros((0, N), np.uint16)
+    return _finish(f"cfg4_bcsr_{which}" + ("_fp8" if ab_dtype == "fp8" else ""), m, k, N, ptr,
+                   cols, vals, B, ab_dtype, "bf16", "bcsr", br, bc, which=which,
+                   blocks_per_row=keep)
 
 
 def config5(seed: int = 0, width: int = 1, N: int = 128, with_b: bool = True) -> Problem:

@@ -56,6 +56,23 @@ def test_builders_match_oracle_block_patterns():
         assert _same(nb, ob) and _same(nw, ow)
 
 
+def test_bcsr8_builder_matches_oracle():
+    """The 8-bit builder (FP8 E4M3 codes) lays out blocks exactly as the 16-bit
+    one: the oracle's encoding with every code narrowed to a byte."""
+    for s, (br, bc) in enumerate([(64, 64), (16, 16), (32, 8)]):
+        p = synth.block_problem(300, 260, 8, br, bc, 0.2, seed=s, ab_dtype="fp8",
+                                entry_density=0.6)
+        assert int(p.vals.max()) <= 255
+        ptr, idx, blk = ws.csr_to_bcsr(p.m, p.k, p.row_ptr, p.col_idx, p.vals, br, bc,
+                                       code_bytes=1)
+        optr, oidx, oblk = oracle.encode_bcsr(p.m, p.k, p.row_ptr, p.col_idx, p.vals, br, bc)
+        assert blk.dtype == np.uint8
+        assert np.array_equal(ptr, optr) and np.array_equal(idx, oidx)
+        assert np.array_equal(blk, oblk.astype(np.uint8))
+    with pytest.raises(ValueError):
+        ws.csr_to_bcsr(2, 2, [0, 1, 1], [0], np.array([300], np.uint16), 16, 16, code_bytes=1)
+
+
 def test_one_by_one_is_csr():
     p = synth.random_problem(64, 90, 8, 0.1, seed=4)
     brp, bci, blk = ws.csr_to_bcsr(p.m, p.k, p.row_ptr, p.col_idx, p.vals, 1, 1)

@@ -468,3 +468,79 @@ def test_col_major_rejected_where_unsupported(ws):
     with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):   # m, k not multiples of 8
         ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
                         p.ab_dtype, p.c_dtype, options={"col_major": 1})
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 A and B (the sweep kernel)
+# --------------------------------------------------------------------------
+
+FP8_CASES = [
+    # m, k, N, block density, c, ranges per XCD, kind
+    (1280, 640, 4104, 0.25, "bf16", 1, "normal"),
+    (700, 600, 8192, 0.3, "fp32", 2, "normal"),
+    (640, 512, 4096, 0.95, "fp16", 1, "normal"),
+    (576, 520, 5000, 0.4, "fp32", 0, "int"),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fp8_sweep_kernel(ws, case):
+    """FP8 E4M3 A and B, fp32 accumulation: ragged m, k and N, empty and full
+    block rows, padded leading dimensions; small-integer data (exact in E4M3,
+    every partial sum exact in fp32) must match the oracle bit for bit."""
+    m, k, N, dens, ct, H, kind = case
+    p = synth.block_problem(m, k, N, 64, 64, dens, seed=m + N + H, ab_dtype="fp8", c_dtype=ct,
+                            kind=kind)
+    opts = {"ranges_per_xcd": H} if H else None
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options=opts)
+    assert A.plan.info()["kernel"] == 2
+    assert A.d_vals.dtype == torch.uint8 and A.d_vals.numel() == A.h_vals.size
+    B = A.device_b(p.B, padded=True)
+    assert B.dtype == torch.uint8 and B.stride(0) == ws.recommended_ld(p.N, 1)
+    C = A.new_c(padded=True)
+    C.fill_(float("nan"))
+    A.run(B, C)
+    torch.cuda.synchronize()
+    got = C.float().cpu().numpy().astype(np.float64)
+    ref = check(p, got)
+    if kind == "int":
+        assert np.array_equal(got, ref)
+
+
+def test_config4_gate_fp8_sampled(ws):
+    p = synth.config4("gate", ab_dtype="fp8")
+    _say("gpu case:", p.name, p.m, p.k, p.N)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    assert A.plan.info()["kernel"] == 2
+    B = A.device_b(p.B)
+    C = A.new_c()
+    C.fill_(float("nan"))
+    A.run(B, C)
+    torch.cuda.synchronize()
+    got = C.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    rows = np.random.default_rng(4).choice(p.m, 48, replace=False)
+    check(p, got, rows=rows)
+
+
+def test_fp8_rejected_where_unsupported(ws):
+    def plan(p, options=None, fmt=None):
+        return ws.DeviceSparse(fmt or p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row,
+                               p.b_col, p.ab_dtype, p.c_dtype, options=options)
+    p = synth.block_problem(256, 256, 4096, 64, 64, 0.3, seed=5, ab_dtype="fp8")
+    for options in ({"kernel": 1}, {"kernel": 0}, {"col_major": 1}):
+        with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):
+            plan(p, options)
+    q = synth.block_problem(256, 256, 4096, 32, 32, 0.3, seed=5, ab_dtype="fp8")
+    with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):
+        plan(q)
+    q = synth.block_problem(256, 256, 1024, 64, 64, 0.3, seed=5, ab_dtype="fp8")
+    with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):   # N too small for the sweep
+        plan(q)
+    q = synth.block_problem(128, 1024, 4096, 64, 64, 1.0, seed=5, ab_dtype="fp8")
+    with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):   # 16 blocks in a block row
+        plan(q)
+    with pytest.raises(ValueError):
+        plan(p, fmt="wcsr")

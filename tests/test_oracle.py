@@ -484,3 +484,29 @@ def test_symmetric_permutation_keeps_the_product():
 
 def oracle_encode16(x: float) -> int:
     return int(np.asarray(x, np.float16).view(np.uint16))
+
+
+def test_fp8_e4m3_decode_matches_torch_on_all_codes():
+    # OCP FP8 E4M3 (the format of gfx950's fp8 MFMA): every one of the 256 codes
+    # against torch's float8_e4m3fn, NaN for both NaN codes
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint16)
+    ours = oracle.decode16(codes, "fp8")
+    ref = torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    both_nan = np.isnan(ours) & np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)) and np.isnan(ours).sum() == 2
+    assert np.array_equal(ours[~both_nan], ref[~both_nan])
+    assert oracle.decode16(np.array([0x7E, 0x01, 0x08, 0xB8]), "fp8").tolist() == [448.0, 2.0 ** -9,
+                                                                                    2.0 ** -6, -1.0]
+
+
+def test_fp8_generator_encoding_matches_torch():
+    torch = pytest.importorskip("torch")
+    from synth.generators import fp8_e4m3_bits
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(100000) * s for s in (0.002, 0.02, 1.0, 50.0)]).astype(np.float32)
+    ref = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(fp8_e4m3_bits(x), ref.astype(np.uint16))
+    # and the oracle's decoder inverts it on its range
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint16)
+    assert np.array_equal(fp8_e4m3_bits(oracle.decode16(codes, "fp8")), codes)

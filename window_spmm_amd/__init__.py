@@ -30,9 +30,10 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARGUMENT, ERR_BAD_FORMAT, ERR_UNSUPPORTED, ERR_OUT_OF_MEMORY, ERR_HIP = range(6)
-DTYPES = {"fp16": 0, "bf16": 1, "fp32": 2}
+DTYPES = {"fp16": 0, "bf16": 1, "fp32": 2, "fp8": 3}
 EXPORTED = [
-    "spmm_csr_to_bcsr_count", "spmm_csr_to_bcsr", "spmm_csr_to_wcsr_count", "spmm_csr_to_wcsr",
+    "spmm_csr_to_bcsr_count", "spmm_csr_to_bcsr", "spmm_csr_to_bcsr8", "spmm_csr_to_wcsr_count",
+    "spmm_csr_to_wcsr",
     "spmm_wcsr_split_count", "spmm_wcsr_split", "spmm_bcsr_plan", "spmm_wcsr_plan",
     "spmm_bcsr_run", "spmm_wcsr_run", "spmm_plan_info", "spmm_plan_destroy",
     "spmm_status_string", "spmm_last_error", "spmm_recommended_ld", "spmm_rcm_order",
@@ -82,6 +83,7 @@ _Psz = ctypes.POINTER(ctypes.c_size_t)
 _sigs = {
     "spmm_csr_to_bcsr_count": [_i64, _i64, _vp, _vp, _i32, _i32, _P64],
     "spmm_csr_to_bcsr": [_i64, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp],
+    "spmm_csr_to_bcsr8": [_i64, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp],
     "spmm_csr_to_wcsr_count": [_i64, _i64, _vp, _vp, _i32, _i32, _P64],
     "spmm_csr_to_wcsr": [_i64, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp],
     "spmm_wcsr_split_count": [_i64, _vp, _i64, _P64, _P64],
@@ -138,6 +140,15 @@ def _host(a, dtype) -> np.ndarray:
     return a
 
 
+def _codes8(a) -> np.ndarray:
+    """8-bit codes from any integer array holding values 0..255 (e.g. FP8 codes
+    kept in uint16 arrays); anything else is an error, never a truncation."""
+    a = np.asarray(a)
+    if a.dtype != np.uint8 and a.size and (int(a.min()) < 0 or int(a.max()) > 255):
+        raise ValueError("8-bit codes must lie in 0..255")
+    return np.ascontiguousarray(a, dtype=np.uint8)
+
+
 def _hp(a: np.ndarray):
     return ctypes.c_void_p(a.ctypes.data) if a.size else ctypes.c_void_p(0)
 
@@ -155,17 +166,24 @@ def _dp(x) -> ctypes.c_void_p:
 # host-side builders
 # --------------------------------------------------------------------------
 
-def csr_to_bcsr(m: int, k: int, row_ptr, col_idx, values, b_row: int, b_col: int):
-    """CSR -> BCSR ``(block_row_ptr, block_col_idx, blocks)`` (numpy)."""
-    rp, ci, v = _host(row_ptr, np.int32), _host(col_idx, np.int32), _host(values, np.uint16)
+def csr_to_bcsr(m: int, k: int, row_ptr, col_idx, values, b_row: int, b_col: int,
+                code_bytes: int = 2):
+    """CSR -> BCSR ``(block_row_ptr, block_col_idx, blocks)`` (numpy).  Values
+    are 16-bit codes, or 8-bit codes (FP8 E4M3) with ``code_bytes=1``."""
+    if code_bytes not in (1, 2):
+        raise ValueError("code_bytes must be 1 or 2")
+    ct = np.uint8 if code_bytes == 1 else np.uint16
+    rp, ci = _host(row_ptr, np.int32), _host(col_idx, np.int32)
+    v = _codes8(values) if code_bytes == 1 else _host(values, ct)
     n = ctypes.c_int64(0)
     _check(_lib.spmm_csr_to_bcsr_count(m, k, _hp(rp), _hp(ci), b_row, b_col, ctypes.byref(n)),
            "spmm_csr_to_bcsr_count")
     brp = np.empty(-(-m // b_row) + 1, np.int32)
     bci = np.empty(n.value, np.int32)
-    blk = np.empty(n.value * b_row * b_col, np.uint16)
-    _check(_lib.spmm_csr_to_bcsr(m, k, _hp(rp), _hp(ci), _hp(v), b_row, b_col, _hp(brp), _hp(bci),
-                                 _hp(blk)), "spmm_csr_to_bcsr")
+    blk = np.empty(n.value * b_row * b_col, ct)
+    fn, name = (_lib.spmm_csr_to_bcsr8, "spmm_csr_to_bcsr8") if code_bytes == 1 else \
+        (_lib.spmm_csr_to_bcsr, "spmm_csr_to_bcsr")
+    _check(fn(m, k, _hp(rp), _hp(ci), _hp(v), b_row, b_col, _hp(brp), _hp(bci), _hp(blk)), name)
     return brp, bci, blk
 
 
@@ -328,8 +346,12 @@ class DeviceSparse:
         self.fmt, self.m, self.k, self.N = fmt, int(m), int(k), int(N)
         self.ab_dtype, self.c_dtype = ab_dtype, c_dtype
         self.b_row, self.b_col = int(b_row), int(b_col)
+        self.code_bytes = 1 if ab_dtype == "fp8" else 2
         if fmt == "bcsr":
-            ptr, idx, vals = csr_to_bcsr(m, k, row_ptr, col_idx, values, b_row, b_col)
+            ptr, idx, vals = csr_to_bcsr(m, k, row_ptr, col_idx, values, b_row, b_col,
+                                         self.code_bytes)
+        elif self.code_bytes == 1:
+            raise ValueError("WCSR holds 16-bit values only")
         elif fmt == "wcsr":
             ptr, idx, vals = csr_to_wcsr(m, k, row_ptr, col_idx, values, b_row, b_col)
         else:
@@ -337,8 +359,9 @@ class DeviceSparse:
         self.h_ptr, self.h_idx, self.h_vals = ptr, idx, vals
         self.d_idx = torch.from_numpy(idx.copy()).to(device) if idx.size else \
             torch.empty(4, dtype=torch.int32, device=device)
-        self.d_vals = torch.from_numpy(vals.view(np.int16).copy()).to(device) if vals.size else \
-            torch.empty(8, dtype=torch.int16, device=device)
+        vt = (np.uint8, torch.uint8) if self.code_bytes == 1 else (np.int16, torch.int16)
+        self.d_vals = torch.from_numpy(vals.view(vt[0]).copy()).to(device) if vals.size else \
+            torch.empty(16, dtype=vt[1], device=device)
         self.device, self.split_cols = device, int(split_cols)
         self.replan(options)
 
@@ -375,13 +398,16 @@ class DeviceSparse:
         return torch.empty((self.m, ld), dtype=dt, device=device)[:, :self.N]
 
     def device_b(self, codes: np.ndarray, device="cuda", padded: bool = False):
-        """Copies host 16-bit codes of B (k x N) to the device (padded rows optionally)."""
+        """Copies host codes of B (k x N; 16-bit, or 8-bit for FP8) to the device
+        (padded rows optionally)."""
         import torch
-        src = torch.from_numpy(np.ascontiguousarray(codes).view(np.int16))
+        vt = (np.uint8, torch.uint8) if self.code_bytes == 1 else (np.int16, torch.int16)
+        src = torch.from_numpy(_codes8(codes) if self.code_bytes == 1 else
+                               np.ascontiguousarray(codes).view(vt[0]))
         if not padded:
             return src.to(device)
-        ld = recommended_ld(self.N, 2)
-        out = torch.empty((self.k, ld), dtype=torch.int16, device=device)[:, :self.N]
+        ld = recommended_ld(self.N, self.code_bytes)
+        out = torch.empty((self.k, ld), dtype=vt[1], device=device)[:, :self.N]
         out.copy_(src)
         return out
 

@@ -115,8 +115,8 @@ spmm_status_t check_common(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, i
     if (b_col % 8 != 0 || (bcsr && (b_col > 256 || (b_col & (b_col - 1)) != 0)))
         return fail(SPMM_ERR_UNSUPPORTED, "b_col = %d: must be %s", b_col,
                     bcsr ? "a power of two in [8, 256]" : "a multiple of 8");
-    if (ab != SPMM_FP16 && ab != SPMM_BF16)
-        return fail(SPMM_ERR_UNSUPPORTED, "A/B dtype must be FP16 or BF16");
+    if (ab != SPMM_FP16 && ab != SPMM_BF16 && !(bcsr && ab == SPMM_FP8_E4M3))
+        return fail(SPMM_ERR_UNSUPPORTED, "A/B dtype must be FP16 or BF16 (FP8_E4M3: BCSR only)");
     if (ct != SPMM_FP32 && ct != SPMM_BF16 && ct != SPMM_FP16)
         return fail(SPMM_ERR_UNSUPPORTED, "C dtype must be FP32, BF16 or FP16");
     if (N % 8 != 0)
@@ -218,6 +218,7 @@ spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int
         return fail(SPMM_ERR_UNSUPPORTED, "B and C must be 16-byte aligned");
     const bool cm = pl->opt.col_major != 0;
     const uint64_t esz = pl->ct == SPMM_FP32 ? 4u : 2u;
+    const uint64_t esz_b = pl->ab == SPMM_FP8_E4M3 ? 1u : 2u;
     if (cm ? (ldb < pl->k || ldc < pl->m) : (ldb < pl->N || ldc < pl->N))
         return fail(SPMM_ERR_UNSUPPORTED, cm ? "column-major: ldb must be >= k and ldc >= m"
                                              : "ldb/ldc must be >= N");
@@ -225,7 +226,7 @@ spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int
         return fail(SPMM_ERR_UNSUPPORTED, "ldb/ldc must be multiples of 8");
     if (ldb >= (int64_t(1) << 23))
         return fail(SPMM_ERR_UNSUPPORTED, "ldb must be below 2^23");
-    if ((uint64_t)(cm ? pl->N : pl->k) * (uint64_t)ldb * 2u >= kMaxBBytes)
+    if ((uint64_t)(cm ? pl->N : pl->k) * (uint64_t)ldb * esz_b >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "B must be smaller than 4 GiB - 256 bytes");
     // (the last column tile's lanes address up to 511 columns past N; their
     // 32-bit store offsets must stay past the end of C^T without wrapping)
@@ -273,9 +274,10 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.N = pl->N;
     // the extent of B ends with column N - 1 of row k - 1: loads of columns past N
     // in that row and of rows past k fall outside it and read zeros
+    const uint64_t esz_b = pl->ab == SPMM_FP8_E4M3 ? 1u : 2u;
     p.b_bytes = pl->opt.col_major
-                    ? ((uint64_t)(pl->N - 1) * (uint64_t)ldb + (uint64_t)pl->k) * 2u
-                    : pl->k > 0 ? ((uint64_t)(pl->k - 1) * (uint64_t)ldb + (uint64_t)pl->N) * 2u : 0u;
+                    ? ((uint64_t)(pl->N - 1) * (uint64_t)ldb + (uint64_t)pl->k) * esz_b
+                    : pl->k > 0 ? ((uint64_t)(pl->k - 1) * (uint64_t)ldb + (uint64_t)pl->N) * esz_b : 0u;
     p.col_major = pl->opt.col_major;
     p.n_items = pl->n_items;
     p.n_col_tiles = pl->n_col_tiles;
@@ -658,13 +660,21 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
                             sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks),
                                                 opt.col_major != 0) >= 2;
     const bool sweep_auto = sweep_fits && tiles512 >= 16;
+    if (ab_dtype == SPMM_FP8_E4M3 &&
+        (!sweep_fits || opt.col_major || (opt.kernel != -1 && opt.kernel != 2))) {
+        free_plan(pl);
+        return fail(SPMM_ERR_UNSUPPORTED,
+                    "FP8_E4M3 runs on the sweep kernel: b_row = b_col = 64, N >= 4096, at most %d "
+                    "blocks per block row, row-major B and C", kSweepMaxBlocks);
+    }
     if (opt.col_major && (!lds_ok || m % 8 || k % 8 || opt.kernel == 0)) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED,
                     "column-major B and C need b_row = b_col = 64, N >= 256, m and k multiples "
                     "of 8 and kernel 1 or 2");
     }
-    pl->kernel = opt.kernel >= 0 ? opt.kernel : sweep_auto ? 2 : lds_ok ? 1 : 0;
+    pl->kernel = opt.kernel >= 0 ? opt.kernel
+                 : sweep_auto || ab_dtype == SPMM_FP8_E4M3 ? 2 : lds_ok ? 1 : 0;
     if ((pl->kernel == 1 && !lds_ok) || (pl->kernel == 2 && !sweep_fits)) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED,
@@ -842,7 +852,7 @@ extern "C" int64_t spmm_recommended_ld(int64_t N, int32_t elem_bytes)
         return N;
     const int64_t ld = ceil_div(N, 8) * 8;
     // Row pitches that are a multiple of 4 KiB put the rows of a column slice into
-    // the same L2 sets; 64 extra elements (an odd number of 128-byte lines for
-    // 16-bit data) spread them.
-    return (ld * elem_bytes) % 4096 == 0 ? ld + 64 : ld;
+    // the same L2 sets; 64 extra elements (128 for 1-byte data, so one 128-byte
+    // line for 8- and 16-bit data) spread them.
+    return (ld * elem_bytes) % 4096 == 0 ? ld + (elem_bytes == 1 ? 128 : 64) : ld;
 }

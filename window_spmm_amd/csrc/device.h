@@ -58,6 +58,39 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// fp8 (OCP E4M3) MFMA: 8 codes of A and of B per lane, k = 8g .. 8g+7 for lane
+// 16g + i, byte 0 first.
+__device__ __forceinline__ f32x4_t mfma16x16x32_fp8(u32x2_t a, u32x2_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a),
+                                                      __builtin_bit_cast(long, b), c, 0, 0, 0);
+}
+
+// Byte transpose of one lane's 8 x 8 block: row j is b[j] (bytes 0-3 in b[j][0],
+// 4-7 in b[j][1]); out[c] receives byte column c, rows 0-3 then rows 4-7 -- the
+// MFMA B operand of column c.  Two rounds of byte selects: row pairs first
+// ([r_j c, r_j+1 c] for two columns per word), then pairs of pairs.
+__device__ __forceinline__ void transpose8x8_bytes(const uint32_t (&b)[8][2], u32x2_t (&out)[8])
+{
+    uint32_t ev[4][2], od[4][2];  // row pair, half hf: columns 4hf, 4hf+2 / 4hf+1, 4hf+3
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            ev[pr][hf] = __builtin_amdgcn_perm(b[2 * pr + 1][hf], b[2 * pr][hf], 0x06020400u);
+            od[pr][hf] = __builtin_amdgcn_perm(b[2 * pr + 1][hf], b[2 * pr][hf], 0x07030501u);
+        }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {  // w = 0: rows 0-3 (pairs 0, 1); w = 1: rows 4-7
+            out[4 * hf + 0][w] = __builtin_amdgcn_perm(ev[2 * w + 1][hf], ev[2 * w][hf], 0x05040100u);
+            out[4 * hf + 2][w] = __builtin_amdgcn_perm(ev[2 * w + 1][hf], ev[2 * w][hf], 0x07060302u);
+            out[4 * hf + 1][w] = __builtin_amdgcn_perm(od[2 * w + 1][hf], od[2 * w][hf], 0x05040100u);
+            out[4 * hf + 3][w] = __builtin_amdgcn_perm(od[2 * w + 1][hf], od[2 * w][hf], 0x07060302u);
+        }
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 

@@ -119,10 +119,13 @@ extern "C" spmm_status_t spmm_csr_to_bcsr_count(int64_t m, int64_t k, const int3
     return ok();
 }
 
-extern "C" spmm_status_t spmm_csr_to_bcsr(int64_t m, int64_t k, const int32_t *row_ptr,
-                                          const int32_t *col_idx, const uint16_t *values,
-                                          int32_t b_row, int32_t b_col, int32_t *block_row_ptr,
-                                          int32_t *block_col_idx, uint16_t *blocks)
+namespace {
+
+// The BCSR fill for codes of type T (16-bit or 8-bit values, copied bit-exactly).
+template <typename T>
+spmm_status_t bcsr_fill(int64_t m, int64_t k, const int32_t *row_ptr, const int32_t *col_idx,
+                        const T *values, int32_t b_row, int32_t b_col, int32_t *block_row_ptr,
+                        int32_t *block_col_idx, T *blocks)
 {
     int64_t nnzb = 0;
     spmm_status_t s = spmm_csr_to_bcsr_count(m, k, row_ptr, col_idx, b_row, b_col, &nnzb);
@@ -149,8 +152,8 @@ extern "C" spmm_status_t spmm_csr_to_bcsr(int64_t m, int64_t k, const int32_t *r
                 block_row_ptr[I + 1] = (int32_t)next;
                 continue;
             }
-            uint16_t *base = blocks + next * bsz;
-            std::memset(base, 0, sizeof(uint16_t) * bsz * cols.size());
+            T *base = blocks + next * bsz;
+            std::memset(base, 0, sizeof(T) * bsz * cols.size());
             for (int64_t i = r0; i < r1; ++i)
                 for (int64_t t = row_ptr[i]; t < row_ptr[i + 1]; ++t) {
                     const int32_t c = col_idx[t];
@@ -163,6 +166,26 @@ extern "C" spmm_status_t spmm_csr_to_bcsr(int64_t m, int64_t k, const int32_t *r
         return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" spmm_status_t spmm_csr_to_bcsr(int64_t m, int64_t k, const int32_t *row_ptr,
+                                          const int32_t *col_idx, const uint16_t *values,
+                                          int32_t b_row, int32_t b_col, int32_t *block_row_ptr,
+                                          int32_t *block_col_idx, uint16_t *blocks)
+{
+    return bcsr_fill<uint16_t>(m, k, row_ptr, col_idx, values, b_row, b_col, block_row_ptr,
+                               block_col_idx, blocks);
+}
+
+extern "C" spmm_status_t spmm_csr_to_bcsr8(int64_t m, int64_t k, const int32_t *row_ptr,
+                                           const int32_t *col_idx, const uint8_t *values,
+                                           int32_t b_row, int32_t b_col, int32_t *block_row_ptr,
+                                           int32_t *block_col_idx, uint8_t *blocks)
+{
+    return bcsr_fill<uint8_t>(m, k, row_ptr, col_idx, values, b_row, b_col, block_row_ptr,
+                              block_col_idx, blocks);
 }
 
 extern "C" spmm_status_t spmm_csr_to_wcsr_count(int64_t m, int64_t k, const int32_t *row_ptr,

@@ -73,7 +73,7 @@ constexpr int kSweepMaxBlocks = 8;
 // ranges of range_tiles tiles of 512 columns (256 with col_major), 4 waves,
 // every block of a block row in LDS (max_blocks <= kSweepMaxBlocks).
 hipError_t launch_bcsr64_sweep(int ab_dtype, int max_blocks, const TileParams &p, hipStream_t stream);
-size_t sweep_lds_bytes(int max_blocks);
+size_t sweep_lds_bytes(int max_blocks, int ab_dtype);
 // Work-groups of the sweep kernel resident per CU (0 if the query fails).
 int sweep_blocks_per_cu(int ab_dtype, int max_blocks, bool col_major);
 

@@ -749,12 +749,16 @@ template <int AB, int NW, bool CM>
 __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
 {
     // CM: 4 columns per lane, so that a whole block of B^T (both halves) fits
-    // one ring stage
-    constexpr int R = 64, BC = 64, MT = 4, V = CM ? 4 : 8, DW = 4;
+    // one ring stage.  F8: one-byte codes (8 columns per lane = 2 dwords per row)
+    constexpr bool F8 = AB == SPMM_FP8_E4M3;
+    static_assert(!(F8 && CM), "fp8 runs with row-major B and C");
+    constexpr int ESZ = F8 ? 1 : 2;                // bytes per A / B element
+    constexpr int R = 64, BC = 64, MT = 4, V = CM ? 4 : 8, DW = F8 ? 2 : 4;
     constexpr int NT = NW * 64;
-    constexpr int STRIDE = BC * 2 + 16;            // padded LDS row: conflict-free b128 reads
+    constexpr int STRIDE = BC * ESZ + 16;          // padded LDS row: conflict-free reads
     constexpr int ABUF = R * STRIDE;               // bytes of one block in LDS
-    constexpr int CPB = R * BC / 8;                // 16-byte chunks per block
+    constexpr int CPR = BC * ESZ / 16;             // 16-byte chunks per block row
+    constexpr int CPB = R * CPR;                   // 16-byte chunks per block
     constexpr int MAXC = kSweepMaxBlocks * CPB / NT;  // chunks per thread, fullest row
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_a[];
 
@@ -778,8 +782,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
 
     // the block row's A blocks -> LDS: every load in flight before the first store
     {
-        const __amdgpu_buffer_rsrc_t rA =
-            make_rsrc(p.A + blk0 * R * BC, (uint32_t)(nblk * R * BC * 2));
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+            reinterpret_cast<const uint8_t *>(p.A) + blk0 * R * BC * ESZ, (uint32_t)(nblk * R * BC * ESZ));
         const int nchunks = nblk * CPB;
         u32x4_t v[MAXC];
 #pragma unroll
@@ -791,8 +795,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
         for (int t = 0; t < MAXC; ++t) {
             const int c = threadIdx.x + t * NT;
             if (c < nchunks)
-                *reinterpret_cast<u32x4_t *>(lds_a + (c / CPB) * ABUF + ((c % CPB) >> 3) * STRIDE +
-                                             (c & 7) * 16) = v[t];
+                *reinterpret_cast<u32x4_t *>(lds_a + (c / CPB) * ABUF + ((c % CPB) / CPR) * STRIDE +
+                                             (c % CPR) * 16) = v[t];
         }
     }
     // block columns of the block row: lane q holds block q
@@ -801,13 +805,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
     __syncthreads();
 
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B, (uint32_t)p.b_bytes);
-    const uint32_t ldb2 = (uint32_t)p.ldb * 2;
+    const uint32_t ldb2 = (uint32_t)p.ldb * ESZ;   // bytes per B row
     const uint32_t k32 = (uint32_t)p.k;
     const uint32_t nbc = (uint32_t)((p.k + BC - 1) / BC);
     // this lane's first column in the first tile: row-major li*V + c, CM 16c + li
     const uint32_t lane_col = (uint32_t)(wave * 16 * V + (CM ? li : li * V));
     const int64_t col_first = t_begin * p.tile_cols + lane_col;
-    const uint32_t tile_bytes = (uint32_t)p.tile_cols * 2;
+    const uint32_t tile_bytes = (uint32_t)p.tile_cols * ESZ;
     const int esz = p.c_dtype == SPMM_FP32 ? 4 : 2;
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc((uint8_t *)p.C + row0 * p.ldc * esz, (uint32_t)(R * p.ldc * esz));
@@ -839,13 +843,27 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
                     buf_load<DW>(rB, (jv & (k0 + 8 * hh < k32)) ? base + (uint32_t)(16 * c) * ldb2 + 16 * hh : kOOB,
                                  st.b[2 * c + hh]);
         } else {
-            const uint32_t base = r0 * ldb2 + (uint32_t)col_first * 2 + (uint32_t)t * tile_bytes;
+            const uint32_t base = r0 * ldb2 + (uint32_t)col_first * ESZ + (uint32_t)t * tile_bytes;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 buf_load<DW>(rB, (jv & (r0 + j < k32)) ? base + (uint32_t)j * ldb2 : kOOB, st.b[j]);
         }
     };
     auto compute = [&](const BStage<DW> &st, int q, int half) {
+        if constexpr (F8) {
+            // 8 fp8 codes of A per lane (8-byte LDS reads), B by byte transpose
+            u32x2_t af[MT], bf[8];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                af[mt] = *reinterpret_cast<const u32x2_t *>(lds_a + q * ABUF + (mt * 16 + li) * STRIDE +
+                                                           half * 32 + 8 * g);
+            transpose8x8_bytes(st.b, bf);
+#pragma unroll
+            for (int c = 0; c < V; ++c)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][c] = mfma16x16x32_fp8(af[mt], bf[c], acc[mt][c]);
+        } else {
         u32x4_t af[MT];
         // CM: lane group g, half `half` holds k = 16g + 8*half .. +7 (row-major:
         // 32*half + 8g .. +7); A is read with the same permutation of k
@@ -869,6 +887,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 acc[mt][c] = mfma16x16x32<AB>(af[mt], bf, acc[mt][c]);
+        }
         }
     };
     // stores tile t (one branch on C's type per tile)
@@ -1046,13 +1065,15 @@ hipError_t launch_bcsr64_lds(int ab, const TileParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-size_t sweep_lds_bytes(int max_blocks)
+size_t sweep_lds_bytes(int max_blocks, int ab)
 {
-    return (size_t)max_blocks * 64 * (64 * 2 + 16);
+    return (size_t)max_blocks * 64 * (64 * (ab == SPMM_FP8_E4M3 ? 1 : 2) + 16);
 }
 
 static const void *sweep_fn(int ab, bool cm)
 {
+    if (ab == SPMM_FP8_E4M3)
+        return reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP8_E4M3, 4, false>);
     if (cm)
         return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4, true>)
                                : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4, true>);
@@ -1065,14 +1086,14 @@ hipError_t launch_bcsr64_sweep(int ab, int max_blocks, const TileParams &p, hipS
     TileParams arg = p;
     void *args[] = {&arg};
     return hipLaunchKernel(sweep_fn(ab, p.col_major != 0), dim3((unsigned)(p.n_items * p.n_ranges)),
-                           dim3(256), args, sweep_lds_bytes(max_blocks), stream);
+                           dim3(256), args, sweep_lds_bytes(max_blocks, ab), stream);
 }
 
 int sweep_blocks_per_cu(int ab, int max_blocks, bool col_major)
 {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sweep_fn(ab, col_major), 256,
-                                                     sweep_lds_bytes(max_blocks)) != hipSuccess)
+                                                     sweep_lds_bytes(max_blocks, ab)) != hipSuccess)
         return 0;
     return n;
 }
