@@ -155,6 +155,7 @@ def sweep_candidates(p):
     if p.fmt == "bcsr" and p.b_row == 64 and p.b_col == 64:
         cands += [{"kernel": 1, "waves_n": wn, "order": o} for wn in (2, 4) for o in (0, 1)]
         cands += [{"kernel": 2, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16)]
+        cands += [{"kernel": 2, "cols_per_lane": 4, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16)]
     for V in (2, 4, 8):
         if V == 8 and p.b_row >= 32:
             continue

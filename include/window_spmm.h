@@ -195,7 +195,9 @@ typedef struct {
                                 2 BCSR 64x64 A-stationary sweep (b_row = b_col = 64,
                                   N >= 4096, at most 8 blocks in every block row) */
     int32_t cols_per_lane;   /* 0 auto; kernel 0: 2, 4 or 8 adjacent C columns per lane
-                                (8 only with b_row = 16) */
+                                (8 only with b_row = 16); kernel 2: 8 (512-column tiles,
+                                the default) or 4 (256-column tiles; FP16/BF16 only, and
+                                the only choice with col_major) */
     int32_t waves_n;         /* 0 auto; kernel 0: 1, 2 or 4 waves across the tile's
                                 columns; kernel 1: 2 or 4 */
     int32_t waves_k;         /* 0 auto; kernel 0: 1, 2 or 4 waves splitting the packed

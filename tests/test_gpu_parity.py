@@ -305,6 +305,38 @@ def test_bcsr64_sweep_kernel(ws, case):
     check(p, C.float().cpu().numpy().astype(np.float64))
 
 
+SWEEP256_CASES = [
+    # m, k, N, block density, ab, c, ranges per XCD, kind
+    (1280, 640, 4104, 0.25, "bf16", "fp32", 2, "normal"),
+    (700, 600, 8192, 0.3, "fp16", "fp16", 1, "normal"),
+    (576, 520, 5000, 0.4, "fp16", "fp32", 4, "int"),
+    (640, 512, 4096, 0.95, "bf16", "bf16", 1, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP256_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bcsr64_sweep_kernel_256_columns(ws, case):
+    """The sweep kernel with 4 columns per lane (256-column tiles): ragged m, k
+    and N, empty and full block rows, every output type; exact on integer data."""
+    m, k, N, dens, ab, ct, H, kind = case
+    p = synth.block_problem(m, k, N, 64, 64, dens, seed=m + N + 7 * H, ab_dtype=ab, c_dtype=ct,
+                            kind=kind)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype,
+                        options={"kernel": 2, "cols_per_lane": 4, "ranges_per_xcd": H})
+    info = A.plan.info()
+    assert info["kernel"] == 2 and info["cols_per_lane"] == 4 and info["tile_cols"] == 256
+    B = A.device_b(p.B, padded=True)
+    C = A.new_c(padded=True)
+    C.fill_(float("nan"))
+    A.run(B, C)
+    torch.cuda.synchronize()
+    got = C.float().cpu().numpy().astype(np.float64)
+    ref = check(p, got)
+    if kind == "int":
+        assert np.array_equal(got, ref)
+
+
 # --------------------------------------------------------------------------
 # the five workloads
 # --------------------------------------------------------------------------
@@ -530,7 +562,7 @@ def test_fp8_rejected_where_unsupported(ws):
         return ws.DeviceSparse(fmt or p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row,
                                p.b_col, p.ab_dtype, p.c_dtype, options=options)
     p = synth.block_problem(256, 256, 4096, 64, 64, 0.3, seed=5, ab_dtype="fp8")
-    for options in ({"kernel": 1}, {"kernel": 0}, {"col_major": 1}):
+    for options in ({"kernel": 1}, {"kernel": 0}, {"col_major": 1}, {"cols_per_lane": 4}):
         with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):
             plan(p, options)
     q = synth.block_problem(256, 256, 4096, 32, 32, 0.3, seed=5, ab_dtype="fp8")

@@ -656,9 +656,12 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
     // it needs every block row to fit twice per CU.
     const int64_t tiles512 = ceil_div(N, 512);
     const bool lds_ok = b64 && N >= 256;
+    // kernel 2 runs 8 columns per lane (512-column tiles), or 4 with col_major
+    // or when the options ask for them (256-column tiles, 16-bit inputs)
+    const int sweep_v = opt.col_major || opt.cols_per_lane == 4 ? 4 : 8;
     const bool sweep_fits = b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 8 &&
                             sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks),
-                                                opt.col_major != 0) >= 2;
+                                                opt.col_major != 0, sweep_v) >= 2;
     const bool sweep_auto = sweep_fits && tiles512 >= 16;
     if (ab_dtype == SPMM_FP8_E4M3 &&
         (!sweep_fits || opt.col_major || (opt.kernel != -1 && opt.kernel != 2))) {
@@ -684,12 +687,20 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
     }
     if (pl->kernel == 2) {
         // column-major: 4 columns per lane (a whole block of B^T per ring stage)
-        const int cm_v = opt.col_major ? 4 : 8;
+        if (opt.cols_per_lane != 0 && opt.cols_per_lane != sweep_v) {
+            free_plan(pl);
+            return fail(SPMM_ERR_UNSUPPORTED, "kernel 2 runs 8 or 4 columns per lane (4 with "
+                                              "col_major, 8 with FP8_E4M3)");
+        }
+        if (ab_dtype == SPMM_FP8_E4M3 && sweep_v != 8) {
+            free_plan(pl);
+            return fail(SPMM_ERR_UNSUPPORTED, "kernel 2 runs FP8_E4M3 with 8 columns per lane");
+        }
         pl->n_items = nbr;
-        pl->V = cm_v;
+        pl->V = sweep_v;
         pl->waves_n = 4;
         pl->waves_k = 1;
-        pl->tile_cols = 64 * cm_v;
+        pl->tile_cols = 64 * sweep_v;
         pl->n_col_tiles = ceil_div(N, pl->tile_cols);
         pl->workspace = 0;
         pl->order = 0;

@@ -70,11 +70,12 @@ hipError_t launch_bcsr64_lds(int ab_dtype, const TileParams &p, hipStream_t stre
 // Most blocks in a block row that the sweep kernel holds in LDS.
 constexpr int kSweepMaxBlocks = 8;
 // BCSR with 64x64 blocks, A-stationary: n_items block rows x n_ranges column
-// ranges of range_tiles tiles of 512 columns (256 with col_major), 4 waves,
-// every block of a block row in LDS (max_blocks <= kSweepMaxBlocks).
+// ranges of range_tiles tiles of p.tile_cols = 64 * (columns per lane) columns
+// (512 or 256; 256 with col_major), 4 waves, every block of a block row in LDS
+// (max_blocks <= kSweepMaxBlocks).
 hipError_t launch_bcsr64_sweep(int ab_dtype, int max_blocks, const TileParams &p, hipStream_t stream);
 size_t sweep_lds_bytes(int max_blocks, int ab_dtype);
 // Work-groups of the sweep kernel resident per CU (0 if the query fails).
-int sweep_blocks_per_cu(int ab_dtype, int max_blocks, bool col_major);
+int sweep_blocks_per_cu(int ab_dtype, int max_blocks, bool col_major, int cols_per_lane);
 
 }  // namespace wspmm

@@ -85,13 +85,16 @@ __device__ __forceinline__ void buf_store_row_dt(__amdgpu_buffer_rsrc_t r, uint3
                 u32x4_t{__builtin_bit_cast(uint32_t, v[c]), __builtin_bit_cast(uint32_t, v[c + 1]),
                         __builtin_bit_cast(uint32_t, v[c + 2]), __builtin_bit_cast(uint32_t, v[c + 3])},
                 r, (int)(off == kOOB ? kOOB : off + 4 * c), 0, kNT);
-    } else {
-        static_assert(V == 8, "16-bit rows of 8 values: one 16-byte store");
+    } else if constexpr (V == 8) {
         u32x4_t w;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             w[c] = pack2(DT, v[2 * c], v[2 * c + 1]);
         __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, kNT);
+    } else {
+        static_assert(V == 4, "16-bit rows of 4 or 8 values: one store");
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack2(DT, v[0], v[1]), pack2(DT, v[2], v[3])}, r,
+                                              (int)off, 0, kNT);
     }
 }
 
@@ -744,16 +747,19 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
 // range, the block rows in order, so the work-groups resident on one XCD sweep
 // the same column tiles at about the same time and share each tile's B rows in
 // that XCD's L2, and A is read once per (block row, range).  CM: column-major B
-// and C, as in bcsr64_lds_kernel.
-template <int AB, int NW, bool CM>
+// and C, as in bcsr64_lds_kernel.  VR: row-major columns per lane (8, or 4 for
+// 256-column tiles, whose B column slices take half the L2).
+template <int AB, int NW, bool CM, int VR>
 __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
 {
     // CM: 4 columns per lane, so that a whole block of B^T (both halves) fits
     // one ring stage.  F8: one-byte codes (8 columns per lane = 2 dwords per row)
     constexpr bool F8 = AB == SPMM_FP8_E4M3;
-    static_assert(!(F8 && CM), "fp8 runs with row-major B and C");
+    static_assert(!(F8 && CM) && !(F8 && VR != 8), "fp8 runs with row-major B and C, 8 columns per lane");
+    static_assert(VR == 8 || (VR == 4 && !CM), "4 or 8 row-major columns per lane");
     constexpr int ESZ = F8 ? 1 : 2;                // bytes per A / B element
-    constexpr int R = 64, BC = 64, MT = 4, V = CM ? 4 : 8, DW = F8 ? 2 : 4;
+    constexpr int R = 64, BC = 64, MT = 4, V = CM ? 4 : VR;
+    constexpr int DW = CM ? 4 : V * ESZ / 4;       // dwords of one B row segment per lane
     constexpr int NT = NW * 64;
     constexpr int STRIDE = BC * ESZ + 16;          // padded LDS row: conflict-free reads
     constexpr int ABUF = R * STRIDE;               // bytes of one block in LDS
@@ -1070,29 +1076,33 @@ size_t sweep_lds_bytes(int max_blocks, int ab)
     return (size_t)max_blocks * 64 * (64 * (ab == SPMM_FP8_E4M3 ? 1 : 2) + 16);
 }
 
-static const void *sweep_fn(int ab, bool cm)
+static const void *sweep_fn(int ab, bool cm, int v)
 {
     if (ab == SPMM_FP8_E4M3)
-        return reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP8_E4M3, 4, false>);
+        return reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP8_E4M3, 4, false, 8>);
     if (cm)
-        return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4, true>)
-                               : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4, true>);
-    return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4, false>)
-                           : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4, false>);
+        return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4, true, 8>)
+                               : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4, true, 8>);
+    if (v == 4)
+        return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4, false, 4>)
+                               : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4, false, 4>);
+    return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4, false, 8>)
+                           : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4, false, 8>);
 }
 
 hipError_t launch_bcsr64_sweep(int ab, int max_blocks, const TileParams &p, hipStream_t stream)
 {
     TileParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel(sweep_fn(ab, p.col_major != 0), dim3((unsigned)(p.n_items * p.n_ranges)),
-                           dim3(256), args, sweep_lds_bytes(max_blocks, ab), stream);
+    return hipLaunchKernel(sweep_fn(ab, p.col_major != 0, p.tile_cols / 64),
+                           dim3((unsigned)(p.n_items * p.n_ranges)), dim3(256), args,
+                           sweep_lds_bytes(max_blocks, ab), stream);
 }
 
-int sweep_blocks_per_cu(int ab, int max_blocks, bool col_major)
+int sweep_blocks_per_cu(int ab, int max_blocks, bool col_major, int v)
 {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sweep_fn(ab, col_major), 256,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sweep_fn(ab, col_major, v), 256,
                                                      sweep_lds_bytes(max_blocks, ab)) != hipSuccess)
         return 0;
     return n;
