@@ -206,6 +206,46 @@ def test_wcsr_split_invariance_and_determinism(ws):
     check(q, outs[0])
 
 
+@pytest.mark.parametrize("ct", ["fp32", "bf16"])
+def test_split_merge_across_column_tiles_and_plans(ws, ct):
+    """Split row tiles: many split windows, four column tiles (the last one
+    ragged), two plans launched alternately and, for each plan, two different B
+    matrices in turn (a merge that read partial tiles of an earlier launch
+    would show): every launch must give the oracle's result (bit-exact on
+    integer data with fp32 C) and the same bits for the same input."""
+    kind = "int" if ct == "fp32" else "normal"
+    probs = [synth.random_problem(700, 6000, 392, 0.04, seed=31, ab_dtype="fp16", c_dtype=ct,
+                                  kind=kind, fmt="wcsr", b_row=16, b_col=8, empty_row_frac=0.1),
+             synth.random_problem(260, 2500, 136, 0.08, seed=32, ab_dtype="fp16", c_dtype=ct,
+                                  kind=kind, fmt="wcsr", b_row=16, b_col=8)]
+    cases = []
+    for prob in probs:
+        A = ws.DeviceSparse(prob.fmt, prob.m, prob.k, prob.N, prob.row_ptr, prob.col_idx, prob.vals,
+                            prob.b_row, prob.b_col, prob.ab_dtype, prob.c_dtype, split_cols=64)
+        assert A.plan.info()["n_merges"] > 10, A.plan.info()
+        for B in (prob.B, np.ascontiguousarray(prob.B[::-1])):
+            ref, bound = oracle.spmm(prob.m, prob.k, prob.N, prob.coo_rows(), prob.col_idx,
+                                     prob.vals, B, prob.ab_dtype)
+            cases.append((prob, A, torch.from_numpy(B.view(np.int16)).cuda(), ref, bound))
+    _say("split merge cases:", [(c[0].name, c[0].N) for c in cases])
+    first = {}
+    for rep in range(3):
+        for i, (prob, A, dB, ref, bound) in enumerate(cases):
+            C = A.new_c()
+            C.fill_(float("nan"))
+            A.run(dB, C)
+            torch.cuda.synchronize()
+            got = C.float().cpu().numpy().astype(np.float64)
+            if kind == "int":
+                assert np.array_equal(got, ref), (rep, i)
+            else:
+                ok, worst, at = oracle.within_tolerance(got, ref, bound, TOL, out_dtype=prob.c_dtype)
+                assert ok, (rep, i, at, worst)
+            if i in first:
+                assert np.array_equal(got, first[i]), (rep, i)
+            first.setdefault(i, got)
+
+
 @pytest.mark.parametrize("source", ["lists", "spread"])
 @pytest.mark.parametrize("fmt", ["wcsr", "bcsr"])
 def test_work_sources_repeated_launches(ws, fmt, source):

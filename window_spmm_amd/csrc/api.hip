@@ -325,22 +325,29 @@ namespace wspmm {
 namespace {
 
 // Sub-task size when the caller leaves it to the plan.  `slots` work-groups of
-// the tile kernel are resident at once.  If no row tile is longer than the
-// total work divided by the slots, T covers the longest one (nothing is cut, no
-// merge pass); otherwise T is that quotient, so that no task outlasts the
-// average work of a slot.  T is a multiple of `align`, at least 512 and at
-// most kMaxSplit.
+// the tile kernel are resident at once.  If no row tile is longer than
+// `slack10` tenths of the total work divided by the slots, T covers the longest
+// one (nothing is cut, no merge pass); otherwise T is that quotient, so that no
+// task outlasts the average work of a slot.  T is a multiple of `align`, at
+// least 512 and at most kMaxSplit.
 constexpr int64_t kMaxSplit = 8192;
+// slack10 of persistent plans.  Their work-groups share CUs in pairs and the
+// assignment is balanced with the longest tasks first, so a task up to half as
+// long again as a slot's share still ends with its CU; a merge pass costs a
+// launch and a round trip (measured on the 16384^2 WCSR workload: its longest
+// window, 1.32 shares, cut into tasks and merged ran 51.2-51.5 us, uncut
+// 49.0-49.4 us).
+constexpr int64_t kPersistentSlack10 = 15;
 
 int64_t auto_split(int64_t n_rows, const std::function<int64_t(int64_t)> &start, int64_t align,
-                   int64_t slots)
+                   int64_t slots, int64_t slack10)
 {
     const int64_t total = start(n_rows) - start(0);
     int64_t longest = 0;
     for (int64_t w = 0; w < n_rows; ++w)
         longest = std::max(longest, start(w + 1) - start(w));
     const int64_t share = ceil_div(total, std::max<int64_t>(1, slots));
-    int64_t T = longest <= share ? longest : share;
+    int64_t T = longest * 10 <= share * slack10 ? longest : share;
     T = std::max<int64_t>(512, ceil_div(T, align) * align);
     return std::min<int64_t>(T, kMaxSplit);
 }
@@ -547,7 +554,8 @@ spmm_status_t plan_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
         const int64_t buf_max = ((lds_per_cu / per_cu_regs - (int64_t)lds0) / 4) / (spread ? 1 : 2);
         int64_t cap = ((buf_max - 256) / 256 * 256) << shift;
         cap = std::max<int64_t>(512, cap / align * align);
-        split_cols = auto_split(n_rows, start, align, slots / std::max<int64_t>(1, pl->n_col_tiles));
+        split_cols = auto_split(n_rows, start, align, slots / std::max<int64_t>(1, pl->n_col_tiles),
+                                spread ? 10 : kPersistentSlack10);
         split_cols = std::min(split_cols, std::max<int64_t>(align, cap));
     }
     // Spread work-groups run in row order when B is much larger than an L2 and
