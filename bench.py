@@ -304,6 +304,90 @@ def run_ffn_table():
         raise SystemExit("a sparse result disagrees with torch.mm of its densified weight")
 
 
+def time_runs(A, B, C, steps, warmup):
+    """Mean HIP-event time (s) of one SpMM on the launch stream, after warm-up."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        A.run(B, C, stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for s, e in ev:
+        s.record(stream)
+        A.run(B, C, stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([s.elapsed_time(e) for s, e in ev])) / 1e3
+
+
+def roofline_time(p, alg):
+    """t_roof = max(stored flops / MFMA peak, algorithmic bytes / HBM peak) in s."""
+    peak = PEAK_MFMA_TFLOPS_FP8 if p.ab_dtype == "fp8" else PEAK_MFMA_TFLOPS
+    return max(alg["flops_stored"] / (peak * 1e12), alg["bytes_alg"] / (PEAK_HBM_GBS * 1e9))
+
+
+def run_population(args):
+    """Config 3 as the workload defines it: every matrix of the seeded WCSR
+    population (32 matrices, m = k from 8K to 512K, banded and uniform, Zipf
+    row lengths) at N = 32, 128 and 256, timed like the paper's runs (warm-up,
+    then HIP events around each launch), with geometric means of the effective
+    TFLOP/s (2*nnz*N/t) and of the roofline fractions over the 96 runs and per
+    N.  Stands in for the paper's SuiteSparse collection, which is not used."""
+    import dataclasses
+    import torch
+    import synth
+    import window_spmm_amd as ws
+    dev = torch.device("cuda:0")
+    specs = synth.config3_specs()
+    members = range(len(specs))
+    if args.members:
+        lo, _, hi = args.members.partition("-")
+        members = range(int(lo), int(hi or lo) + 1)
+    runs = []
+    for j in members:
+        print("bench: population member %d (m=%d, mean row %.1f, %s)" % (
+            j, specs[j][0], specs[j][1], "banded" if specs[j][2] else "uniform"),
+            file=sys.stderr, flush=True)
+        p256 = synth.config3_matrix(j, 256)
+        for N in (32, 128, 256):
+            p = dataclasses.replace(p256, N=N, B=np.ascontiguousarray(p256.B[:, :N]),
+                                    name="cfg3_m%d_N%d" % (j, N))
+            A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row,
+                                p.b_col, p.ab_dtype, p.c_dtype, device=dev)
+            B = A.device_b(p.B, dev, padded=True)
+            C = A.new_c(dev, padded=True)
+            t = time_runs(A, B, C, args.steps, args.warmup)
+            alg = algorithmic(p, A)
+            info = A.plan.info()
+            r = {"member": j, "m": p.m, "nnz": p.nnz, "banded": bool(p.meta["banded"]), "N": N,
+                 "us": t * 1e6, "tflops_true": alg["flops_true"] / t / 1e12,
+                 "frac": roofline_time(p, alg) / t, "t_roof_us": roofline_time(p, alg) * 1e6,
+                 "fill": p.nnz / A.stored_entries, "n_tasks": info["n_tasks"],
+                 "n_merges": info["n_merges"]}
+            runs.append(r)
+            print("bench:   N=%3d %9.1f us  %7.2f TFLOP/s  frac %.3f  (t_roof %.1f us, fill %.3f, "
+                  "%d tasks, %d merges)" % (N, r["us"], r["tflops_true"], r["frac"], r["t_roof_us"],
+                                            r["fill"], r["n_tasks"], r["n_merges"]),
+                  file=sys.stderr, flush=True)
+            del A, B, C
+        del p256
+        torch.cuda.empty_cache()
+
+    def gm(xs):
+        return float(np.exp(np.mean(np.log(xs)))) if xs else None
+
+    out = {"population": "cfg3: 32 seeded WCSR matrices x N in {32, 128, 256}, window 16, "
+                          "b_col 8, fp16 in, fp32 out",
+           "runs": len(runs), "steps": args.steps, "warmup": args.warmup,
+           "geomean_tflops_true": gm([r["tflops_true"] for r in runs]),
+           "geomean_frac": gm([r["frac"] for r in runs]),
+           "per_N": {N: {"geomean_tflops_true": gm([r["tflops_true"] for r in runs if r["N"] == N]),
+                         "geomean_frac": gm([r["frac"] for r in runs if r["N"] == N])}
+                     for N in (32, 128, 256)},
+           "detail": runs}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +396,9 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--which", default="gate", help="config 4 weight: gate, up or down")
     ap.add_argument("--member", type=int, default=0, help="config 3 matrix index")
+    ap.add_argument("--population", action="store_true",
+                    help="config 3: every matrix of the population at N = 32, 128, 256, geo-means")
+    ap.add_argument("--members", default="", help="with --population: a range of members, e.g. 0-7")
     ap.add_argument("--n3", type=int, default=128, help="config 3 N")
     ap.add_argument("--n4", type=int, default=65536, help="config 4 N (tokens)")
     ap.add_argument("--width", type=int, default=1, help="config 5 line width in blocks")
@@ -341,6 +428,9 @@ def main():
         return
     if args.ffn_table:
         run_ffn_table()
+        return
+    if args.population:
+        run_population(args)
         return
 
     if args.gpus != 1:

@@ -176,7 +176,11 @@ __device__ __forceinline__ void store_tile_cm(int dt, const f32x4_t (&acc)[MT][V
 // Stores the V results of one row of one lane (V adjacent columns) at byte
 // offset `off` of r; kOOB drops the store.  For a given V both the fp32 and the
 // 16-bit forms issue the same number of store instructions, so wait counts on
-// loads issued before the stores stay exact whatever the destination.
+// loads issued before the stores stay exact whatever the destination.  The
+// stores are non-temporal: C (and a partial tile) is written once, and kept out
+// of the way it displaces less of the B rows other work-groups still gather
+// (measured: 42.6-44.0 -> 41.3-41.5 us on the 65536^2 BCSR P*V workload, 4 %
+// on small WCSR matrices, no change on the 16384^2 WCSR one).
 template <int V>
 __device__ __forceinline__ void buf_store_row(__amdgpu_buffer_rsrc_t r, uint32_t off, int dt,
                                               const float *v)
@@ -188,11 +192,11 @@ __device__ __forceinline__ void buf_store_row(__amdgpu_buffer_rsrc_t r, uint32_t
                 __builtin_amdgcn_raw_buffer_store_b128(
                     u32x4_t{__builtin_bit_cast(uint32_t, v[c]), __builtin_bit_cast(uint32_t, v[c + 1]),
                             __builtin_bit_cast(uint32_t, v[c + 2]), __builtin_bit_cast(uint32_t, v[c + 3])},
-                    r, (int)(off == kOOB ? kOOB : off + 4 * c), 0, 0);
+                    r, (int)(off == kOOB ? kOOB : off + 4 * c), 0, kNT);
         } else {
             __builtin_amdgcn_raw_buffer_store_b64(
                 u32x2_t{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1])}, r,
-                (int)off, 0, 0);
+                (int)off, 0, kNT);
         }
     } else {
         uint32_t w[V / 2];
@@ -200,12 +204,12 @@ __device__ __forceinline__ void buf_store_row(__amdgpu_buffer_rsrc_t r, uint32_t
         for (int c = 0; c < V; c += 2)
             w[c / 2] = pack2(dt, v[c], v[c + 1]);
         if constexpr (V == 8) {
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[0], w[1], w[2], w[3]}, r, (int)off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(0u, r, (int)kOOB, 0, 0);  // count filler
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[0], w[1], w[2], w[3]}, r, (int)off, 0, kNT);
+            __builtin_amdgcn_raw_buffer_store_b32(0u, r, (int)kOOB, 0, kNT);  // count filler
         } else if constexpr (V == 4) {
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w[0], w[1]}, r, (int)off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w[0], w[1]}, r, (int)off, 0, kNT);
         } else {
-            __builtin_amdgcn_raw_buffer_store_b32(w[0], r, (int)off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(w[0], r, (int)off, 0, kNT);
         }
     }
 }
