@@ -489,7 +489,7 @@ spmm_status_t make_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
     } catch (const std::bad_alloc &) {
         return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
     }
-    if (pl->n_merges > 0 && ceil_div((int64_t)pl->b_row * (pl->N / 8), 256) > 65535)
+    if (pl->n_merges > 0 && ceil_div((int64_t)pl->b_row * (pl->N / 8), 32) > 65535)
         return fail(SPMM_ERR_UNSUPPORTED, "N too large for the merge grid");
     if (pl->n_merges > 0 && (uint64_t)pl->b_row * (uint64_t)pl->N * 4u >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "b_row * N * 4 bytes of a partial tile must be below 4 GiB");

@@ -975,20 +975,24 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
     }
 }
 
-// One work-group per (merge record, chunk of 256*8 tile elements): adds the
-// partial tiles of a split window in slot order and writes C once.
+// Merge pass: one work-group per (merge record, 32 chunks of 8 tile columns).
+// Eight adjacent lanes share a chunk: lane t adds slots t, t+8, t+16, ... in
+// that order (its loads, two slots at a time, are independent of the other
+// lanes'), then the eight running sums are combined pairwise across the lanes
+// ((s0+s1)+(s2+s3))+((s4+s5)+(s6+s7)) and lane 0 writes C once.  The order
+// depends only on the number of slots, so results are bitwise reproducible for
+// a given plan, and a merge with up to 16 slots costs one memory round trip
+// instead of one per four slots.
 __global__ __launch_bounds__(256) void wcsr_merge_kernel(MergeParams p)
 {
     const int3 mr = p.merges[blockIdx.x];
-    const int64_t chunk = (int64_t)blockIdx.y * 256 + threadIdx.x;  // 8 columns each
+    const int t = threadIdx.x & 7;
+    const int64_t chunk = (int64_t)blockIdx.y * 32 + (threadIdx.x >> 3);  // 8 columns each
     const int64_t per_row = p.N / 8;
-    if (chunk >= (int64_t)p.R * per_row)
-        return;
     const int64_t r = chunk / per_row;
     const int64_t col = (chunk - r * per_row) * 8;
     const int64_t row = (int64_t)mr.x * p.R + r;
-    if (row >= p.m)
-        return;
+    const bool valid = (chunk < (int64_t)p.R * per_row) & (row < p.m);
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const float *src = p.partial + ((int64_t)mr.y * p.R + r) * p.N + col;
     const int64_t slot_stride = (int64_t)p.R * p.N;
@@ -996,23 +1000,29 @@ __global__ __launch_bounds__(256) void wcsr_merge_kernel(MergeParams p)
         s[0] += a[0]; s[1] += a[1]; s[2] += a[2]; s[3] += a[3];
         s[4] += b[0]; s[5] += b[1]; s[6] += b[2]; s[7] += b[3];
     };
-    // four slots' loads in flight at a time; the adds stay in slot order
-    int t = 0;
-    for (; t + 4 <= mr.z; t += 4) {
-        f32x4_t a[4], b[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a[u] = *reinterpret_cast<const f32x4_t *>(src + (t + u) * slot_stride);
-            b[u] = *reinterpret_cast<const f32x4_t *>(src + (t + u) * slot_stride + 4);
+    if (valid) {
+        int u = t;
+        for (; u + 8 < mr.z; u += 16) {
+            const float *q0 = src + u * slot_stride, *q1 = src + (u + 8) * slot_stride;
+            const f32x4_t a0 = *reinterpret_cast<const f32x4_t *>(q0);
+            const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(q0 + 4);
+            const f32x4_t a1 = *reinterpret_cast<const f32x4_t *>(q1);
+            const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(q1 + 4);
+            add(a0, b0);
+            add(a1, b1);
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            add(a[u], b[u]);
+        if (u < mr.z)
+            add(*reinterpret_cast<const f32x4_t *>(src + u * slot_stride),
+                *reinterpret_cast<const f32x4_t *>(src + u * slot_stride + 4));
     }
-    for (; t < mr.z; ++t)
-        add(*reinterpret_cast<const f32x4_t *>(src + t * slot_stride),
-            *reinterpret_cast<const f32x4_t *>(src + t * slot_stride + 4));
-    store_row<8>(p.C, row * p.ldc + col, p.c_dtype, s);
+    // every lane of the wave takes part in the exchanges
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            s[e] += __shfl_xor(s[e], off, 8);
+    if (valid && t == 0)
+        store_row<8>(p.C, row * p.ldc + col, p.c_dtype, s);
 }
 
 // The tile kernel instantiation for (format, tile rows, columns per lane, A/B type).
@@ -1138,7 +1148,7 @@ int tiles_blocks_per_cu(int fmt, int R, int V, int ab, int threads, size_t lds)
 hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stream)
 {
     const int64_t chunks = (int64_t)p.R * (p.N / 8);
-    dim3 grid((unsigned)n_merges, (unsigned)((chunks + 255) / 256));
+    dim3 grid((unsigned)n_merges, (unsigned)((chunks + 31) / 32));
     hipLaunchKernelGGL(wcsr_merge_kernel, grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
