@@ -305,19 +305,23 @@ def run_ffn_table():
 
 
 def time_runs(A, B, C, steps, warmup):
-    """Mean HIP-event time (s) of one SpMM on the launch stream, after warm-up."""
+    """Time (s) of one SpMM on the launch stream: after warm-up, one HIP event
+    pair around `steps` back-to-back launches, divided by `steps`.  Returns
+    (per-launch event time, per-launch wall time)."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         A.run(B, C, stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for s, e in ev:
-        s.record(stream)
-        A.run(B, C, stream)
-        e.record(stream)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    return float(np.mean([s.elapsed_time(e) for s, e in ev])) / 1e3
+    t0 = time.perf_counter()
+    s.record(stream)
+    for _ in range(steps):
+        A.run(B, C, stream)
+    e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return s.elapsed_time(e) / 1e3 / steps, wall / steps
 
 
 def roofline_time(p, alg):
@@ -356,7 +360,7 @@ def run_population(args):
                                 p.b_col, p.ab_dtype, p.c_dtype, device=dev)
             B = A.device_b(p.B, dev, padded=True)
             C = A.new_c(dev, padded=True)
-            t = time_runs(A, B, C, args.steps, args.warmup)
+            t, _ = time_runs(A, B, C, args.steps, args.warmup)
             alg = algorithmic(p, A)
             info = A.plan.info()
             r = {"member": j, "m": p.m, "nnz": p.nnz, "banded": bool(p.meta["banded"]), "N": N,
@@ -473,23 +477,11 @@ def main():
         return
 
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        A.run(B, C, stream)
-    torch.cuda.synchronize()
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s, e in ev:
-        s.record(stream)
-        A.run(B, C, stream)
-        e.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    ev_ms = np.array([s.elapsed_time(e) for s, e in ev])
-    t_kernel = float(ev_ms.mean()) / 1e3
+    # one HIP event pair on the launch stream around the timed region (the
+    # steps are launched back to back); per-launch time = region / steps
+    t_kernel, t_wall = time_runs(A, B, C, args.steps, args.warmup)
+    ms_step = t_wall * 1e3
 
     cold = None
     if args.cold:
