@@ -34,7 +34,7 @@
 // the reduction (waves_k, interleaved 32-wide k' steps); the waves_k partial
 // sums are added in a fixed order through LDS, so results are deterministic.
 // WCSR tasks that cover only part of a long window write fp32 partial tiles to
-// a workspace slot; wcsr_merge adds the slots of a window in slot order and
+// a workspace slot; wcsr_merge adds the slots of a window in a fixed order and
 // rounds once (this replaces the paper's atomicAdd merge, Section III-C).
 //
 // Work-group order: dispatch hands consecutive work-group ids to the 8 XCDs in
