@@ -143,7 +143,10 @@ spmm_status_t check_common(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, i
 }
 
 // Tile shape: V columns per lane (wave width 16V), waves along N, waves along k'.
-spmm_status_t choose_config(spmm_plan_s *pl, double mean_kprime, int n_cu)
+// wide: 16-row tiles take two waves along N when N spans two or more wave
+// widths, so that one work-group covers 256 columns and each window's indices
+// and values are read once (used for row-ordered plans with few items).
+spmm_status_t choose_config(spmm_plan_s *pl, double mean_kprime, int n_cu, bool wide)
 {
     const spmm_plan_options_t &o = pl->opt;
     int V = pl->N >= 128 ? 8 : (pl->N >= 64 ? 4 : 2);
@@ -157,7 +160,9 @@ spmm_status_t choose_config(spmm_plan_s *pl, double mean_kprime, int n_cu)
     }
     const int64_t wave_cols = 16 * V;
     const int64_t col_waves = ceil_div(pl->N, wave_cols);
-    int wn = o.waves_n > 0 ? o.waves_n : (pl->b_row == 64 && col_waves >= 2) ? 2 : 1;
+    int wn = o.waves_n > 0 ? o.waves_n
+             : (pl->b_row == 64 && col_waves >= 2) ? 2
+             : (wide && pl->b_row == 16 && col_waves >= 2) ? 2 : 1;
     const int64_t col_tiles = std::max<int64_t>(1, ceil_div(pl->N, wave_cols * wn));
     // add reduction waves while the grid is small and the items are long
     const int64_t waves = std::max<int64_t>(1, pl->n_items * col_tiles * wn);
@@ -537,17 +542,40 @@ spmm_status_t plan_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
 {
     const int64_t total = start(n_rows) - start(0);
     pl->n_items = n_rows;
-    spmm_status_t s = choose_config(pl, n_rows > 0 ? (double)total / (double)n_rows : 0.0, n_cu);
-    if (s != SPMM_OK)
-        return s;
-    const int threads = 64 * pl->waves_n * pl->waves_k;
-    // work-groups per CU that registers allow
-    const size_t lds0 = tile_lds_bytes(0, pl->b_row, pl->V, pl->waves_n, pl->waves_k, true);
-    const int per_cu_regs = std::max(1, tiles_blocks_per_cu(pl->fmt, pl->b_row, pl->V, pl->ab,
-                                                            threads, lds0));
-    const int64_t slots = (int64_t)n_cu * per_cu_regs;
-    const bool spread = pl->opt.distribution >= 0 ? pl->opt.distribution == 1
-                                                   : n_rows * pl->n_col_tiles >= kSpreadItems * slots;
+    // A banded pattern whose B is much larger than an L2: one work-group per
+    // item, in row order with a contiguous range of rows per XCD, so that
+    // neighbouring row tiles share B rows in that XCD's L2.  Where that is what
+    // turns the plan from lists into one work-group per item (few items), the
+    // tile also takes 256 columns.  Measured on the WCSR population's banded
+    // members at N = 256 against longest-first lists: 35232 rows 88.0 -> 52.5
+    // us, 54803 rows 212.5 -> 100.3 us; at 343589 to 400511 rows, which have
+    // items enough for one work-group each anyway, 128-column tiles stay
+    // 9-19 % faster.
+    const bool banded_large =
+        pl->k * pl->N * 2 > 2 * std::max<int64_t>(1, l2_bytes) &&
+        banded_pattern(n_rows, h_ptr, pl->col_idx, pl->fmt == 0 ? pl->b_col : 1, pl->k,
+                       pl->fmt == 0 ? 1 : pl->b_col);
+    const bool want_local = pl->opt.distribution != 0 && pl->opt.row_order != 0 && banded_large;
+    const double mean_kprime = n_rows > 0 ? (double)total / (double)n_rows : 0.0;
+    int64_t slots = 0;
+    int per_cu_regs = 1;
+    size_t lds0 = 0;
+    bool many = false;
+    for (int pass = 0; pass < 2; ++pass) {
+        spmm_status_t s = choose_config(pl, mean_kprime, n_cu, pass == 1);
+        if (s != SPMM_OK)
+            return s;
+        const int threads = 64 * pl->waves_n * pl->waves_k;
+        // work-groups per CU that registers allow
+        lds0 = tile_lds_bytes(0, pl->b_row, pl->V, pl->waves_n, pl->waves_k, true);
+        per_cu_regs = std::max(1, tiles_blocks_per_cu(pl->fmt, pl->b_row, pl->V, pl->ab, threads, lds0));
+        slots = (int64_t)n_cu * per_cu_regs;
+        if (pass == 0)
+            many = n_rows * pl->n_col_tiles >= kSpreadItems * slots;
+        if (!want_local || many)
+            break;
+    }
+    const bool spread = pl->opt.distribution >= 0 ? pl->opt.distribution == 1 : want_local || many;
     if (split_cols == 0) {
         // the index buffers of every resident work-group must fit its share of
         // the LDS, which caps the task length
@@ -563,9 +591,7 @@ spmm_status_t plan_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
     // otherwise longest first, which balances better.
     int local = pl->opt.row_order;
     if (local < 0)
-        local = spread && pl->k * pl->N * 2 > 2 * std::max<int64_t>(1, l2_bytes) &&
-                banded_pattern(n_rows, h_ptr, pl->col_idx, pl->fmt == 0 ? pl->b_col : 1, pl->k,
-                               pl->fmt == 0 ? 1 : pl->b_col);
+        local = spread && banded_large;
     return make_tasks(pl, n_rows, start, split_cols, shift, n_cu, spread, local != 0);
 }
 
