@@ -406,6 +406,22 @@ def test_config3_members(ws, N):
         check(p, got, rows=rows)
 
 
+@pytest.mark.parametrize("N", [256, 136])
+def test_banded_large_b_row_order_wide_tiles(ws, N):
+    """A banded pattern whose B spans several L2s (population member 18: 36674
+    rows, band 1 % of n) with few windows per resident work-group: the plan runs
+    one work-group per window in row order with 256-column tiles (N = 136: one
+    ragged tile).  Full parity with the oracle."""
+    import dataclasses
+    p = synth.config3_matrix(18, 256)
+    p = dataclasses.replace(p, N=N, B=np.ascontiguousarray(p.B[:, :N]), name="cfg3_m18_N%d" % N)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    info = A.plan.info()
+    assert info["tile_cols"] == 256 and info["waves_n"] == 2, info
+    check(p, run_gpu(ws, p, A=A))
+
+
 def test_config4_gate_sampled(ws):
     p = synth.config4("gate")
     got = run_gpu(ws, p)
