@@ -304,24 +304,35 @@ def run_ffn_table():
         raise SystemExit("a sparse result disagrees with torch.mm of its densified weight")
 
 
-def time_runs(A, B, C, steps, warmup):
-    """Time (s) of one SpMM on the launch stream: after warm-up, one HIP event
-    pair around `steps` back-to-back launches, divided by `steps`.  Returns
-    (per-launch event time, per-launch wall time)."""
+def time_calls(launch, steps, warmup):
+    """Time (s) of one call of `launch(stream)` on the current stream: after
+    warm-up, one HIP event pair around `steps` back-to-back calls, divided by
+    `steps`.  Returns (per-call event time, per-call wall time)."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        A.run(B, C, stream)
+        launch(stream)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     s.record(stream)
     for _ in range(steps):
-        A.run(B, C, stream)
+        launch(stream)
     e.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return s.elapsed_time(e) / 1e3 / steps, wall / steps
+
+
+def time_runs(A, B, C, steps, warmup):
+    """time_calls for one SpMM through the plan of A."""
+    return time_calls(lambda st: A.run(B, C, st), steps, warmup)
+
+
+def launch_floor(steps=100, warmup=10):
+    """Per-launch time (s) of the library's empty kernel, timed like a run."""
+    import window_spmm_amd as ws
+    return time_calls(lambda st: ws.launch_floor(st), steps, warmup)[0]
 
 
 def roofline_time(p, alg):
@@ -347,6 +358,8 @@ def run_population(args):
     if args.members:
         lo, _, hi = args.members.partition("-")
         members = range(int(lo), int(hi or lo) + 1)
+    floor = launch_floor()
+    print("bench: launch floor %.2f us" % (floor * 1e6), file=sys.stderr, flush=True)
     runs = []
     for j in members:
         print("bench: population member %d (m=%d, mean row %.1f, %s)" % (
@@ -366,6 +379,7 @@ def run_population(args):
             r = {"member": j, "m": p.m, "nnz": p.nnz, "banded": bool(p.meta["banded"]), "N": N,
                  "us": t * 1e6, "tflops_true": alg["flops_true"] / t / 1e12,
                  "frac": roofline_time(p, alg) / t, "t_roof_us": roofline_time(p, alg) * 1e6,
+                 "frac_with_floor": min(1.0, (roofline_time(p, alg) + floor) / t),
                  "fill": p.nnz / A.stored_entries, "n_tasks": info["n_tasks"],
                  "n_merges": info["n_merges"]}
             runs.append(r)
@@ -385,6 +399,8 @@ def run_population(args):
            "runs": len(runs), "steps": args.steps, "warmup": args.warmup,
            "geomean_tflops_true": gm([r["tflops_true"] for r in runs]),
            "geomean_frac": gm([r["frac"] for r in runs]),
+           "launch_floor_us": floor * 1e6,
+           "geomean_frac_with_floor": gm([r["frac_with_floor"] for r in runs]),
            "per_N": {N: {"geomean_tflops_true": gm([r["tflops_true"] for r in runs if r["N"] == N]),
                          "geomean_frac": gm([r["frac"] for r in runs if r["N"] == N])}
                      for N in (32, 128, 256)},
@@ -544,6 +560,9 @@ def main():
         "bytes_alg": alg["bytes_alg"],
         "roofline": roof,
     }
+    floor = launch_floor()
+    out["launch_floor_us"] = floor * 1e6
+    out["roofline_fraction_with_floor"] = min(1.0, (max(t_roof_mfma, t_roof_hbm) + floor) / t_kernel)
     if cold is not None:
         out["cold_us"] = cold * 1e6
         out["roofline_fraction_cold"] = max(t_roof_mfma, t_roof_hbm) / cold

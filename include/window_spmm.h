@@ -286,6 +286,13 @@ spmm_status_t spmm_plan_info(spmm_plan_t plan, spmm_plan_info_t *info);
  * Returns N unchanged for N <= 0 or elem_bytes <= 0. */
 int64_t spmm_recommended_ld(int64_t N, int32_t elem_bytes);
 
+/* Launch floor: enqueues one empty kernel (one work-group of 64 threads) on
+ * `stream` (a hipStream_t; NULL = the null stream).  A measurement aid: timed
+ * like a run, it gives the cost of a launch that does no work, against which
+ * the runs of small problems are read.  SPMM_ERR_HIP if the launch fails
+ * (e.g. no device). */
+spmm_status_t spmm_launch_floor(void *stream);
+
 /* Frees the plan's host and device memory.  NULL is accepted.  The caller must
  * make sure no run using the plan is still executing. */
 spmm_status_t spmm_plan_destroy(spmm_plan_t plan);

@@ -81,6 +81,14 @@ def test_plan_without_gpu_reports_hip_error():
     assert _code(lambda: ws.bcsr_plan(16, 64, 64, 16, 16, ptr, 256, 256)) == ws.ERR_HIP
 
 
+def test_launch_floor_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert ws._lib.spmm_launch_floor(None) == ws.ERR_HIP
+    assert ws._lib.spmm_last_error().decode()
+
+
 def test_recommended_ld():
     # pitches that are a multiple of 4 KiB get 64 extra elements; others are kept
     assert ws.recommended_ld(65536, 2) == 65600

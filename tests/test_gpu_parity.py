@@ -632,3 +632,10 @@ def test_fp8_rejected_where_unsupported(ws):
         plan(q)
     with pytest.raises(ValueError):
         plan(p, fmt="wcsr")
+
+
+def test_launch_floor_kernel_runs(ws):
+    """The empty kernel behind the benchmark's launch floor launches and ends."""
+    for _ in range(3):
+        ws.launch_floor()
+    torch.cuda.synchronize()

@@ -38,6 +38,7 @@ EXPORTED = [
     "spmm_bcsr_run", "spmm_wcsr_run", "spmm_plan_info", "spmm_plan_destroy",
     "spmm_status_string", "spmm_last_error", "spmm_recommended_ld", "spmm_rcm_order",
     "spmm_csr_permute", "spmm_plan_options_default", "spmm_bcsr_plan_ex", "spmm_wcsr_plan_ex",
+    "spmm_launch_floor",
 ]
 
 
@@ -102,6 +103,7 @@ _sigs = {
     "spmm_wcsr_run": [_vp, _vp, _i64, _vp, _i64, _vp, _vp],
     "spmm_plan_info": [_vp, ctypes.POINTER(PlanInfo)],
     "spmm_plan_destroy": [_vp],
+    "spmm_launch_floor": [_vp],
 }
 for _name, _args in _sigs.items():
     _f = getattr(_lib, _name)
@@ -308,6 +310,11 @@ def _stream_handle(stream):
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def launch_floor(stream=None):
+    """Enqueues one empty kernel on `stream` (spmm_launch_floor)."""
+    _check(_lib.spmm_launch_floor(_stream_handle(stream)), "spmm_launch_floor")
 
 
 def _ld(t) -> int:

@@ -897,6 +897,21 @@ extern "C" spmm_status_t spmm_plan_destroy(spmm_plan_t plan)
     return ok();
 }
 
+namespace wspmm {
+namespace {
+// The empty kernel behind spmm_launch_floor.
+__global__ void launch_floor_kernel() {}
+}  // namespace
+}  // namespace wspmm
+
+extern "C" spmm_status_t spmm_launch_floor(void *stream)
+{
+    hipLaunchKernelGGL(wspmm::launch_floor_kernel, dim3(1), dim3(64), 0,
+                       reinterpret_cast<hipStream_t>(stream));
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? ok() : hip_fail(e, "empty kernel launch");
+}
+
 extern "C" int64_t spmm_recommended_ld(int64_t N, int32_t elem_bytes)
 {
     if (N <= 0 || elem_bytes <= 0)
