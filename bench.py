@@ -425,7 +425,8 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="WCSR sub-task size (0 = plan's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cold", action="store_true", help="also time with caches flushed")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timing (a 1 GiB fill before each launch)")
     ap.add_argument("--no-pad", action="store_true", help="B and C with leading dimension N")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
@@ -500,18 +501,15 @@ def main():
     ms_step = t_wall * 1e3
 
     cold = None
-    if args.cold:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
-        cms = []
-        for _ in range(min(args.steps, 30)):
-            flush.fill_(1.0)
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record(stream)
-            A.run(B, C, stream)
-            e.record(stream)
-            torch.cuda.synchronize()
-            cms.append(s.elapsed_time(e))
-        cold = float(np.mean(cms)) / 1e3
+    if not args.no_cold:
+        # caches flushed before every launch: a 1 GiB fill (more than the MALL
+        # and the L2s together) precedes each run; per-run time = the region of
+        # K (fill, run) pairs minus the region of K fills alone
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        k = min(args.steps, 30)
+        t_pair, _ = time_calls(lambda st: (flush.fill_(1.0), A.run(B, C, st)), k, 2)
+        t_fill, _ = time_calls(lambda st: flush.fill_(1.0), k, 2)
+        cold = max(t_pair - t_fill, 1e-9)
         del flush
 
     peak_mfma = PEAK_MFMA_TFLOPS_FP8 if p.ab_dtype == "fp8" else PEAK_MFMA_TFLOPS
