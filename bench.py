@@ -425,8 +425,9 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="WCSR sub-task size (0 = plan's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold-cache timing (a 1 GiB fill before each launch)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time with caches flushed (a 1 GiB fill before each launch)")
+    ap.add_argument("--no-cold", action="store_true", help="no cold-cache timing (the default)")
     ap.add_argument("--no-pad", action="store_true", help="B and C with leading dimension N")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
@@ -501,7 +502,7 @@ def main():
     ms_step = t_wall * 1e3
 
     cold = None
-    if not args.no_cold:
+    if args.cold and not args.no_cold:
         # caches flushed before every launch: a 1 GiB fill (more than the MALL
         # and the L2s together) precedes each run; per-run time = the region of
         # K (fill, run) pairs minus the region of K fills alone
