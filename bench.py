@@ -329,6 +329,30 @@ def time_runs(A, B, C, steps, warmup):
     return time_calls(lambda st: A.run(B, C, st), steps, warmup)
 
 
+def measured_peaks():
+    """What this GPU reaches on plain dense work, timed like a run, next to the
+    published peaks the roofline uses: a 1 GiB device-to-device copy (HBM read
+    plus write) and an 8192^3 bf16 GEMM through torch.mm (hipBLASLt)."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    t_copy, _ = time_calls(lambda st: b.copy_(a), 10, 3)
+    del a, b
+    m = 8192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    x = torch.randn((m, m), generator=g, device="cuda").to(torch.bfloat16)
+    y = torch.randn((m, m), generator=g, device="cuda").to(torch.bfloat16)
+    z = torch.empty_like(x)
+    t_mm, _ = time_calls(lambda st: torch.mm(x, y, out=z), 10, 3)
+    del x, y, z
+    return {"hbm_copy_GBs": 2.0 * n * 4 / t_copy / 1e9,
+            "dense_bf16_gemm_TFLOPs": 2.0 * m ** 3 / t_mm / 1e12,
+            "how": "1 GiB fp32 device copy (read + write bytes); torch.mm 8192^3 bf16; "
+                   "one event pair around 10 launches after 3 warm-up launches"}
+
+
 def launch_floor(steps=100, warmup=10):
     """Per-launch time (s) of the library's empty kernel, timed like a run."""
     import window_spmm_amd as ws
@@ -561,6 +585,7 @@ def main():
     }
     floor = launch_floor()
     out["launch_floor_us"] = floor * 1e6
+    out["measured_peaks"] = measured_peaks()
     out["roofline_fraction_with_floor"] = min(1.0, (max(t_roof_mfma, t_roof_hbm) + floor) / t_kernel)
     if cold is not None:
         out["cold_us"] = cold * 1e6
