@@ -141,10 +141,22 @@ def cpu_baseline(p, budget_s: float):
         t_total += time.perf_counter() - t0
         reps += 1
     t = t_total / reps
+    # the same sample on one thread, once
+    t0 = time.perf_counter()
+    oracle.spmm(n_rows, p.k, p.N, r, c, v, p.B, p.ab_dtype, nthreads=1)
+    t1 = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": 2.0 * r.size * p.N / t / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": "rows 0..%d of the same matrix (%d nonzeros, N=%d), fp64, %d repetition(s), "
-                      "%.2f s each" % (n_rows - 1, r.size, p.N, reps, t)}
+                      "%.2f s each" % (n_rows - 1, r.size, p.N, reps, t),
+            "one_thread": {"value": 2.0 * r.size * p.N / t1 / 1e12, "seconds": t1},
+            "cpu_model": model}
 
 
 def sweep_candidates(p):
