@@ -406,6 +406,21 @@ def test_config3_members(ws, N):
         check(p, got, rows=rows)
 
 
+@pytest.mark.parametrize("member,N", [(3, 32), (15, 32), (15, 128), (13, 256)])
+def test_config3_members_with_many_merges(ws, member, N):
+    """Population members whose Zipf row lengths make a few windows very long:
+    the plan cuts them into many 512-column tasks (tens of split windows with up
+    to ~18 slots each, so the merge pass runs several rounds per lane group).
+    Full parity with the oracle."""
+    p = synth.config3_matrix(member, N)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    info = A.plan.info()
+    _say("   plan", info)
+    assert info["n_merges"] > 0, info
+    check(p, run_gpu(ws, p, A=A))
+
+
 @pytest.mark.parametrize("N", [256, 136])
 def test_banded_large_b_row_order_wide_tiles(ws, N):
     """A banded pattern whose B spans several L2s (population member 18: 36674
