@@ -421,15 +421,18 @@ def test_config3_members_with_many_merges(ws, member, N):
     check(p, run_gpu(ws, p, A=A))
 
 
-@pytest.mark.parametrize("N", [256, 136])
-def test_banded_large_b_row_order_wide_tiles(ws, N):
+@pytest.mark.parametrize("fmt,N", [("wcsr", 256), ("wcsr", 136), ("bcsr", 264)])
+def test_banded_large_b_row_order_wide_tiles(ws, fmt, N):
     """A banded pattern whose B spans several L2s (population member 18: 36674
-    rows, band 1 % of n) with few windows per resident work-group: the plan runs
-    one work-group per window in row order with 256-column tiles (N = 136: one
-    ragged tile).  Full parity with the oracle."""
+    rows, band 1 % of n) with few row tiles per resident work-group: the plan
+    runs one work-group per row tile in row order with 256-column tiles (N =
+    136: one ragged tile; BCSR with 16 x 16 blocks at N = 264: a second, ragged
+    column tile and a ragged last block row).  Full parity with the oracle."""
     import dataclasses
     p = synth.config3_matrix(18, 256)
-    p = dataclasses.replace(p, N=N, B=np.ascontiguousarray(p.B[:, :N]), name="cfg3_m18_N%d" % N)
+    B = p.B if N <= 256 else np.concatenate([p.B, p.B[:, :N - 256]], axis=1)
+    p = dataclasses.replace(p, N=N, B=np.ascontiguousarray(B[:, :N]), fmt=fmt,
+                            b_col=16 if fmt == "bcsr" else p.b_col, name="cfg3_m18_%s_N%d" % (fmt, N))
     A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
                         p.ab_dtype, p.c_dtype)
     info = A.plan.info()
