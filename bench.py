@@ -481,6 +481,10 @@ def main():
     if args.fp8 and args.config != 4:
         raise SystemExit("--fp8 applies to config 4")
 
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
     if args.copy_probe:
         copy_probe()
         return
@@ -490,11 +494,6 @@ def main():
     if args.population:
         run_population(args)
         return
-
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
 
     import torch
     import window_spmm_amd as ws
