@@ -390,6 +390,23 @@ def test_config2_full(ws, cfg2):
     check(cfg2, run_gpu(ws, cfg2))
 
 
+def test_plan_shapes_of_measured_workloads(ws, cfg2):
+    """The plan's automatic choices on workloads whose best shape was measured
+    (plan sweeps): the 16384^2 WCSR workload takes 8 columns per lane and 4
+    reduction waves with no window cut (no merge pass); a small uniform
+    population member (50443 rows, about 156 packed columns per window) takes
+    one reduction wave."""
+    A = ws.DeviceSparse(cfg2.fmt, cfg2.m, cfg2.k, cfg2.N, cfg2.row_ptr, cfg2.col_idx, cfg2.vals,
+                        cfg2.b_row, cfg2.b_col, cfg2.ab_dtype, cfg2.c_dtype)
+    info = A.plan.info()
+    assert (info["cols_per_lane"], info["waves_n"], info["waves_k"], info["n_merges"]) == (8, 1, 4, 0), info
+    p = synth.config3_matrix(13, 128, with_b=False)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    info = A.plan.info()
+    assert (info["cols_per_lane"], info["waves_k"]) == (8, 1), info
+
+
 @pytest.mark.parametrize("N", [32, 128, 256])
 def test_config3_members(ws, N):
     specs = synth.config3_specs()
