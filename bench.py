@@ -6,10 +6,18 @@ kernel).  Throughput follows the AsyncSparse paper's evaluation (Section IV):
 2 * nnz * N / t with nnz the true nonzero count of A; the stored-entry rate
 (2 * stored * N / t) is reported next to it.
 
-Default workload: the WCSR matrix 16384 x 16384 at about 1% density (window 16,
-column padding 8), N = 128, fp16 in, fp32 out.  ``--config`` selects another
-workload (1: small BCSR, 3: one WCSR population member, 4: BCSR at Qwen2.5-7B
-gate_proj shape, 5: block-sparse P*V).  Prints one JSON line.
+Default workload: BCSR at the Qwen2.5-7B gate_proj shape (18944 x 3584 bf16
+weight, 64 x 64 blocks, 6 of 56 per block row, times 65536 tokens, bf16 out),
+the largest of the five workloads; then, as extra keys of the same line, the
+WCSR matrix 16384 x 16384 at about 1% density (window 16, column padding 8),
+N = 128, fp16 in, fp32 out.  ``--config`` selects another workload (1: small
+BCSR, 2: the WCSR matrix alone, 3: one WCSR population member, 5: block-sparse
+P*V).  Prints one JSON line.
+
+Timing: `value`, `ms_per_step` and `roofline` use cold-cache time, each launch
+preceded by a 1 GiB fill (more than the 256 MB MALL and the L2s together), the
+fills' own time subtracted; warm time (launches back to back, the paper's
+protocol) is reported next to it.  ``--warm-only`` skips the cold pass.
 """
 
 from __future__ import annotations
@@ -341,6 +349,88 @@ def time_runs(A, B, C, steps, warmup):
     return time_calls(lambda st: A.run(B, C, st), steps, warmup)
 
 
+def timed_pair(A, B, C, steps, warmup, cold=True):
+    """Warm and cold per-launch time (s) of one SpMM.
+
+    Warm: after `warmup` launches, one HIP event pair on the launch stream
+    around `steps` back-to-back launches.  Cold: `steps` steps of (1 GiB fill,
+    launch), the fill writing more than the MALL and every L2 hold, so each
+    launch starts with its inputs in HBM only; the region of `steps` fills
+    alone is timed the same way and subtracted.  Every region is bracketed by
+    torch.cuda.synchronize() on both sides.  Returns (warm, cold or None, the
+    regions' raw times in ms)."""
+    import torch
+    t_warm, wall_warm = time_runs(A, B, C, steps, warmup)
+    region = {"warm_ms": t_warm * steps * 1e3, "warm_wall_ms": wall_warm * steps * 1e3}
+    if not cold:
+        return t_warm, None, region
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=C.device)
+    t_pair, _ = time_calls(lambda st: (flush.fill_(1.0), A.run(B, C, st)), steps, 2)
+    t_fill, _ = time_calls(lambda st: flush.fill_(1.0), steps, 2)
+    del flush
+    region.update({"fill_and_run_ms": t_pair * steps * 1e3, "fill_only_ms": t_fill * steps * 1e3})
+    return t_warm, max(t_pair - t_fill, 1e-9), region
+
+
+def roofline_of(p, alg, t, info, key):
+    """The roofline record of one launch time t (s): the bound (MFMA or HBM,
+    whichever takes longer at its published peak), achieved rate, fraction,
+    and the HBM traffic the counters recorded for this workload."""
+    peak_mfma = PEAK_MFMA_TFLOPS_FP8 if p.ab_dtype == "fp8" else PEAK_MFMA_TFLOPS
+    t_roof_mfma = alg["flops_stored"] / (peak_mfma * 1e12)
+    t_roof_hbm = alg["bytes_alg"] / (PEAK_HBM_GBS * 1e9)
+    if t_roof_hbm >= t_roof_mfma:
+        roof = {"bound": "hbm", "achieved": alg["bytes_alg"] / t / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": alg["flops_stored"] / t / 1e12,
+                "peak": peak_mfma, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(key)
+    roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roof["kernel_us"] = t * 1e6
+    roof["kernels"] = KERNEL_NAMES.get(info["kernel"], "spmm_tile_kernel") + \
+        (" + wcsr_merge_kernel" if info["n_merges"] else "")
+    return roof
+
+
+KERNEL_NAMES = {0: "spmm_tile_kernel", 1: "bcsr64_lds_kernel", 2: "bcsr64_sweep_kernel"}
+
+
+def wcsr_extra(args, dev):
+    """The WCSR half of the default line: the 16384^2 matrix at about 1%
+    density, window 16, N = 128, timed warm and cold like the main workload."""
+    import torch
+    import window_spmm_amd as ws
+    print("bench: WCSR workload (config 2)", file=sys.stderr, flush=True)
+    p, workload = make_problem(2, args)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, device=dev)
+    B = A.device_b(p.B, dev, padded=True)
+    C = A.new_c(dev, padded=True)
+    alg = algorithmic(p, A)
+    info = A.plan.info()
+    t_warm, t_cold, region = timed_pair(A, B, C, max(args.steps, 20), args.warmup,
+                                        not args.warm_only)
+    t = t_cold if t_cold is not None else t_warm
+    t_roof = roofline_time(p, alg)
+    out = {"workload": workload, "timing": "cold" if t_cold is not None else "warm",
+           "tflops_true": alg["flops_true"] / t / 1e12,
+           "tflops_stored": alg["flops_stored"] / t / 1e12,
+           "roofline_fraction": t_roof / t, "t_roof_us": t_roof * 1e6,
+           "warm_us": t_warm * 1e6, "roofline_fraction_warm": t_roof / t_warm,
+           "bytes_alg": alg["bytes_alg"], "nnz": p.nnz, "stored_entries": A.stored_entries,
+           "roofline": roofline_of(p, alg, t, info, "config2"),
+           "plan": {k: info[k] for k in ("kernel", "tile_cols", "waves_n", "waves_k",
+                                         "cols_per_lane", "split_cols", "n_tasks", "n_merges")},
+           "timed_regions": region}
+    if t_cold is not None:
+        out["cold_us"] = t_cold * 1e6
+    del A, B, C
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_peaks():
     """What this GPU reaches on plain dense work, timed like a run, next to the
     published peaks the roofline uses: a 1 GiB device-to-device copy (HBM read
@@ -449,7 +539,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--which", default="gate", help="config 4 weight: gate, up or down")
     ap.add_argument("--member", type=int, default=0, help="config 3 matrix index")
     ap.add_argument("--population", action="store_true",
@@ -461,9 +551,10 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="WCSR sub-task size (0 = plan's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time with caches flushed (a 1 GiB fill before each launch)")
-    ap.add_argument("--no-cold", action="store_true", help="no cold-cache timing (the default)")
+    ap.add_argument("--warm-only", action="store_true",
+                    help="no cold-cache pass: value and roofline from warm launches")
+    ap.add_argument("--no-wcsr", action="store_true",
+                    help="default workload: leave out the WCSR (config 2) extra keys")
     ap.add_argument("--no-pad", action="store_true", help="B and C with leading dimension N")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
@@ -529,45 +620,20 @@ def main():
         run_sweep(p, A, B, C, alg, workload, {"col_major": 1} if args.col_major else None)
         return
 
-    stream = torch.cuda.current_stream()
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    # one HIP event pair on the launch stream around the timed region (the
-    # steps are launched back to back); per-launch time = region / steps
-    t_kernel, t_wall = time_runs(A, B, C, args.steps, args.warmup)
-    ms_step = t_wall * 1e3
+    t_warm, t_cold, region = timed_pair(A, B, C, args.steps, args.warmup, not args.warm_only)
+    t_kernel = t_cold if t_cold is not None else t_warm
 
-    cold = None
-    if args.cold and not args.no_cold:
-        # caches flushed before every launch: a 1 GiB fill (more than the MALL
-        # and the L2s together) precedes each run; per-run time = the region of
-        # K (fill, run) pairs minus the region of K fills alone
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        k = min(args.steps, 30)
-        t_pair, _ = time_calls(lambda st: (flush.fill_(1.0), A.run(B, C, st)), k, 2)
-        t_fill, _ = time_calls(lambda st: flush.fill_(1.0), k, 2)
-        cold = max(t_pair - t_fill, 1e-9)
-        del flush
-
-    peak_mfma = PEAK_MFMA_TFLOPS_FP8 if p.ab_dtype == "fp8" else PEAK_MFMA_TFLOPS
-    t_roof_mfma = alg["flops_stored"] / (peak_mfma * 1e12)
-    t_roof_hbm = alg["bytes_alg"] / (PEAK_HBM_GBS * 1e9)
-    if t_roof_hbm >= t_roof_mfma:
-        roof = {"bound": "hbm", "achieved": alg["bytes_alg"] / t_kernel / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": alg["flops_stored"] / t_kernel / 1e12,
-                "peak": peak_mfma, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
     key = "config%d" % args.config + ("_" + args.which if args.config == 4 else "") + \
           ("_m%d_n%d" % (args.member, args.n3) if args.config == 3 else "") + \
           ("_colmajor" if args.col_major else "") + ("_fp8" if args.fp8 else "")
-    roof["traffic"] = measured_traffic(key)
-    roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-    roof["kernel_us"] = t_kernel * 1e6
-    roof["kernels"] = {1: "bcsr64_lds_kernel", 2: "bcsr64_sweep_kernel"}.get(info["kernel"], "spmm_tile_kernel") + \
-        (" + wcsr_merge_kernel" if info["n_merges"] else "")
+    roof = roofline_of(p, alg, t_kernel, info, key)
+    peak_mfma = PEAK_MFMA_TFLOPS_FP8 if p.ab_dtype == "fp8" else PEAK_MFMA_TFLOPS
+    t_roof_mfma = alg["flops_stored"] / (peak_mfma * 1e12)
+    t_roof_hbm = alg["bytes_alg"] / (PEAK_HBM_GBS * 1e9)
+    ms_step = t_kernel * 1e3
 
-    value = alg["flops_true"] / (ms_step / 1e3) / 1e12
+    value = alg["flops_true"] / t_kernel / 1e12
     out = {
         "metric": METRIC,
         "value": value,
@@ -587,23 +653,34 @@ def main():
                    "stored_entries": A.stored_entries, "c_dtype": p.c_dtype,
                    "plan": {k: info[k] for k in ("kernel", "tile_cols", "waves_n", "waves_k", "cols_per_lane",
                                                  "split_cols", "n_tasks", "n_merges")}},
-        "tflops_true_event": alg["flops_true"] / t_kernel / 1e12,
-        "tflops_stored_event": alg["flops_stored"] / t_kernel / 1e12,
+        "timing": "cold" if t_cold is not None else "warm",
+        "tflops_true": value,
+        "tflops_stored": alg["flops_stored"] / t_kernel / 1e12,
         "roofline_fraction": max(t_roof_mfma, t_roof_hbm) / t_kernel,
         "t_roof_us": max(t_roof_mfma, t_roof_hbm) * 1e6,
         "bytes_alg": alg["bytes_alg"],
+        "warm_us": t_warm * 1e6,
+        "roofline_fraction_warm": max(t_roof_mfma, t_roof_hbm) / t_warm,
+        "tflops_true_warm": alg["flops_true"] / t_warm / 1e12,
         "roofline": roof,
+        "timed_regions": region,
     }
+    if t_cold is not None:
+        out["cold_us"] = t_cold * 1e6
+        out["roofline_fraction_cold"] = max(t_roof_mfma, t_roof_hbm) / t_cold
     floor = launch_floor()
     out["launch_floor_us"] = floor * 1e6
-    out["measured_peaks"] = measured_peaks()
     out["roofline_fraction_with_floor"] = min(1.0, (max(t_roof_mfma, t_roof_hbm) + floor) / t_kernel)
-    if cold is not None:
-        out["cold_us"] = cold * 1e6
-        out["roofline_fraction_cold"] = max(t_roof_mfma, t_roof_hbm) / cold
     if not args.no_cpu:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    default_line = args.config == 4 and args.which == "gate" and not (args.fp8 or args.col_major) \
+        and args.n4 == 65536
+    if default_line and not args.no_wcsr:
+        del A, B, C
+        torch.cuda.empty_cache()
+        out["wcsr_cfg2"] = wcsr_extra(args, dev)
+    out["measured_peaks"] = measured_peaks()
     print(json.dumps(out), flush=True)
 
 

@@ -20,6 +20,9 @@
  *  - 16-bit values are passed as raw codes (uint16_t): IEEE binary16 or
  *    bfloat16 according to the dtype argument.  Builders copy codes bit-exactly.
  *  - Matrices are row-major; leading dimensions (ldb, ldc) count elements.
+ *  - Test hook: with the environment variable SPMM_TEST_FAIL_ALLOC set to a
+ *    value other than "" or "0", every host and device allocation the library
+ *    makes fails, so that the SPMM_ERR_OUT_OF_MEMORY paths can be exercised.
  */
 #ifndef WINDOW_SPMM_H
 #define WINDOW_SPMM_H
@@ -219,13 +222,25 @@ typedef struct {
 
 void spmm_plan_options_default(spmm_plan_options_t *opt);
 
-/* BCSR plan.  h_block_row_ptr[ceil(m/b_row)+1] (host, read during the call);
- * d_block_col_idx[nnz_blocks], d_blocks[nnz_blocks*b_row*b_col] (device).
- * Block-column indices are not read on the host; an index whose block lies
- * outside [0, k) contributes nothing (its B rows read as zero).  Long block rows
+/* BCSR plan.  The product of the paper's BCSR kernel (Section III-A: each
+ * work-group owns a block row and a column tile of C and walks the block row's
+ * stored blocks, multiplying each dense block with the B tile of its block
+ * column; Section IV-C: the tile width is chosen per N).
+ * h_block_row_ptr[ceil(m/b_row)+1] (host, read during the call);
+ * d_block_col_idx[nnz_blocks], d_blocks[nnz_blocks*b_row*b_col] (device; the
+ * arrays spmm_csr_to_bcsr produced, copied to the device by the caller).
+ * nnz_blocks is h_block_row_ptr[ceil(m/b_row)].
+ * Block-column indices are read on the host only for a sample of up to 64
+ * block rows (see "Synchronisation"); an index whose block lies outside
+ * [0, k) contributes nothing (its B rows read as zero).  Long block rows
  * may be split into sub-tasks exactly like WCSR windows (same rule, counted in
  * packed columns = blocks * b_col) and merged in a fixed order; the plan then
- * needs a workspace.  UNSUPPORTED if nnz_blocks * b_col >= 2^31. */
+ * needs a workspace.  UNSUPPORTED if nnz_blocks * b_col >= 2^31.
+ * Synchronisation: a plan call is blocking.  It allocates and fills its device
+ * tables with synchronous copies, and it reads a few device index entries back
+ * to the host (synchronous device-to-host copies on the null stream, which
+ * wait for the device) to tell banded from scattered patterns.  Make plans
+ * outside timed or captured regions. */
 spmm_status_t spmm_bcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
                              int32_t b_col, const int32_t *h_block_row_ptr,
                              const int32_t *d_block_col_idx, const void *d_blocks,
@@ -237,12 +252,19 @@ spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t
                                 spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
                                 const spmm_plan_options_t *options, size_t *workspace_bytes);
 
-/* WCSR plan.  h_window_row_ptr[ceil(m/b_row)+1] (host; every window width a
+/* WCSR plan.  The product of the paper's WCSR kernel (Section III-B and
+ * Section III-C: a work-group gathers the B rows named by its window's column
+ * union and multiplies them with the window's packed value tile; long windows
+ * are cut into fixed-size sub-tasks, one task descriptor per work-group, whose
+ * partial tiles are merged -- here by a second pass in a fixed order instead of
+ * the paper's atomic adds).
+ * h_window_row_ptr[ceil(m/b_row)+1] (host; every window width a
  * multiple of b_col, else BAD_FORMAT); d_window_col_idx[P], d_values[b_row*P]
- * (device).  A column index outside [0, k) (the -1 pads included) reads B as
- * zero.  split_cols: sub-task size T (positive multiple of 32, at most 8192), or
- * 0 to let the plan choose.  UNSUPPORTED if a window tile (b_row * width * 2
- * bytes) reaches 2^32 - 256. */
+ * (device), P = h_window_row_ptr[ceil(m/b_row)].  A column index outside
+ * [0, k) (the -1 pads included) reads B as zero.  split_cols: sub-task size T
+ * (positive multiple of 32, at most 8192), or 0 to let the plan choose.
+ * UNSUPPORTED if a window tile (b_row * width * 2 bytes) reaches 2^32 - 256.
+ * Synchronisation as for spmm_bcsr_plan. */
 spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
                              int32_t b_col, const int32_t *h_window_row_ptr,
                              const int32_t *d_window_col_idx, const void *d_values,
@@ -256,8 +278,10 @@ spmm_status_t spmm_wcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t
                                 spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype, int64_t split_cols,
                                 const spmm_plan_options_t *options, size_t *workspace_bytes);
 
-/* Run: C = A * B, enqueued on `stream` (a hipStream_t; NULL = the null stream),
- * no host synchronisation.  d_B: k x N codes with leading dimension ldb (the
+/* Run: C = A * B (the problem of Section II-C: A sparse m x k, B dense k x N),
+ * computed by the kernels of Section III-A..III-C as chosen by the plan, fp32
+ * accumulation, one rounding to c_dtype.  Enqueued on `stream` (a hipStream_t;
+ * NULL = the null stream), no host synchronisation and no allocation.  d_B: k x N codes with leading dimension ldb (the
  * kernels read no byte past element (k - 1) * ldb + N - 1); d_C:
  * m x N of c_dtype with leading dimension ldc.  Rows < m and columns < N of C
  * are overwritten (C is never read); rows without entries become 0.

@@ -4,8 +4,9 @@ INFRASTRUCTURE ONLY (see the package docstring).
 The AsyncSparse paper preprocesses every evaluation matrix with reverse
 Cuthill-McKee before building its formats (Section IV-A), citing Cuthill and
 McKee, "Reducing the bandwidth of sparse symmetric matrices" (1969).  The paper
-does not fix a start-vertex rule or tie-breaking; the oracle uses the rules
-stated for the library's ``spmm_rcm_order`` (C header), each a standard choice:
+does not fix a start-vertex rule or tie-breaking, so the oracle fixes them, each
+a standard choice from the reordering literature (George and Liu's
+pseudo-peripheral search for the start, degree-then-index order for ties):
 
 1. graph: the pattern of A plus its transpose, self loops dropped;
 2. each component starts from the unnumbered vertex of least degree (ties:

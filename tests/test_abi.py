@@ -119,3 +119,33 @@ def test_plan_options_default_and_checks():
                      options={"kernel": 1})
     with pytest.raises(ValueError):
         ws.PlanOptions.of({"tile": 3})
+
+
+def test_allocation_failure_hook_gives_out_of_memory(monkeypatch):
+    """SPMM_TEST_FAIL_ALLOC makes every guarded allocation fail: each builder,
+    the split and the reordering calls then return OUT_OF_MEMORY with a
+    message and write nothing; without it the same calls succeed."""
+    import synth
+    p = synth.random_problem(40, 50, 8, 0.1, seed=3)
+    sq = synth.random_problem(40, 40, 8, 0.1, seed=4)  # square, for the reordering calls
+    calls = {
+        "bcsr": lambda: ws.csr_to_bcsr(p.m, p.k, p.row_ptr, p.col_idx, p.vals, 16, 16),
+        "bcsr8": lambda: ws.csr_to_bcsr(p.m, p.k, p.row_ptr, p.col_idx, p.vals & 0x7F, 16, 16,
+                                        code_bytes=1),
+        "wcsr": lambda: ws.csr_to_wcsr(p.m, p.k, p.row_ptr, p.col_idx, p.vals, 16, 8),
+        "split": lambda: ws.wcsr_split(np.array([0, 64, 64, 200], np.int32), 32),
+        "rcm": lambda: ws.rcm_order(40, sq.row_ptr, sq.col_idx),
+        "permute": lambda: ws.csr_permute(40, sq.row_ptr, sq.col_idx, sq.vals,
+                                          np.arange(40, dtype=np.int32)),
+    }
+    for name, fn in calls.items():
+        fn()  # succeeds without the hook
+    monkeypatch.setenv("SPMM_TEST_FAIL_ALLOC", "1")
+    for name, fn in calls.items():
+        with pytest.raises(ws.SpmmError) as e:
+            fn()
+        assert e.value.code == ws.ERR_OUT_OF_MEMORY, name
+        assert "allocation" in str(e.value), name
+    monkeypatch.setenv("SPMM_TEST_FAIL_ALLOC", "0")
+    for fn in calls.values():
+        fn()

@@ -407,20 +407,47 @@ def test_plan_shapes_of_measured_workloads(ws, cfg2):
     assert (info["cols_per_lane"], info["waves_k"]) == (8, 1), info
 
 
-@pytest.mark.parametrize("N", [32, 128, 256])
-def test_config3_members(ws, N):
-    specs = synth.config3_specs()
-    small = sorted(range(32), key=lambda j: specs[j][0] * specs[j][1])[:3]
-    for j in small:
-        p = synth.config3_matrix(j, N)
-        check(p, run_gpu(ws, p))
-    # the largest member, on sampled rows
-    j = max(range(32), key=lambda j: specs[j][0] * specs[j][1])
-    if N == 128:
-        p = synth.config3_matrix(j, N)
-        got = run_gpu(ws, p)
-        rows = np.random.default_rng(0).choice(p.m, 512, replace=False)
-        check(p, got, rows=rows)
+# members up to this many rows are compared with the oracle on every row
+CFG3_FULL_ROWS = 60000
+
+
+def _cfg3_rows(p, seed):
+    """Rows of a large population member to compare with the oracle: 512 at
+    random, the first and last 16 (ragged last window), and every row of the
+    four longest windows (the Zipf tail: these are the windows the plan cuts
+    into sub-tasks and merges)."""
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(p.m, 512, replace=False).tolist())
+    rows |= set(range(16)) | set(range(p.m - 16, p.m))
+    nw = -(-p.m // p.b_row)
+    lens = np.add.reduceat(np.diff(p.row_ptr.astype(np.int64)),
+                           np.arange(0, p.m, p.b_row)) if p.m else np.zeros(0)
+    for w in np.argsort(-lens)[:4]:
+        rows |= set(range(int(w) * p.b_row, min(p.m, (int(w) + 1) * p.b_row)))
+    assert nw == lens.size
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("member", range(32))
+def test_config3_member_all_n(ws, member):
+    """Config 3 run by run: population member `member` at N = 32, 128 and 256
+    (the 96 runs of the workload, three per test), through the default plan.
+    Members up to 60000 rows are compared with the oracle on every row; larger
+    ones on sampled rows that include every row of their longest (split)
+    windows; every element of C must have been written (C starts as NaN)."""
+    import dataclasses
+    p256 = synth.config3_matrix(member, 256)
+    for N in (32, 128, 256):
+        p = dataclasses.replace(p256, N=N, B=np.ascontiguousarray(p256.B[:, :N]),
+                                name="cfg3_m%d_N%d" % (member, N))
+        A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row,
+                            p.b_col, p.ab_dtype, p.c_dtype)
+        _say("   plan", {k: v for k, v in A.plan.info().items()
+                         if k in ("tile_cols", "waves_k", "n_tasks", "n_merges")})
+        got = run_gpu(ws, p, A=A)
+        assert np.isfinite(got).all()
+        check(p, got, rows=None if p.m <= CFG3_FULL_ROWS else _cfg3_rows(p, member))
+        del A, got
 
 
 @pytest.mark.parametrize("member,N", [(3, 32), (15, 32), (15, 128), (13, 256)])
@@ -457,12 +484,33 @@ def test_banded_large_b_row_order_wide_tiles(ws, fmt, N):
     check(p, run_gpu(ws, p, A=A))
 
 
-def test_config4_gate_sampled(ws):
-    p = synth.config4("gate")
+def _block_rows_sample(p, seed, n_random=48):
+    """Random rows plus every row of the first and last block rows."""
+    rows = set(np.random.default_rng(seed).choice(p.m, n_random, replace=False).tolist())
+    rows |= set(range(min(p.m, p.b_row))) | set(range(max(0, p.m - p.b_row), p.m))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("which", ["gate", "up"])
+def test_config4_gate_up_sampled(ws, which):
+    """Config 4's 18944 x 3584 weights (gate and up are two seeded draws) at the
+    full N = 65536 tokens, the launch configuration the benchmark times: every
+    element written, sampled rows (each compared across all 65536 columns, so
+    every column tile) against the oracle."""
+    p = synth.config4(which)
     got = run_gpu(ws, p)
     assert np.isfinite(got).all()
-    rows = np.random.default_rng(1).choice(p.m, 48, replace=False)
-    check(p, got, rows=rows)
+    check(p, got, rows=_block_rows_sample(p, 1 if which == "gate" else 4))
+
+
+def test_config4_down_full_n_sampled(ws):
+    """Config 4's down weight (3584 x 18944, 30 blocks per block row) at the
+    full N = 65536: B is 2.5 GB, so the B offsets reach the top of the 32-bit
+    buffer range of the kernels' addressing."""
+    p = synth.config4("down")
+    got = run_gpu(ws, p)
+    assert np.isfinite(got).all()
+    check(p, got, rows=_block_rows_sample(p, 2))
 
 
 def test_config4_down_sampled(ws):
@@ -472,12 +520,70 @@ def test_config4_down_sampled(ws):
     check(p, got, rows=rows)
 
 
-def test_config5_sampled(ws):
-    p = synth.config5()
+@pytest.mark.parametrize("width", [1, 9])
+def test_config5_sampled(ws, width):
+    """Config 5 (block-sparse attention probabilities times V): the literal
+    pattern (1-block-wide lines) and the variant whose lines are 9 blocks
+    wide (about 9 % of causal blocks), on sampled rows."""
+    p = synth.config5(width=width)
     got = run_gpu(ws, p)
     assert np.isfinite(got).all()
-    rows = np.random.default_rng(3).choice(p.m, 2048, replace=False)
+    rows = np.random.default_rng(3 + width).choice(p.m, 2048, replace=False)
     check(p, got, rows=rows)
+
+
+WIDE_BCSR_CASES = [
+    # m, k, N, b_row, b_col, ab, c: blocks 128 and 256 columns wide, ragged m, k, N
+    (200, 700, 72, 16, 128, "fp16", "fp32"),
+    (333, 900, 264, 32, 128, "bf16", "bf16"),
+    (130, 1000, 136, 64, 128, "bf16", "fp32"),
+    (96, 1300, 40, 16, 256, "fp16", "fp16"),
+    (250, 777, 200, 32, 256, "bf16", "fp32"),
+    (129, 1100, 128, 64, 256, "fp16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_BCSR_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bcsr_wide_blocks(ws, case):
+    """BCSR with 128- and 256-column blocks (the generic kernel's wide-block
+    path: several 32-column steps per block, block rows of up to 8192 packed
+    columns) on every tile height, ragged m, k and N, all output types."""
+    m, k, N, br, bc, ab, ct = case
+    p = synth.block_problem(m, k, N, br, bc, 0.4, seed=m + bc, ab_dtype=ab, c_dtype=ct,
+                            entry_density=0.5)
+    check(p, run_gpu(ws, p))
+
+
+@pytest.mark.parametrize("br,bc", [(16, 128), (64, 256)])
+def test_bcsr_wide_blocks_split_block_row(ws, br, bc):
+    """One block row far longer than the others: the plan cuts it into
+    sub-tasks whose partial tiles the merge pass adds (n_merges > 0)."""
+    import dataclasses
+    m, k, N = 8 * br, 40 * bc, 136
+    p = synth.block_problem(m, k, N, br, bc, 0.08, seed=br + bc, ab_dtype="bf16",
+                            c_dtype="fp32", entry_density=0.3)
+    # make block row 3 dense: every entry of its rows present
+    dense = synth.block_problem(br, k, N, br, bc, 1.0, seed=5, ab_dtype="bf16", c_dtype="fp32",
+                                entry_density=1.0)
+    rows = []
+    for i in range(m):
+        if 3 * br <= i < 4 * br:
+            r = i - 3 * br
+            rows.append((dense.col_idx[dense.row_ptr[r]:dense.row_ptr[r + 1]],
+                         dense.vals[dense.row_ptr[r]:dense.row_ptr[r + 1]]))
+        else:
+            rows.append((p.col_idx[p.row_ptr[i]:p.row_ptr[i + 1]],
+                         p.vals[p.row_ptr[i]:p.row_ptr[i + 1]]))
+    ptr = np.concatenate([[0], np.cumsum([len(c) for c, _ in rows])]).astype(np.int32)
+    p = dataclasses.replace(p, row_ptr=ptr, col_idx=np.concatenate([c for c, _ in rows]).astype(np.int32),
+                            vals=np.concatenate([v for _, v in rows]).astype(np.uint16),
+                            name="wide_split_%dx%d" % (br, bc))
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    info = A.plan.info()
+    _say("   plan", info)
+    assert info["n_merges"] > 0, info
+    check(p, run_gpu(ws, p, A=A))
 
 
 @pytest.mark.parametrize("opts", [{"kernel": 1, "waves_n": 2}, {"kernel": 1, "waves_n": 4},

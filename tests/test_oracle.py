@@ -510,3 +510,70 @@ def test_fp8_generator_encoding_matches_torch():
     # and the oracle's decoder inverts it on its range
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint16)
     assert np.array_equal(fp8_e4m3_bits(oracle.decode16(codes, "fp8")), codes)
+
+
+# --------------------------------------------------------------------------
+# bandwidth and fill ratio: closed forms and independent counts
+# --------------------------------------------------------------------------
+
+def _csr_of_pairs(n, pairs):
+    pairs = sorted(set(pairs))
+    rows = np.array([i for i, _ in pairs], np.int64)
+    cols = np.array([j for _, j in pairs], np.int32)
+    ptr = np.concatenate([[0], np.cumsum(np.bincount(rows, minlength=n))]).astype(np.int32)
+    return ptr, cols
+
+
+def test_bandwidth_closed_forms():
+    """max |i - j| (the quantity reverse Cuthill-McKee reduces, Section IV-A)
+    on patterns whose value is known without computing it: empty and diagonal
+    0, tridiagonal 1, dense n - 1, an arrow (first row and column full) n - 1,
+    a band of half-width b exactly b, a single entry (i, j) exactly |i - j|."""
+    n = 23
+    assert oracle.bandwidth(n, np.zeros(n + 1, np.int32), np.zeros(0, np.int32)) == 0
+    assert oracle.bandwidth(n, *_csr_of_pairs(n, [(i, i) for i in range(n)])) == 0
+    tri = [(i, j) for i in range(n) for j in (i - 1, i, i + 1) if 0 <= j < n]
+    assert oracle.bandwidth(n, *_csr_of_pairs(n, tri)) == 1
+    dense = [(i, j) for i in range(n) for j in range(n)]
+    assert oracle.bandwidth(n, *_csr_of_pairs(n, dense)) == n - 1
+    arrow = [(0, j) for j in range(n)] + [(i, 0) for i in range(n)] + [(i, i) for i in range(n)]
+    assert oracle.bandwidth(n, *_csr_of_pairs(n, arrow)) == n - 1
+    for b in (2, 5, 9):
+        band = [(i, j) for i in range(n) for j in range(max(0, i - b), min(n, i + b + 1))]
+        assert oracle.bandwidth(n, *_csr_of_pairs(n, band)) == b
+    for i, j in ((0, 17), (17, 0), (22, 3), (11, 11), (21, 22)):
+        assert oracle.bandwidth(n, *_csr_of_pairs(n, [(i, j)])) == abs(i - j)
+
+
+def test_bandwidth_sees_the_largest_offset_anywhere():
+    """A tridiagonal pattern with one far entry planted at each position in
+    turn (first row, last row, below and above the diagonal): the result is
+    that entry's offset, whatever row it sits in."""
+    n = 40
+    tri = [(i, j) for i in range(n) for j in (i - 1, i, i + 1) if 0 <= j < n]
+    for i, j in ((0, 31), (39, 2), (20, 0), (5, 39), (39, 39 - 13)):
+        assert oracle.bandwidth(n, *_csr_of_pairs(n, tri + [(i, j)])) == max(1, abs(i - j))
+
+
+@pytest.mark.parametrize("br,bc", [(4, 4), (16, 8), (64, 64), (3, 5)])
+def test_fill_ratio_counts_stored_entries(br, bc):
+    """The fill ratio of Section II-C (real nonzeros over stored block
+    entries) against a count taken from the encoded blocks themselves: the
+    generators never store a zero value, so the nonzero codes in the blocks
+    are exactly the real entries and the zero codes the fill."""
+    for seed in range(4):
+        p = synth.random_problem(97, 130, 8, 0.04 * (seed + 1), seed=seed, empty_row_frac=0.1)
+        brp, bci, blocks = oracle.encode_bcsr(p.m, p.k, p.row_ptr, p.col_idx, p.vals, br, bc)
+        counted = np.count_nonzero(blocks) / blocks.size
+        assert oracle.fill_ratio(p.nnz, int(bci.size), br, bc) == pytest.approx(counted, abs=1e-15)
+
+
+def test_fill_ratio_closed_forms():
+    """A full matrix tiled exactly fills every block (1); one entry fills one
+    block slot (1 / (b_row * b_col)); the identity of order 64 in 16 x 16
+    blocks keeps the 4 diagonal blocks at 16 of 256 entries each (1/16); no
+    blocks at all gives 0."""
+    assert oracle.fill_ratio(64 * 128, 2 * 2, 32, 64) == 1.0
+    assert oracle.fill_ratio(1, 1, 64, 64) == 1 / 4096
+    assert oracle.fill_ratio(64, 4, 16, 16) == 1 / 16
+    assert oracle.fill_ratio(0, 0, 16, 16) == 0.0

@@ -243,13 +243,17 @@ def csr_permute(n: int, row_ptr, col_idx, values, perm):
 # --------------------------------------------------------------------------
 
 class Plan:
-    """Owns a spmm_plan_t; keeps the device arrays it refers to alive."""
+    """Owns a spmm_plan_t; keeps the device arrays it refers to alive and
+    remembers the problem it was made for, so that runs can check their
+    operands against it before anything reaches a kernel."""
 
-    def __init__(self, handle, fmt: str, workspace_bytes: int, keep=()):
+    def __init__(self, handle, fmt: str, workspace_bytes: int, keep=(), problem=None):
         self._h = handle
         self.fmt = fmt
         self.workspace_bytes = int(workspace_bytes)
         self._keep = keep
+        # m, k, N, ab_dtype, c_dtype, col_major, device index (None: unknown)
+        self.problem = problem or {}
 
     @property
     def handle(self):
@@ -275,10 +279,76 @@ class Plan:
             pass
 
 
+# Bytes per element of each dtype name, and the torch dtypes a tensor holding
+# such elements may have (16-bit codes may also travel as raw int16/uint16).
+_ELEM_BYTES = {"fp16": 2, "bf16": 2, "fp32": 4, "fp8": 1}
+_TORCH_OK = {"fp32": ("float32",), "bf16": ("bfloat16", "int16", "uint16"),
+             "fp16": ("float16", "int16", "uint16"), "fp8": ("uint8", "int8", "float8_e4m3fn")}
+
+
+def _is_tensor(x) -> bool:
+    return x is not None and not isinstance(x, int) and hasattr(x, "data_ptr")
+
+
+def _check_dtype(name: str, t, dtype: str):
+    tn = str(t.dtype).replace("torch.", "")
+    if tn not in _TORCH_OK[dtype]:
+        raise ValueError("%s: torch dtype %s does not hold %s elements (expected one of %s)"
+                         % (name, tn, dtype, ", ".join(_TORCH_OK[dtype])))
+
+
+def _check_device_array(name: str, t, elem_bytes: int, need: int, device=None):
+    """A plan's device array: contiguous, on a GPU, elements of the right size,
+    at least `need` of them.  Raw integer addresses are the caller's business."""
+    if not _is_tensor(t):
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if device is not None and t.device.index != device:
+        raise ValueError("%s is on cuda:%s, the plan's other arrays on cuda:%s"
+                         % (name, t.device.index, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.element_size() != elem_bytes:
+        raise ValueError("%s holds %d-byte elements, %d-byte elements expected"
+                         % (name, t.element_size(), elem_bytes))
+    if t.numel() < need:
+        raise ValueError("%s holds %d elements, the row pointer needs %d" % (name, t.numel(), need))
+
+
+def _plan_checks(fmt, m, k, N, b_row, b_col, rp, d_idx, d_vals, ab_dtype, c_dtype, options):
+    """Host-side checks of a plan call that the C library cannot make (it sees
+    raw pointers): the row pointer's length and the device arrays' sizes.
+    Returns the problem record the plan keeps for its runs."""
+    if ab_dtype not in _ELEM_BYTES or c_dtype not in _ELEM_BYTES:
+        raise ValueError("unknown dtype %r / %r" % (ab_dtype, c_dtype))
+    if min(int(m), int(k), int(N)) < 0 or int(b_row) < 1 or int(b_col) < 1:
+        raise ValueError("negative size or non-positive block size")
+    nrow = -(-int(m) // int(b_row))
+    if rp.ndim != 1 or rp.size != nrow + 1:
+        raise ValueError("row pointer has %d entries, ceil(m / b_row) + 1 = %d expected"
+                         % (rp.size, nrow + 1))
+    total = int(rp[-1])
+    if total < 0:
+        raise ValueError("row pointer ends below 0")
+    n_vals = total * int(b_row) * (int(b_col) if fmt == "bcsr" else 1)
+    dev = d_idx.device.index if _is_tensor(d_idx) and d_idx.is_cuda else None
+    _check_device_array("index array", d_idx, 4, total, dev)
+    _check_device_array("value array", d_vals, _ELEM_BYTES[ab_dtype], n_vals, dev)
+    if dev is None and _is_tensor(d_vals) and d_vals.is_cuda:
+        dev = d_vals.device.index
+    return {"m": int(m), "k": int(k), "N": int(N), "ab_dtype": ab_dtype, "c_dtype": c_dtype,
+            "col_major": int((options or {}).get("col_major", 0)), "device": dev}
+
+
 def bcsr_plan(m, k, N, b_row, b_col, h_block_row_ptr, d_block_col_idx, d_blocks,
               ab_dtype="bf16", c_dtype="fp32", options=None) -> Plan:
-    """spmm_bcsr_plan_ex; ``options``: dict of PlanOptions fields to pin."""
+    """spmm_bcsr_plan_ex; ``options``: dict of PlanOptions fields to pin.
+    ValueError if the row pointer's length or a device array's size, element
+    size or device does not fit the problem."""
     rp = _host(h_block_row_ptr, np.int32)
+    prob = _plan_checks("bcsr", m, k, N, b_row, b_col, rp, d_block_col_idx, d_blocks, ab_dtype,
+                        c_dtype, options)
     h = ctypes.c_void_p(0)
     ws = ctypes.c_size_t(0)
     opt = PlanOptions.of(options)
@@ -286,13 +356,16 @@ def bcsr_plan(m, k, N, b_row, b_col, h_block_row_ptr, d_block_col_idx, d_blocks,
                                   _dp(d_block_col_idx), _dp(d_blocks), DTYPES[ab_dtype],
                                   DTYPES[c_dtype], ctypes.byref(opt), ctypes.byref(ws)),
            "spmm_bcsr_plan_ex")
-    return Plan(h, "bcsr", ws.value, (d_block_col_idx, d_blocks))
+    return Plan(h, "bcsr", ws.value, (d_block_col_idx, d_blocks), prob)
 
 
 def wcsr_plan(m, k, N, b_row, b_col, h_window_row_ptr, d_window_col_idx, d_values,
               ab_dtype="fp16", c_dtype="fp32", split_cols=0, options=None) -> Plan:
-    """spmm_wcsr_plan_ex; ``options``: dict of PlanOptions fields to pin."""
+    """spmm_wcsr_plan_ex; ``options``: dict of PlanOptions fields to pin.
+    ValueError as for bcsr_plan."""
     rp = _host(h_window_row_ptr, np.int32)
+    prob = _plan_checks("wcsr", m, k, N, b_row, b_col, rp, d_window_col_idx, d_values, ab_dtype,
+                        c_dtype, options)
     h = ctypes.c_void_p(0)
     ws = ctypes.c_size_t(0)
     opt = PlanOptions.of(options)
@@ -300,7 +373,7 @@ def wcsr_plan(m, k, N, b_row, b_col, h_window_row_ptr, d_window_col_idx, d_value
                                   _dp(d_window_col_idx), _dp(d_values), DTYPES[ab_dtype],
                                   DTYPES[c_dtype], int(split_cols), ctypes.byref(opt),
                                   ctypes.byref(ws)), "spmm_wcsr_plan_ex")
-    return Plan(h, "wcsr", ws.value, (d_window_col_idx, d_values))
+    return Plan(h, "wcsr", ws.value, (d_window_col_idx, d_values), prob)
 
 
 def _stream_handle(stream):
@@ -320,17 +393,58 @@ def launch_floor(stream=None):
 def _ld(t) -> int:
     if t is None:
         return 0
+    if isinstance(t, int):
+        raise ValueError("B and C must be tensors (their leading dimension is read from them)")
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError("B and C must be 2-D with unit column stride")
     return int(t.stride(0))
 
 
+def _run_checks(plan: Plan, B, C, workspace):
+    """Checks B, C and the workspace against the problem the plan was made for:
+    shapes (k x N and m x N, or N x k and N x m for a column-major plan),
+    element types, device, and the workspace size.  Raises ValueError; nothing
+    is launched."""
+    pr = plan.problem
+    if not pr:
+        return
+    cm = pr["col_major"]
+    want_b = (pr["N"], pr["k"]) if cm else (pr["k"], pr["N"])
+    want_c = (pr["N"], pr["m"]) if cm else (pr["m"], pr["N"])
+    for name, t, want, dt in (("B", B, want_b, pr["ab_dtype"]), ("C", C, want_c, pr["c_dtype"])):
+        if t is None:
+            continue
+        if not _is_tensor(t):
+            raise ValueError("%s must be a tensor" % name)
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+        if pr["device"] is not None and t.device.index != pr["device"]:
+            raise ValueError("%s is on cuda:%s, the plan on cuda:%s" % (name, t.device.index,
+                                                                        pr["device"]))
+        if tuple(t.shape) != want:
+            raise ValueError("%s has shape %s, the plan needs %s%s" % (
+                name, tuple(t.shape), want, " (column-major plan)" if cm else ""))
+        _check_dtype(name, t, dt)
+    if plan.workspace_bytes > 0:
+        if not _is_tensor(workspace):
+            raise ValueError("the plan needs a workspace tensor of %d bytes" % plan.workspace_bytes)
+        if not workspace.is_cuda or (pr["device"] is not None and
+                                     workspace.device.index != pr["device"]):
+            raise ValueError("the workspace must be on the plan's device")
+        if not workspace.is_contiguous() or \
+                workspace.numel() * workspace.element_size() < plan.workspace_bytes:
+            raise ValueError("the workspace must be contiguous and hold %d bytes"
+                             % plan.workspace_bytes)
+
+
 def bcsr_run(plan: Plan, B, C, workspace=None, stream=None):
+    _run_checks(plan, B, C, workspace)
     _check(_lib.spmm_bcsr_run(plan.handle, _dp(B), _ld(B), _dp(C), _ld(C), _dp(workspace),
                               _stream_handle(stream)), "spmm_bcsr_run")
 
 
 def wcsr_run(plan: Plan, B, C, workspace=None, stream=None):
+    _run_checks(plan, B, C, workspace)
     _check(_lib.spmm_wcsr_run(plan.handle, _dp(B), _ld(B), _dp(C), _ld(C), _dp(workspace),
                               _stream_handle(stream)), "spmm_wcsr_run")
 
@@ -388,6 +502,7 @@ class DeviceSparse:
         nbytes = self.plan.workspace_bytes
         self.workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32,
                                      device=self.device) if nbytes else None
+        self._ws_stream = None
         return self
 
     @property
@@ -418,6 +533,21 @@ class DeviceSparse:
         out.copy_(src)
         return out
 
-    def run(self, B, C, stream=None):
-        (bcsr_run if self.fmt == "bcsr" else wcsr_run)(self.plan, B, C, self.workspace, stream)
+    def run(self, B, C, stream=None, workspace=None):
+        """Enqueues C = A * B on `stream` (the current stream if None).  The
+        object owns one workspace; runs that may overlap (on different
+        streams) each need their own, passed as `workspace`.  Without one, a
+        plan that uses its workspace (split windows) refuses a stream other
+        than the one of its first run."""
+        if workspace is None:
+            workspace = self.workspace
+            if workspace is not None:
+                h = _stream_handle(stream).value
+                if self._ws_stream is None:
+                    self._ws_stream = h
+                elif h != self._ws_stream:
+                    raise ValueError("this plan's own workspace is in use by another stream; "
+                                     "pass a workspace of %d bytes for this one"
+                                     % self.plan.workspace_bytes)
+        (bcsr_run if self.fmt == "bcsr" else wcsr_run)(self.plan, B, C, workspace, stream)
         return C

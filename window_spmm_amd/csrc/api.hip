@@ -193,6 +193,9 @@ spmm_status_t upload(const T *h, int64_t n, T **d)
     *d = nullptr;
     if (n == 0)
         return SPMM_OK;
+    if (test_fail_alloc())
+        return fail(SPMM_ERR_OUT_OF_MEMORY, "device allocation of %lld bytes refused "
+                    "(SPMM_TEST_FAIL_ALLOC)", (long long)(sizeof(T) * n));
     hipError_t e = hipMalloc(reinterpret_cast<void **>(d), sizeof(T) * (size_t)n);
     if (e != hipSuccess) {
         *d = nullptr;
@@ -391,6 +394,7 @@ spmm_status_t make_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
                          int64_t split_cols, int shift, int n_cu, bool spread, bool local)
 {
     try {
+        alloc_probe();
         std::vector<int32_t> tasks, merges;
         split_tasks(n_rows, start, split_cols, tasks, merges);
         const int64_t nt = (int64_t)tasks.size() / 4, nm = (int64_t)merges.size() / 3;

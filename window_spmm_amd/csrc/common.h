@@ -2,6 +2,7 @@
 #pragma once
 
 #include <functional>
+#include <new>
 #include <vector>
 
 #include "window_spmm.h"
@@ -12,6 +13,18 @@ namespace wspmm {
 spmm_status_t fail(spmm_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 // Clears the thread-local message and returns SPMM_OK.
 spmm_status_t ok();
+
+// Test hook for the out-of-memory paths: when the environment variable
+// SPMM_TEST_FAIL_ALLOC is set to anything but "" or "0", every allocation
+// the library guards fails (host allocations throw std::bad_alloc from here,
+// device allocations report failure), so that the OUT_OF_MEMORY handling
+// can be exercised without exhausting memory.  A no-op otherwise.
+bool test_fail_alloc();
+inline void alloc_probe()
+{
+    if (test_fail_alloc())
+        throw std::bad_alloc();
+}
 
 // Checks a CSR pattern: row_ptr[0] = 0, non-decreasing, columns in [0, k) and
 // strictly increasing inside every row.

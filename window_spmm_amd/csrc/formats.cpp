@@ -100,6 +100,7 @@ extern "C" spmm_status_t spmm_csr_to_bcsr_count(int64_t m, int64_t k, const int3
     if (s != SPMM_OK)
         return s;
     try {
+        alloc_probe();
         const int64_t nbr = ceil_div(m, b_row), nbc = ceil_div(k, b_col);
         std::vector<int64_t> mark(nbc > 0 ? nbc : 1, -1);
         std::vector<int32_t> cols;
@@ -134,6 +135,7 @@ spmm_status_t bcsr_fill(int64_t m, int64_t k, const int32_t *row_ptr, const int3
     if (!block_row_ptr || (nnzb > 0 && (!block_col_idx || !blocks)) || (row_ptr[m] > 0 && !values))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "null output or values pointer");
     try {
+        alloc_probe();
         const int64_t nbr = ceil_div(m, b_row), nbc = ceil_div(k, b_col);
         const int64_t bsz = (int64_t)b_row * b_col;
         std::vector<int64_t> mark(nbc > 0 ? nbc : 1, -1);
@@ -200,6 +202,7 @@ extern "C" spmm_status_t spmm_csr_to_wcsr_count(int64_t m, int64_t k, const int3
     if (s != SPMM_OK)
         return s;
     try {
+        alloc_probe();
         const int64_t nw = ceil_div(m, b_row);
         std::vector<int64_t> mark(k > 0 ? k : 1, -1);
         std::vector<int32_t> cols;
@@ -232,6 +235,7 @@ extern "C" spmm_status_t spmm_csr_to_wcsr(int64_t m, int64_t k, const int32_t *r
         (row_ptr[m] > 0 && !values))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "null output or values pointer");
     try {
+        alloc_probe();
         const int64_t nw = ceil_div(m, b_row);
         std::vector<int64_t> mark(k > 0 ? k : 1, -1);
         std::vector<int32_t> pos(k > 0 ? k : 1, 0);
@@ -347,6 +351,7 @@ extern "C" spmm_status_t spmm_wcsr_split(int64_t n_windows, const int32_t *wptr,
     if ((nt > 0 && !tasks) || (nm > 0 && !merges))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "null tasks or merges pointer");
     try {
+        alloc_probe();
         std::vector<int32_t> t, m;
         split_tasks(n_windows, [wptr](int64_t w) { return (int64_t)wptr[w]; }, split_cols, t, m);
         std::copy(t.begin(), t.end(), tasks);

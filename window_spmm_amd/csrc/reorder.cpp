@@ -104,6 +104,7 @@ extern "C" spmm_status_t spmm_rcm_order(int64_t n, const int32_t *row_ptr, const
     if (s != SPMM_OK)
         return s;
     try {
+        alloc_probe();
         Graph g;
         symmetrize(n, row_ptr, col_idx, g);
         std::vector<char> placed(n, 0);
@@ -188,6 +189,7 @@ extern "C" spmm_status_t spmm_csr_permute(int64_t n, const int32_t *row_ptr, con
     if (nnz > 0 && (!values || !out_col_idx || !out_values))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "null pointer");
     try {
+        alloc_probe();
         std::vector<int32_t> inv(n, -1);
         for (int64_t i = 0; i < n; ++i) {
             const int32_t p = perm[i];

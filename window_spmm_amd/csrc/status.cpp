@@ -1,6 +1,8 @@
 // Status strings and the per-thread last-error message.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "common.h"
 
@@ -23,6 +25,12 @@ spmm_status_t ok()
 {
     g_last_error[0] = '\0';
     return SPMM_OK;
+}
+
+bool test_fail_alloc()
+{
+    const char *v = std::getenv("SPMM_TEST_FAIL_ALLOC");
+    return v && v[0] != '\0' && std::strcmp(v, "0") != 0;
 }
 
 }  // namespace wspmm
