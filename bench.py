@@ -176,6 +176,7 @@ def sweep_candidates(p):
         cands += [{"kernel": 1, "waves_n": wn, "order": o} for wn in (2, 4) for o in (0, 1)]
         cands += [{"kernel": 2, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16)]
         cands += [{"kernel": 2, "cols_per_lane": 4, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16)]
+        cands += [{"kernel": 3, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16, 32)]
     for V in (2, 4, 8):
         if V == 8 and p.b_row >= 32:
             continue
@@ -394,7 +395,8 @@ def roofline_of(p, alg, t, info, key):
     return roof
 
 
-KERNEL_NAMES = {0: "spmm_tile_kernel", 1: "bcsr64_lds_kernel", 2: "bcsr64_sweep_kernel"}
+KERNEL_NAMES = {0: "spmm_tile_kernel", 1: "bcsr64_lds_kernel", 2: "bcsr64_sweep_kernel",
+                3: "bcsr64_pair_kernel"}
 
 
 def wcsr_extra(args, dev):
@@ -553,6 +555,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--warm-only", action="store_true",
                     help="no cold-cache pass: value and roofline from warm launches")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="leave out the measured copy and GEMM peaks (for profiled runs)")
     ap.add_argument("--no-wcsr", action="store_true",
                     help="default workload: leave out the WCSR (config 2) extra keys")
     ap.add_argument("--no-pad", action="store_true", help="B and C with leading dimension N")
@@ -565,6 +569,8 @@ def main():
                          "dense torch.mm (the paper's Table III, kernel level)")
     ap.add_argument("--fp8", action="store_true",
                     help="config 4 with FP8 E4M3 weights and activations")
+    ap.add_argument("--options", default="",
+                    help="plan options to pin, as JSON (e.g. '{\"kernel\": 3, \"ranges_per_xcd\": 8}')")
     ap.add_argument("--col-major", action="store_true",
                     help="BCSR 64x64: B and C column-major (B^T: N x k, C^T: N x m), the "
                          "token-major activation layout")
@@ -595,9 +601,12 @@ def main():
     print("bench: generating config %d" % args.config, file=sys.stderr, flush=True)
     p, workload = make_problem(args.config, args)
     print("bench: building format and plan", file=sys.stderr, flush=True)
+    opts = json.loads(args.options) if args.options else {}
+    if args.col_major:
+        opts["col_major"] = 1
     A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
                         p.ab_dtype, p.c_dtype, device=dev, split_cols=args.split,
-                        options={"col_major": 1} if args.col_major else None)
+                        options=opts or None)
     info = A.plan.info()
     if args.col_major:
         # B^T (N x k) and C^T (N x m), rows padded like the row-major operands
@@ -648,11 +657,12 @@ def main():
         "dtype": p.ab_dtype,
         "data": "synthetic (seeded; no dataset)",
         "config": {"workload": workload, "format": p.fmt, "m": p.m, "k": p.k, "N": p.N,
+                   "options": opts,
                    "ldb": int(B.stride(0)), "ldc": int(C.stride(0)),
                    "b_row": p.b_row, "b_col": p.b_col, "nnz": p.nnz,
                    "stored_entries": A.stored_entries, "c_dtype": p.c_dtype,
                    "plan": {k: info[k] for k in ("kernel", "tile_cols", "waves_n", "waves_k", "cols_per_lane",
-                                                 "split_cols", "n_tasks", "n_merges")}},
+                                                 "ranges_per_xcd", "split_cols", "n_tasks", "n_merges")}},
         "timing": "cold" if t_cold is not None else "warm",
         "tflops_true": value,
         "tflops_stored": alg["flops_stored"] / t_kernel / 1e12,
@@ -680,7 +690,8 @@ def main():
         del A, B, C
         torch.cuda.empty_cache()
         out["wcsr_cfg2"] = wcsr_extra(args, dev)
-    out["measured_peaks"] = measured_peaks()
+    if not args.no_peaks:
+        out["measured_peaks"] = measured_peaks()
     print(json.dumps(out), flush=True)
 
 

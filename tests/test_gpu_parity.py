@@ -780,3 +780,107 @@ def test_launch_floor_kernel_runs(ws):
     for _ in range(3):
         ws.launch_floor()
     torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# kernel 3: BCSR 64 x 64 with A in the registers of a wave pair
+# --------------------------------------------------------------------------
+
+def _short_rows_problem(m, k, N, ab, ct, seed, kind="normal", max_blocks=6):
+    """64 x 64 BCSR pattern whose block rows hold 0 .. max_blocks blocks (at
+    random, so empty rows and odd counts occur), every entry of a kept block
+    structural; ragged m and k cut the last block row and block column."""
+    from synth.generators import _block_rows_to_csr
+    g = np.random.default_rng(seed)
+    nbr, nbc = -(-m // 64), -(-k // 64)
+    sel = [np.sort(g.choice(nbc, int(g.integers(0, min(max_blocks, nbc) + 1)), replace=False))
+           for _ in range(nbr)]
+    sel[0] = np.arange(min(max_blocks, nbc))  # one full row
+    ptr, cols = _block_rows_to_csr(nbr, 64, 64, m, k, sel)
+    enc = synth.bf16_bits if ab == "bf16" else synth.fp16_bits
+    if kind == "int":
+        v = g.integers(1, 4, cols.size) * g.choice([-1, 1], cols.size)
+        b = g.integers(-2, 3, (k, N))
+    else:
+        v = g.normal(0.0, 1.0, cols.size)
+        v[v == 0] = 1.0
+        b = g.normal(0.0, 1.0, (k, N))
+    return synth.Problem("short_m%d_k%d_N%d_%s_%s_%s" % (m, k, N, ab, ct, kind), m, k, N,
+                         ptr.astype(np.int32), cols.astype(np.int32), enc(v.astype(np.float64)),
+                         np.ascontiguousarray(enc(b.astype(np.float64))), ab, ct, "bcsr", 64, 64)
+
+
+PAIR_CASES = [
+    # m, k, N, ab, c, ranges per XCD (0: the plan's)
+    (1000, 700, 1032, "bf16", "fp32", 0),
+    (640, 3584, 2048, "bf16", "bf16", 0),
+    (333, 1000, 1160, "fp16", "fp16", 1),
+    (700, 450, 4096, "fp16", "fp32", 16),
+    (129, 4000, 1024, "bf16", "bf16", 2),
+    (64, 64, 1024, "bf16", "fp32", 0),
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bcsr64_pair_kernel(ws, case):
+    """Kernel 3 on short block rows (0 to 6 blocks, so each wave of the pair
+    holds 0 to 3), ragged m, k and N (a partial last strip), every output type,
+    one to sixteen column ranges per XCD (sixteen: more ranges than strips, so
+    some work-groups have none)."""
+    m, k, N, ab, ct, h = case
+    p = _short_rows_problem(m, k, N, ab, ct, seed=m + N)
+    opts = {"kernel": 3}
+    if h:
+        opts["ranges_per_xcd"] = h
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options=opts)
+    assert A.plan.info()["kernel"] == 3
+    check(p, run_gpu(ws, p, A=A))
+
+
+def test_bcsr64_pair_kernel_integer_exact_padded_ld(ws):
+    """Kernel 3 on integer data (every partial sum exact in fp32) with B and C
+    rows padded beyond N: bit-equal to the oracle, and two launches agree."""
+    p = _short_rows_problem(500, 1300, 1096, "bf16", "fp32", seed=9, kind="int")
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"kernel": 3})
+    ld = p.N + 72
+    Bp = torch.full((p.k, ld), -1, dtype=torch.int16, device="cuda")
+    Bp[:, :p.N] = torch.from_numpy(p.B.view(np.int16)).cuda()
+    Cp = torch.full((p.m, ld), float("nan"), dtype=torch.float32, device="cuda")
+    outs = []
+    for _ in range(2):
+        Cp[:, :p.N].fill_(float("nan"))
+        A.run(Bp[:, :p.N], Cp[:, :p.N])
+        torch.cuda.synchronize()
+        outs.append(Cp[:, :p.N].cpu().numpy().astype(np.float64))
+    ref, _ = oracle.spmm(p.m, p.k, p.N, p.coo_rows(), p.col_idx, p.vals, p.B, p.ab_dtype)
+    assert np.array_equal(outs[0], ref) and np.array_equal(outs[1], ref)
+    assert torch.isnan(Cp[:, p.N:]).all(), "a store reached the row padding of C"
+
+
+@pytest.mark.parametrize("which", ["gate", "up"])
+def test_config4_pair_kernel_sampled(ws, which):
+    """Config 4 gate and up (6 blocks in every block row, N = 65536) through
+    kernel 3: every element written, sampled rows against the oracle."""
+    p = synth.config4(which)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"kernel": 3})
+    got = run_gpu(ws, p, A=A)
+    assert np.isfinite(got).all()
+    check(p, got, rows=_block_rows_sample(p, 11 if which == "gate" else 12))
+
+
+def test_pair_kernel_refused_where_it_cannot_run(ws):
+    """Kernel 3 holds at most 6 blocks per block row, 16-bit inputs, row-major
+    operands: other problems are refused with UNSUPPORTED."""
+    p = _short_rows_problem(256, 1024, 1024, "bf16", "fp32", seed=1, max_blocks=7)
+    nb = max(np.diff(ws.csr_to_bcsr(p.m, p.k, p.row_ptr, p.col_idx, p.vals, 64, 64)[0]))
+    if nb > 6:
+        with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):
+            ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, 64, 64,
+                            "bf16", "fp32", options={"kernel": 3})
+    q = _short_rows_problem(256, 1024, 1024, "bf16", "fp32", seed=2)
+    with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):
+        ws.DeviceSparse(q.fmt, q.m, q.k, q.N, q.row_ptr, q.col_idx, q.vals, 64, 64, "bf16", "fp32",
+                        options={"kernel": 3, "col_major": 1})

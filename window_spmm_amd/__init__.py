@@ -400,7 +400,7 @@ def _ld(t) -> int:
     return int(t.stride(0))
 
 
-def _run_checks(plan: Plan, B, C, workspace):
+def _run_checks(plan: Plan, B, C, workspace, check_workspace: bool = True):
     """Checks B, C and the workspace against the problem the plan was made for:
     shapes (k x N and m x N, or N x k and N x m for a column-major plan),
     element types, device, and the workspace size.  Raises ValueError; nothing
@@ -425,7 +425,7 @@ def _run_checks(plan: Plan, B, C, workspace):
             raise ValueError("%s has shape %s, the plan needs %s%s" % (
                 name, tuple(t.shape), want, " (column-major plan)" if cm else ""))
         _check_dtype(name, t, dt)
-    if plan.workspace_bytes > 0:
+    if check_workspace and plan.workspace_bytes > 0:
         if not _is_tensor(workspace):
             raise ValueError("the plan needs a workspace tensor of %d bytes" % plan.workspace_bytes)
         if not workspace.is_cuda or (pr["device"] is not None and
@@ -447,6 +447,7 @@ def wcsr_run(plan: Plan, B, C, workspace=None, stream=None):
     _run_checks(plan, B, C, workspace)
     _check(_lib.spmm_wcsr_run(plan.handle, _dp(B), _ld(B), _dp(C), _ld(C), _dp(workspace),
                               _stream_handle(stream)), "spmm_wcsr_run")
+
 
 
 # --------------------------------------------------------------------------

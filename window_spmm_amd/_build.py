@@ -25,7 +25,9 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-I", INCLU
 # kernels.hip: MFMA accumulators stay in ordinary VGPRs (the unified register
 # file of gfx950), which avoids copies around its two-waves-per-SIMD loops.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-HIP_SOURCES = [("kernels.hip", VGPR_FORM), ("api.hip", [])]
+# bcsr64_pair.hip runs one wave per SIMD with its accumulators in the
+# accumulation registers (its A fragments and B ring fill the VGPRs).
+HIP_SOURCES = [("kernels.hip", VGPR_FORM), ("bcsr64_pair.hip", []), ("api.hip", [])]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wextra"]
 
 

@@ -35,10 +35,11 @@ struct spmm_plan_s {
     int64_t stored_entries;
     int V, waves_n, waves_k;
     int kernel;                 // 0: generic tile kernel, 1: BCSR 64x64 with LDS-shared A,
-                                // 2: BCSR 64x64, A-stationary sweep over column ranges
+                                // 2: BCSR 64x64, A-stationary sweep over column ranges,
+                                // 3: BCSR 64x64, A in the registers of a wave pair
     int max_blocks;             // kernel 2: most blocks in a block row (LDS size)
     spmm_plan_options_t opt;    // the caller's choices (auto fields: the plan's)
-    int64_t n_ranges, range_tiles;  // kernel 2: column ranges (multiple of 8), tiles each
+    int64_t n_ranges, range_tiles;  // kernels 2, 3: column ranges (multiple of 8), tiles each
     int64_t tile_cols, n_col_tiles;
     size_t workspace;
     int device;
@@ -54,7 +55,7 @@ constexpr uint64_t kMaxBBytes = 0xFFFFFF00ull;
 // Range checks of plan options that do not depend on the matrix.
 spmm_status_t check_options(const spmm_plan_options_t &o, bool bcsr)
 {
-    if (o.kernel < -1 || o.kernel > 2 || (!bcsr && o.kernel > 0))
+    if (o.kernel < -1 || o.kernel > 3 || (!bcsr && o.kernel > 0))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "options.kernel %d is not a kernel of this format",
                     o.kernel);
     if (o.cols_per_lane != 0 && o.cols_per_lane != 2 && o.cols_per_lane != 4 && o.cols_per_lane != 8)
@@ -246,7 +247,7 @@ spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int
     // 32-bit store offsets must stay past the end of C^T without wrapping)
     if (cm && (uint64_t)(pl->N + 1024) * (uint64_t)ldc * esz >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "C^T ((N + 1024) * ldc * element bytes) must be below 4 GiB - 256");
-    if ((pl->kernel == 0 || pl->kernel == 1 || pl->kernel == 2) &&
+    if ((pl->kernel >= 0 && pl->kernel <= 3) &&
         (uint64_t)pl->b_row * (uint64_t)ldc * (pl->ct == SPMM_FP32 ? 4u : 2u) >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "b_row rows of C (b_row * ldc * element bytes) must be below 4 GiB");
     if (pl->workspace > 0 && (!ws || ((uintptr_t)ws & 15)))
@@ -308,7 +309,8 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.grid = pl->grid;
     p.n_ranges = pl->n_ranges;
     p.range_tiles = pl->range_tiles;
-    hipError_t e = pl->kernel == 2   ? launch_bcsr64_sweep(pl->ab, pl->max_blocks, p, st)
+    hipError_t e = pl->kernel == 3   ? launch_bcsr64_pair(pl->ab, p, st)
+                   : pl->kernel == 2 ? launch_bcsr64_sweep(pl->ab, pl->max_blocks, p, st)
                    : pl->kernel == 1 ? launch_bcsr64_lds(pl->ab, p, st)
                                      : launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, st);
     if (e != hipSuccess)
@@ -707,6 +709,12 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
                             sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks),
                                                 opt.col_major != 0, sweep_v) >= 2;
     const bool sweep_auto = sweep_fits && tiles512 >= 16;
+    // Kernel 3 holds a block row's A in the registers of two waves: at most
+    // kPairMaxBlocks blocks per block row, 16-bit inputs, row-major operands,
+    // two resident work-groups per CU.
+    const bool pair_fits = b64 && max_blocks <= kPairMaxBlocks && N >= 1024 && !opt.col_major &&
+                           (ab_dtype == SPMM_FP16 || ab_dtype == SPMM_BF16) &&
+                           pair_blocks_per_cu(ab_dtype) >= 2;
     if (ab_dtype == SPMM_FP8_E4M3 &&
         (!sweep_fits || opt.col_major || (opt.kernel != -1 && opt.kernel != 2))) {
         free_plan(pl);
@@ -722,14 +730,35 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
     }
     pl->kernel = opt.kernel >= 0 ? opt.kernel
                  : sweep_auto || ab_dtype == SPMM_FP8_E4M3 ? 2 : lds_ok ? 1 : 0;
-    if ((pl->kernel == 1 && !lds_ok) || (pl->kernel == 2 && !sweep_fits)) {
+    if ((pl->kernel == 1 && !lds_ok) || (pl->kernel == 2 && !sweep_fits) ||
+        (pl->kernel == 3 && !pair_fits)) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED,
                     "kernel %d cannot run this problem (b_row %d, b_col %d, N %lld, %d blocks in "
                     "the longest block row)",
                     opt.kernel, b_row, b_col, (long long)N, max_blocks);
     }
-    if (pl->kernel == 2) {
+    if (pl->kernel == 3) {
+        if (opt.cols_per_lane != 0 && opt.cols_per_lane != 8) {
+            free_plan(pl);
+            return fail(SPMM_ERR_UNSUPPORTED, "kernel 3 runs 8 columns per lane");
+        }
+        pl->n_items = nbr;
+        pl->V = 8;
+        pl->waves_n = 1;
+        pl->waves_k = 2;
+        pl->tile_cols = 128;
+        pl->n_col_tiles = ceil_div(N, 128);
+        pl->workspace = 0;
+        pl->order = 0;
+        // ranges of eight 128-column strips by default (a block row's A is
+        // loaded once per range)
+        const int64_t h = opt.ranges_per_xcd > 0
+                              ? opt.ranges_per_xcd
+                              : std::max<int64_t>(1, std::min<int64_t>(64, pl->n_col_tiles / 64));
+        pl->n_ranges = 8 * h;
+        pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
+    } else if (pl->kernel == 2) {
         // column-major: 4 columns per lane (a whole block of B^T per ring stage)
         if (opt.cols_per_lane != 0 && opt.cols_per_lane != sweep_v) {
             free_plan(pl);
@@ -782,7 +811,7 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
             return s;
         }
     }
-    if (pl->n_items * (pl->kernel == 2 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
+    if (pl->n_items * (pl->kernel >= 2 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
     }
@@ -851,7 +880,7 @@ extern "C" spmm_status_t spmm_wcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         free_plan(pl);
         return s;
     }
-    if (pl->n_items * (pl->kernel == 2 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
+    if (pl->n_items * (pl->kernel >= 2 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");
     }
@@ -884,7 +913,7 @@ extern "C" spmm_status_t spmm_plan_info(spmm_plan_t pl, spmm_plan_info_t *info)
     info->waves_k = pl->waves_k;
     info->cols_per_lane = pl->V;
     info->kernel = pl->kernel;
-    info->ranges_per_xcd = pl->kernel == 2 ? (int32_t)(pl->n_ranges / 8) : 0;
+    info->ranges_per_xcd = pl->kernel >= 2 ? (int32_t)(pl->n_ranges / 8) : 0;
     info->col_major = pl->opt.col_major;
     info->split_cols = pl->kernel == 0 ? pl->split_cols : 0;
     info->n_tasks = pl->kernel == 0 ? pl->n_tasks : 0;

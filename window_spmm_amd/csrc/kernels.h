@@ -77,5 +77,14 @@ hipError_t launch_bcsr64_sweep(int ab_dtype, int max_blocks, const TileParams &p
 size_t sweep_lds_bytes(int max_blocks, int ab_dtype);
 // Work-groups of the sweep kernel resident per CU (0 if the query fails).
 int sweep_blocks_per_cu(int ab_dtype, int max_blocks, bool col_major, int cols_per_lane);
+// Most blocks in a block row that the pair kernel holds in registers.
+constexpr int kPairMaxBlocks = 6;
+// BCSR with 64x64 blocks, A in the registers of a wave pair: n_items block rows x
+// n_ranges column ranges of range_tiles strips of 128 columns (p.tile_cols =
+// 128), two waves per work-group (FP16/BF16, row-major B and C).
+hipError_t launch_bcsr64_pair(int ab_dtype, const TileParams &p, hipStream_t stream);
+size_t pair_lds_bytes();
+// Work-groups of the pair kernel resident per CU (0 if the query fails).
+int pair_blocks_per_cu(int ab_dtype);
 
 }  // namespace wspmm
