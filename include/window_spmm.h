@@ -305,6 +305,24 @@ spmm_status_t spmm_bcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void
 spmm_status_t spmm_wcsr_run(spmm_plan_t plan, const void *d_B, int64_t ldb, void *d_C, int64_t ldc,
                             void *d_workspace, void *stream);
 
+/* The WCSR run for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and result as spmm_wcsr_run, but the fp32 partial tiles of split
+ * windows go into a static device array of the library,
+ * SPMM_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, instead of a workspace.  The call
+ * allocates and frees nothing; the caller still passes B and C as for
+ * spmm_wcsr_run, with the same requirements.  UNSUPPORTED if the plan's
+ * workspace_bytes exceeds SPMM_NOALLOC_SCRATCH_BYTES (a larger split size
+ * shrinks it).  Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (different streams, or a run still executing) race and
+ * give wrong results; serialise them or use spmm_wcsr_run with a workspace each.
+ * The array keeps the last call's contents; nothing needs clearing (every
+ * partial slot a run reads is written earlier in the same run).  The first call
+ * on a device looks up the array's address on that device. */
+#define SPMM_NOALLOC_SCRATCH_BYTES (32u << 20)
+spmm_status_t spmm_wcsr_run_noalloc(spmm_plan_t plan, const void *d_B, int64_t ldb, void *d_C,
+                                    int64_t ldc, void *stream);
+
 spmm_status_t spmm_plan_info(spmm_plan_t plan, spmm_plan_info_t *info);
 
 /* Leading dimension (elements) to allocate for a dense operand with N columns of

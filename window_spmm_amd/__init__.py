@@ -38,8 +38,10 @@ EXPORTED = [
     "spmm_bcsr_run", "spmm_wcsr_run", "spmm_plan_info", "spmm_plan_destroy",
     "spmm_status_string", "spmm_last_error", "spmm_recommended_ld", "spmm_rcm_order",
     "spmm_csr_permute", "spmm_plan_options_default", "spmm_bcsr_plan_ex", "spmm_wcsr_plan_ex",
-    "spmm_launch_floor",
+    "spmm_launch_floor", "spmm_wcsr_run_noalloc",
 ]
+# bytes of the library's static partial-tile scratch (SPMM_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class PlanInfo(ctypes.Structure):
@@ -101,6 +103,7 @@ _sigs = {
                           ctypes.c_int, ctypes.c_int, _i64, ctypes.POINTER(PlanOptions), _Psz],
     "spmm_bcsr_run": [_vp, _vp, _i64, _vp, _i64, _vp, _vp],
     "spmm_wcsr_run": [_vp, _vp, _i64, _vp, _i64, _vp, _vp],
+    "spmm_wcsr_run_noalloc": [_vp, _vp, _i64, _vp, _i64, _vp],
     "spmm_plan_info": [_vp, ctypes.POINTER(PlanInfo)],
     "spmm_plan_destroy": [_vp],
     "spmm_launch_floor": [_vp],
@@ -448,6 +451,14 @@ def wcsr_run(plan: Plan, B, C, workspace=None, stream=None):
     _check(_lib.spmm_wcsr_run(plan.handle, _dp(B), _ld(B), _dp(C), _ld(C), _dp(workspace),
                               _stream_handle(stream)), "spmm_wcsr_run")
 
+
+def wcsr_run_noalloc(plan: Plan, B, C, stream=None):
+    """spmm_wcsr_run_noalloc: the WCSR run with the library's static partial-tile
+    scratch instead of a workspace (allocates nothing; runs on one GPU must not
+    overlap)."""
+    _run_checks(plan, B, C, None, check_workspace=False)
+    _check(_lib.spmm_wcsr_run_noalloc(plan.handle, _dp(B), _ld(B), _dp(C), _ld(C),
+                                      _stream_handle(stream)), "spmm_wcsr_run_noalloc")
 
 
 # --------------------------------------------------------------------------

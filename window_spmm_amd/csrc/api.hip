@@ -5,6 +5,7 @@
 #include <cstdlib>
 #include <functional>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <queue>
 #include <vector>
@@ -899,6 +900,68 @@ extern "C" spmm_status_t spmm_wcsr_run(spmm_plan_t plan, const void *d_B, int64_
                                        int64_t ldc, void *d_workspace, void *stream)
 {
     return run_plan(plan, 1, d_B, ldb, d_C, ldc, d_workspace, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The run that allocates nothing: the fp32 partial tiles of split windows go
+// into this file's static device array instead of a caller-supplied
+// workspace.  Each GPU the library runs on holds its own copy of the array
+// until the process ends; host code never passes the array's name to a
+// kernel (in host code it only stands in for the symbol), but the device
+// address looked up once per device.
+namespace {
+constexpr size_t kScratchBytes = SPMM_NOALLOC_SCRATCH_BYTES;  // per GPU
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_address[kMaxDevices];               // per device, null until looked up
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+// Device address of `scratch` on device dev (which must be current).
+spmm_status_t scratch_address(int dev, void **out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SPMM_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                    kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_address[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(SPMM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_address[dev] = ptr;
+    }
+    *out = g_scratch_address[dev];
+    return SPMM_OK;
+}
+}  // namespace
+
+extern "C" spmm_status_t spmm_wcsr_run_noalloc(spmm_plan_t plan, const void *d_B, int64_t ldb,
+                                               void *d_C, int64_t ldc, void *stream)
+{
+    if (!plan)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "null plan");
+    if (plan->fmt != 1)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "spmm_wcsr_run_noalloc takes a WCSR plan");
+    if (plan->workspace > kScratchBytes)
+        return fail(SPMM_ERR_UNSUPPORTED,
+                    "the plan needs %zu bytes of partial tiles; the static scratch holds %zu "
+                    "(use spmm_wcsr_run with a workspace, or a plan with a larger split size)",
+                    plan->workspace, kScratchBytes);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "plan was made on device %d, current is %d",
+                    plan->device, dev);
+    void *ws = nullptr;
+    if (plan->workspace > 0 && plan->m > 0 && plan->N > 0) {
+        const spmm_status_t s = scratch_address(dev, &ws);
+        if (s != SPMM_OK)
+            return s;
+    }
+    return run_plan(plan, 1, d_B, ldb, d_C, ldc, ws, stream);
 }
 
 extern "C" spmm_status_t spmm_plan_info(spmm_plan_t pl, spmm_plan_info_t *info)
