@@ -177,6 +177,7 @@ def sweep_candidates(p):
         cands += [{"kernel": 2, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16)]
         cands += [{"kernel": 2, "cols_per_lane": 4, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16)]
         cands += [{"kernel": 3, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16, 32)]
+        cands += [{"kernel": 4, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16, 32)]
     for V in (2, 4, 8):
         if V == 8 and p.b_row >= 32:
             continue
@@ -396,7 +397,7 @@ def roofline_of(p, alg, t, info, key):
 
 
 KERNEL_NAMES = {0: "spmm_tile_kernel", 1: "bcsr64_lds_kernel", 2: "bcsr64_sweep_kernel",
-                3: "bcsr64_pair_kernel"}
+                3: "bcsr64_pair_kernel", 4: "bcsr64_group_kernel"}
 
 
 def wcsr_extra(args, dev):

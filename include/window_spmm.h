@@ -60,8 +60,9 @@ typedef struct {
     int32_t cols_per_lane;   /* adjacent C columns each lane accumulates (V) */
     int32_t kernel;          /* 0: generic tile kernel; 1: BCSR 64x64 kernel with LDS-shared A;
                                 2: BCSR 64x64 A-stationary sweep kernel;
-                                3: BCSR 64x64 with A in the registers of a wave pair */
-    int32_t ranges_per_xcd;  /* kernels 2, 3: column ranges per XCD (0 otherwise) */
+                                3: BCSR 64x64 with A in the registers of a wave pair;
+                                4: BCSR 64x64, groups of 4 block rows sharing B tiles */
+    int32_t ranges_per_xcd;  /* kernels 2, 3, 4: column ranges per XCD (0 otherwise) */
     int32_t col_major;       /* 1 if the plan takes B^T and C^T (spmm_plan_options_t) */
     int32_t reserved;
     int64_t split_cols;      /* sub-task size T in packed columns (0: whole block rows) */
@@ -201,7 +202,12 @@ typedef struct {
                                 3 BCSR 64x64 with each block row's A in the registers of
                                   two waves, 128-column strips (b_row = b_col = 64,
                                   N >= 1024, at most 6 blocks in every block row, FP16 or
-                                  BF16, row-major) */
+                                  BF16, row-major);
+                                4 BCSR 64x64, block rows grouped four at a time by shared
+                                  block columns, each group's B tiles staged once through
+                                  an LDS ring and used by every row of the group that
+                                  holds them (same limits as 3; 64-column strips, so
+                                  cols_per_lane 0 or 4) */
     int32_t cols_per_lane;   /* 0 auto; kernel 0: 2, 4 or 8 adjacent C columns per lane
                                 (8 only with b_row = 16); kernel 2: 8 (512-column tiles,
                                 the default) or 4 (256-column tiles; FP16/BF16 only, and
@@ -216,7 +222,7 @@ typedef struct {
                                 first, 1 row order with a contiguous range per XCD */
     int32_t order;           /* -1 auto; kernel 1: 0 column-tile major with a contiguous
                                 range per XCD, 1 launch order */
-    int32_t ranges_per_xcd;  /* 0 auto; kernels 2 and 3: column ranges per XCD, 1 to 64 */
+    int32_t ranges_per_xcd;  /* 0 auto; kernels 2, 3 and 4: column ranges per XCD, 1 to 64 */
     int32_t col_major;       /* 0: B is k x N and C is m x N, row-major (the default);
                                 1: column-major, the layout of activations stored token by
                                 token: d_B holds B^T (N rows of k, leading dimension ldb >= k)

@@ -107,7 +107,7 @@ def test_plan_options_default_and_checks():
     ws._lib.spmm_plan_options_default(ctypes.byref(o))
     assert {n: getattr(o, n) for n, _ in o._fields_} == ws.PlanOptions.AUTO
     rp = np.array([0, 1], np.int32)
-    bad = [{"kernel": 4}, {"kernel": -2}, {"cols_per_lane": 3}, {"waves_n": 3},
+    bad = [{"kernel": 5}, {"kernel": -2}, {"cols_per_lane": 3}, {"waves_n": 3},
            {"waves_n": 4, "waves_k": 2}, {"distribution": 2}, {"order": -3},
            {"ranges_per_xcd": 65}, {"row_order": 5}]
     for opts in bad:

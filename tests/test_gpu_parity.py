@@ -884,3 +884,60 @@ def test_pair_kernel_refused_where_it_cannot_run(ws):
     with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):
         ws.DeviceSparse(q.fmt, q.m, q.k, q.N, q.row_ptr, q.col_idx, q.vals, 64, 64, "bf16", "fp32",
                         options={"kernel": 3, "col_major": 1})
+
+
+# --------------------------------------------------------------------------
+# kernel 4: groups of block rows sharing B tiles through an LDS ring
+# --------------------------------------------------------------------------
+
+GROUP_CASES = [
+    # m, k, N, ab, c, ranges per XCD (0: the plan's)
+    (64, 64, 1024, "bf16", "fp32", 0),
+    (1000, 700, 1032, "bf16", "fp32", 0),
+    (640, 3584, 2048, "bf16", "bf16", 0),
+    (333, 1000, 1160, "fp16", "fp16", 1),
+    (700, 450, 4096, "fp16", "fp32", 16),
+    (129, 4000, 1024, "bf16", "bf16", 2),
+    (2000, 1500, 1096, "bf16", "fp32", 4),
+]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bcsr64_group_kernel(ws, case):
+    """Kernel 4 on short block rows (0 to 6 blocks: empty rows, groups whose
+    rows share several, one or no block columns, a last group with fewer than
+    four rows), ragged m, k and N (a partial last 64-column strip), every output
+    type, one to sixteen column ranges per XCD."""
+    m, k, N, ab, ct, h = case
+    p = _short_rows_problem(m, k, N, ab, ct, seed=m + N + 1)
+    opts = {"kernel": 4}
+    if h:
+        opts["ranges_per_xcd"] = h
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options=opts)
+    assert A.plan.info()["kernel"] == 4
+    check(p, run_gpu(ws, p, A=A))
+
+
+def test_bcsr64_group_kernel_integer_exact_repeated(ws):
+    """Kernel 4 on integer data: bit-equal to the oracle on three launches in a
+    row (the ring's items must reach every consumer intact every time)."""
+    p = _short_rows_problem(1280, 2600, 2048, "bf16", "fp32", seed=19, kind="int")
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"kernel": 4})
+    outs = run_gpu(ws, p, A=A, repeats=3)
+    ref, _ = oracle.spmm(p.m, p.k, p.N, p.coo_rows(), p.col_idx, p.vals, p.B, p.ab_dtype)
+    for got in outs:
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("which", ["gate", "up"])
+def test_config4_group_kernel_sampled(ws, which):
+    """Config 4 gate and up through kernel 4 at N = 65536: every element
+    written, sampled rows against the oracle."""
+    p = synth.config4(which)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"kernel": 4})
+    got = run_gpu(ws, p, A=A)
+    assert np.isfinite(got).all()
+    check(p, got, rows=_block_rows_sample(p, 21 if which == "gate" else 22))

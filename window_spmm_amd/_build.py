@@ -27,7 +27,8 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-I", INCLU
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 # bcsr64_pair.hip runs one wave per SIMD with its accumulators in the
 # accumulation registers (its A fragments and B ring fill the VGPRs).
-HIP_SOURCES = [("kernels.hip", VGPR_FORM), ("bcsr64_pair.hip", []), ("api.hip", [])]
+HIP_SOURCES = [("kernels.hip", VGPR_FORM), ("bcsr64_pair.hip", []), ("bcsr64_group.hip", []),
+               ("api.hip", [])]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wextra"]
 
 

@@ -26,6 +26,7 @@ struct spmm_plan_s {
     bool two_buffers;           // work-groups run several entries (TileParams::two_buffers)
     int64_t n_entries;          // entries of d_tasks
     int32_t *d_merges;          // (row tile, first_slot, n_slots)
+    int32_t *d_groups;          // kernel 4: group tables (kGroupTableInts ints each)
     int64_t n_items;            // work items per column tile: block rows (LDS kernel)
                                 // or task-table entries, padding included (tile kernel)
     int64_t n_tasks;            // tasks without the padding
@@ -56,7 +57,7 @@ constexpr uint64_t kMaxBBytes = 0xFFFFFF00ull;
 // Range checks of plan options that do not depend on the matrix.
 spmm_status_t check_options(const spmm_plan_options_t &o, bool bcsr)
 {
-    if (o.kernel < -1 || o.kernel > 3 || (!bcsr && o.kernel > 0))
+    if (o.kernel < -1 || o.kernel > 4 || (!bcsr && o.kernel > 0))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "options.kernel %d is not a kernel of this format",
                     o.kernel);
     if (o.cols_per_lane != 0 && o.cols_per_lane != 2 && o.cols_per_lane != 4 && o.cols_per_lane != 8)
@@ -218,6 +219,7 @@ void free_plan(spmm_plan_s *pl)
     if (pl->d_tasks) (void)hipFree(pl->d_tasks);
     if (pl->d_lists) (void)hipFree(pl->d_lists);
     if (pl->d_merges) (void)hipFree(pl->d_merges);
+    if (pl->d_groups) (void)hipFree(pl->d_groups);
     delete pl;
 }
 
@@ -310,7 +312,8 @@ spmm_status_t run_plan(spmm_plan_t pl, int fmt, const void *B, int64_t ldb, void
     p.grid = pl->grid;
     p.n_ranges = pl->n_ranges;
     p.range_tiles = pl->range_tiles;
-    hipError_t e = pl->kernel == 3   ? launch_bcsr64_pair(pl->ab, p, st)
+    hipError_t e = pl->kernel == 4   ? launch_bcsr64_group(pl->ab, p, pl->d_groups, st)
+                   : pl->kernel == 3 ? launch_bcsr64_pair(pl->ab, p, st)
                    : pl->kernel == 2 ? launch_bcsr64_sweep(pl->ab, pl->max_blocks, p, st)
                    : pl->kernel == 1 ? launch_bcsr64_lds(pl->ab, p, st)
                                      : launch_tiles(fmt, pl->b_row, pl->V, pl->ab, p, st);
@@ -608,6 +611,110 @@ spmm_status_t plan_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
     return make_tasks(pl, n_rows, start, split_cols, shift, n_cu, spread, local != 0);
 }
 
+// Kernel 4's groups: block rows taken kGroupRows at a time, greedily by shared
+// block columns -- a group starts from the lowest-numbered block row not yet
+// placed and adds, one at a time, the unplaced block row sharing the most block
+// columns with the group's union so far (ties: the lowest-numbered; a row
+// sharing none when no row shares any) -- so that a group's rows need few
+// distinct B tiles.  Reads the block-column indices back from the device (a
+// synchronous copy).  Fills and uploads the group tables (see kernels.h).
+spmm_status_t plan_groups(spmm_plan_s *pl, int64_t nbr, const int32_t *h_ptr, const int32_t *d_idx)
+{
+    try {
+        alloc_probe();
+        const int64_t nnzb = h_ptr[nbr];
+        std::vector<int32_t> cols((size_t)std::max<int64_t>(1, nnzb));
+        if (nnzb > 0) {
+            const hipError_t e =
+                hipMemcpy(cols.data(), d_idx, sizeof(int32_t) * (size_t)nnzb, hipMemcpyDeviceToHost);
+            if (e != hipSuccess)
+                return hip_fail(e, "hipMemcpy of the block-column indices");
+        }
+        const int64_t nbc = ceil_div(pl->k, 64);
+        // rows holding each block column (block columns outside [0, k) are kept
+        // out of the union: their B rows read as zero and they share nothing)
+        std::vector<std::vector<int32_t>> by_col((size_t)std::max<int64_t>(1, nbc));
+        for (int64_t r = 0; r < nbr; ++r)
+            for (int32_t e = h_ptr[r]; e < h_ptr[r + 1]; ++e)
+                if (cols[e] >= 0 && cols[e] < nbc)
+                    by_col[cols[e]].push_back((int32_t)r);
+        std::vector<char> placed((size_t)nbr, 0);
+        std::vector<int32_t> overlap((size_t)nbr, 0), table;
+        int64_t next_seed = 0, n_groups = 0;
+        while (true) {
+            while (next_seed < nbr && placed[next_seed])
+                ++next_seed;
+            if (next_seed >= nbr)
+                break;
+            std::vector<int32_t> rows{(int32_t)next_seed};
+            placed[next_seed] = 1;
+            std::vector<int32_t> uni;
+            auto add_cols = [&](int32_t r) {
+                for (int32_t e = h_ptr[r]; e < h_ptr[r + 1]; ++e)
+                    if (cols[e] >= 0 && cols[e] < nbc &&
+                        std::find(uni.begin(), uni.end(), cols[e]) == uni.end())
+                        uni.push_back(cols[e]);
+            };
+            add_cols((int32_t)next_seed);
+            while ((int)rows.size() < kGroupRows) {
+                // overlap of every unplaced row with the union, through the by-column lists
+                std::vector<int32_t> touched;
+                for (int32_t c : uni)
+                    for (int32_t r : by_col[c])
+                        if (!placed[r]) {
+                            if (overlap[r]++ == 0)
+                                touched.push_back(r);
+                        }
+                int32_t best = -1;
+                for (int32_t r : touched)
+                    if (best < 0 || overlap[r] > overlap[best] || (overlap[r] == overlap[best] && r < best))
+                        best = r;
+                for (int32_t r : touched)
+                    overlap[r] = 0;
+                if (best < 0) {  // nothing shares a column: the next unplaced row
+                    int64_t r = next_seed;
+                    while (r < nbr && placed[r])
+                        ++r;
+                    if (r >= nbr)
+                        break;
+                    best = (int32_t)r;
+                }
+                placed[best] = 1;
+                rows.push_back(best);
+                add_cols(best);
+            }
+            std::sort(uni.begin(), uni.end());
+            std::vector<int32_t> t(kGroupTableInts, 0);
+            for (int w = 0; w < kGroupRows; ++w)
+                t[w] = w < (int)rows.size() ? rows[w] : -1;
+            t[kGroupRows] = (int32_t)uni.size();
+            const int maxu = kGroupRows * kGroupMaxBlocks;
+            for (size_t u = 0; u < uni.size(); ++u)
+                t[kGroupRows + 1 + u] = uni[u];
+            for (int w = 0; w < (int)rows.size(); ++w) {
+                int q = 0;
+                for (int32_t e = h_ptr[rows[w]]; e < h_ptr[rows[w] + 1]; ++e, ++q) {
+                    const int32_t c = cols[e];
+                    // a block column outside [0, k) contributes nothing: position -1,
+                    // the wave skips the block and is no consumer of any item
+                    int32_t u = -1;
+                    if (c >= 0 && c < nbc) {
+                        u = (int32_t)(std::lower_bound(uni.begin(), uni.end(), c) - uni.begin());
+                        t[kGroupRows + 1 + maxu + u] += 1;
+                    }
+                    t[kGroupRows + 1 + 2 * maxu + w * kGroupMaxBlocks + q] = u;
+                }
+            }
+            table.insert(table.end(), t.begin(), t.end());
+            ++n_groups;
+        }
+        pl->n_items = n_groups;
+        return upload(table.data(), (int64_t)table.size(), &pl->d_groups);
+    } catch (const std::bad_alloc &) {
+        return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+}
+
 spmm_plan_s *new_plan(int fmt, int64_t m, int64_t k, int64_t N, int32_t b_row, int32_t b_col,
                       spmm_dtype_t ab, spmm_dtype_t ct, const void *d_vals, const int32_t *d_idx,
                       int dev)
@@ -716,6 +823,11 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
     const bool pair_fits = b64 && max_blocks <= kPairMaxBlocks && N >= 1024 && !opt.col_major &&
                            (ab_dtype == SPMM_FP16 || ab_dtype == SPMM_BF16) &&
                            pair_blocks_per_cu(ab_dtype) >= 2;
+    // Kernel 4 groups block rows that share B tiles: at most kGroupMaxBlocks
+    // blocks per block row, 16-bit inputs, row-major operands.
+    const bool group_fits = b64 && max_blocks <= kGroupMaxBlocks && N >= 1024 && !opt.col_major &&
+                            (ab_dtype == SPMM_FP16 || ab_dtype == SPMM_BF16) &&
+                            group_blocks_per_cu(ab_dtype) >= 1;
     if (ab_dtype == SPMM_FP8_E4M3 &&
         (!sweep_fits || opt.col_major || (opt.kernel != -1 && opt.kernel != 2))) {
         free_plan(pl);
@@ -732,14 +844,37 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
     pl->kernel = opt.kernel >= 0 ? opt.kernel
                  : sweep_auto || ab_dtype == SPMM_FP8_E4M3 ? 2 : lds_ok ? 1 : 0;
     if ((pl->kernel == 1 && !lds_ok) || (pl->kernel == 2 && !sweep_fits) ||
-        (pl->kernel == 3 && !pair_fits)) {
+        (pl->kernel == 3 && !pair_fits) || (pl->kernel == 4 && !group_fits)) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED,
                     "kernel %d cannot run this problem (b_row %d, b_col %d, N %lld, %d blocks in "
                     "the longest block row)",
                     opt.kernel, b_row, b_col, (long long)N, max_blocks);
     }
-    if (pl->kernel == 3) {
+    if (pl->kernel == 4) {
+        if (opt.cols_per_lane != 0 && opt.cols_per_lane != 4) {
+            free_plan(pl);
+            return fail(SPMM_ERR_UNSUPPORTED, "kernel 4 runs 4 columns per lane");
+        }
+        if ((s = plan_groups(pl, nbr, h_block_row_ptr, d_block_col_idx)) != SPMM_OK) {
+            free_plan(pl);
+            return s;
+        }
+        pl->V = 4;
+        pl->waves_n = 1;
+        pl->waves_k = 1;
+        pl->tile_cols = 64;
+        pl->n_col_tiles = ceil_div(N, 64);
+        pl->workspace = 0;
+        pl->order = 0;
+        // ranges of sixteen 64-column strips by default (a block row's A is
+        // loaded once per range)
+        const int64_t h = opt.ranges_per_xcd > 0
+                              ? opt.ranges_per_xcd
+                              : std::max<int64_t>(1, std::min<int64_t>(64, pl->n_col_tiles / 128));
+        pl->n_ranges = 8 * h;
+        pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
+    } else if (pl->kernel == 3) {
         if (opt.cols_per_lane != 0 && opt.cols_per_lane != 8) {
             free_plan(pl);
             return fail(SPMM_ERR_UNSUPPORTED, "kernel 3 runs 8 columns per lane");

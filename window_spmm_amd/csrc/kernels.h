@@ -86,5 +86,19 @@ hipError_t launch_bcsr64_pair(int ab_dtype, const TileParams &p, hipStream_t str
 size_t pair_lds_bytes();
 // Work-groups of the pair kernel resident per CU (0 if the query fails).
 int pair_blocks_per_cu(int ab_dtype);
+// Kernel 4: groups of kGroupRows block rows (64x64 blocks, at most kGroupMaxBlocks
+// each) sharing B tiles through an LDS ring.  Group table (kGroupTableInts ints
+// per group): rows[kGroupRows] (-1: none), nU, U[kGroupRows * kGroupMaxBlocks]
+// (the union of the rows' block columns, increasing), cnt[same] (rows holding
+// each union column), pos[kGroupRows][kGroupMaxBlocks] (union position of each
+// row's q-th block).  p.n_items = groups, p.n_ranges ranges of p.range_tiles
+// strips of 64 columns (p.tile_cols = 64).
+constexpr int kGroupRows = 4;
+constexpr int kGroupMaxBlocks = 6;
+constexpr int kGroupTableInts = 80;
+hipError_t launch_bcsr64_group(int ab_dtype, const TileParams &p, const int32_t *gtab,
+                               hipStream_t stream);
+size_t group_lds_bytes();
+int group_blocks_per_cu(int ab_dtype);
 
 }  // namespace wspmm
