@@ -470,6 +470,30 @@ def roofline_time(p, alg):
     return max(alg["flops_stored"] / (peak * 1e12), alg["bytes_alg"] / (PEAK_HBM_GBS * 1e9))
 
 
+def tuned_pair(A, B, C, p, alg, args):
+    """A tuned plan (spmm_wcsr_plan_tuned on the run's own B and C) beside the
+    default plan: three rounds that time the default and the tuned plan in
+    turn, like the default timing, and the median of each."""
+    import torch
+    import window_spmm_amd as ws
+    tplan, chosen = ws.wcsr_plan_tuned(p.m, p.k, p.N, p.b_row, p.b_col, A.h_ptr, A.d_idx,
+                                       A.d_vals, B, C, p.ab_dtype, p.c_dtype)
+    nb = tplan.workspace_bytes
+    tws = torch.empty(max(1, (nb + 3) // 4), dtype=torch.float32, device=C.device) if nb else None
+    t_def, t_tun = [], []
+    for _ in range(3):
+        t_def.append(time_runs(A, B, C, args.steps, args.warmup)[0])
+        t_tun.append(time_calls(lambda st: ws.wcsr_run(tplan, B, C, tws, st), args.steps,
+                                args.warmup)[0])
+    td, tt = sorted(t_def)[1], sorted(t_tun)[1]
+    info = tplan.info()
+    tplan.destroy()
+    return {"us": tt * 1e6, "us_default": td * 1e6, "tflops_true": alg["flops_true"] / tt / 1e12,
+            "frac": roofline_time(p, alg) / tt, "frac_default": roofline_time(p, alg) / td,
+            "options": chosen, "kernel": info["kernel"], "tile_cols": info["tile_cols"],
+            "split_cols": info["split_cols"], "timed": info["tuned"]}
+
+
 def run_population(args):
     """Config 3 as the workload defines it: every matrix of the seeded WCSR
     population (32 matrices, m = k from 8K to 512K, banded and uniform, Zipf
@@ -505,17 +529,27 @@ def run_population(args):
             t, _ = time_runs(A, B, C, args.steps, args.warmup)
             alg = algorithmic(p, A)
             info = A.plan.info()
+            tuned = None
+            if args.tuned:
+                tuned = tuned_pair(A, B, C, p, alg, args)
             r = {"member": j, "m": p.m, "nnz": p.nnz, "banded": bool(p.meta["banded"]), "N": N,
                  "us": t * 1e6, "tflops_true": alg["flops_true"] / t / 1e12,
                  "frac": roofline_time(p, alg) / t, "t_roof_us": roofline_time(p, alg) * 1e6,
                  "frac_with_floor": min(1.0, (roofline_time(p, alg) + floor) / t),
                  "fill": p.nnz / A.stored_entries, "n_tasks": info["n_tasks"],
                  "n_merges": info["n_merges"]}
+            if tuned is not None:
+                r["tuned"] = tuned
             runs.append(r)
             print("bench:   N=%3d %9.1f us  %7.2f TFLOP/s  frac %.3f  (t_roof %.1f us, fill %.3f, "
                   "%d tasks, %d merges)" % (N, r["us"], r["tflops_true"], r["frac"], r["t_roof_us"],
                                             r["fill"], r["n_tasks"], r["n_merges"]),
                   file=sys.stderr, flush=True)
+            if tuned is not None:
+                print("bench:          tuned %9.1f us (default %.1f us, interleaved)  frac %.3f  "
+                      "%s split %d" % (tuned["us"], tuned["us_default"], tuned["frac"],
+                                       json.dumps(tuned["options"]), tuned["split_cols"]),
+                      file=sys.stderr, flush=True)
             del A, B, C
         del p256
         torch.cuda.empty_cache()
@@ -534,6 +568,18 @@ def run_population(args):
                          "geomean_frac": gm([r["frac"] for r in runs if r["N"] == N])}
                      for N in (32, 128, 256)},
            "detail": runs}
+    if args.tuned:
+        out["tuned"] = {
+            "how": "spmm_wcsr_plan_tuned per run (candidates timed on the run's own B and C); "
+                   "then three rounds timing the default and the tuned plan in turn, medians",
+            "geomean_tflops_true": gm([r["tuned"]["tflops_true"] for r in runs]),
+            "geomean_frac": gm([r["tuned"]["frac"] for r in runs]),
+            "geomean_frac_default_interleaved": gm([r["tuned"]["frac_default"] for r in runs]),
+            "geomean_speedup": gm([r["tuned"]["us_default"] / r["tuned"]["us"] for r in runs]),
+            "per_N": {N: {"geomean_frac": gm([r["tuned"]["frac"] for r in runs if r["N"] == N]),
+                          "geomean_frac_default_interleaved":
+                              gm([r["tuned"]["frac_default"] for r in runs if r["N"] == N])}
+                      for N in (32, 128, 256)}}
     print(json.dumps(out), flush=True)
 
 
@@ -554,6 +600,9 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="WCSR sub-task size (0 = plan's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--tuned", action="store_true",
+                    help="with --population: also tune each run's plan (spmm_wcsr_plan_tuned) "
+                         "and report it beside the default plan")
     ap.add_argument("--warm-only", action="store_true",
                     help="no cold-cache pass: value and roofline from warm launches")
     ap.add_argument("--no-peaks", action="store_true",

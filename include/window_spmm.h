@@ -64,7 +64,7 @@ typedef struct {
                                 4: BCSR 64x64, groups of 4 block rows sharing B tiles */
     int32_t ranges_per_xcd;  /* kernels 2, 3, 4: column ranges per XCD (0 otherwise) */
     int32_t col_major;       /* 1 if the plan takes B^T and C^T (spmm_plan_options_t) */
-    int32_t reserved;
+    int32_t tuned;           /* configurations timed to choose this plan (0: not a tuned plan) */
     int64_t split_cols;      /* sub-task size T in packed columns (0: whole block rows) */
     int64_t n_tasks;         /* tasks (= work-groups per column tile; 0: whole block rows) */
     int64_t n_merges;        /* row tiles split into more than one task */
@@ -288,6 +288,46 @@ spmm_status_t spmm_wcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t
                                 const int32_t *d_window_col_idx, const void *d_values,
                                 spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype, int64_t split_cols,
                                 const spmm_plan_options_t *options, size_t *workspace_bytes);
+
+/* Tuned plans.  The paper measures throughput against the tile width and keeps
+ * the best (Section IV-C, Fig. 7); the plans above choose with fixed rules from
+ * the problem's shape instead.  A tuned plan makes that measurement on the
+ * caller's operands: it makes the plan spmm_*_plan_ex would make with `options`,
+ * then a plan for every configuration from a fixed candidate list that keeps
+ * the fields `options` pins (the 64x64 block kernels with their range and tile
+ * variants, the generic kernel's columns per lane, wave splits and task
+ * distribution; for WCSR with split_cols = 0 also sub-task sizes 128, 512, 2048
+ * and 8192), times each on `stream` (two untimed runs, then `reps` runs between
+ * two events; reps = 0: about 2 ms of runs, at least 3 and at most 100), then
+ * times the three fastest three more times each, interleaved with the automatic
+ * plan, and returns the one with the lowest median if it is at least 2 % faster
+ * than the automatic plan's median (else the automatic plan; the sub-task sizes
+ * are a second such stage after the first).  Candidates no kernel can run are
+ * skipped.  Arguments as for
+ * spmm_*_plan_ex, plus the operands of the runs to time: d_B, ldb, d_C, ldc as
+ * for spmm_*_run (the same requirements, checked before anything is launched).
+ * d_C is overwritten: on return it holds the product from one of the timed
+ * plans; run the returned plan for the result.  chosen (may be NULL) receives
+ * the options the returned plan was made with (fields left automatic stay so;
+ * spmm_plan_info gives what the plan picked for them, and tuned = the number of
+ * configurations timed).  The call is blocking (it waits for the timed runs)
+ * and allocates a workspace for the candidates that need one, freed before it
+ * returns.  INVALID_ARGUMENT if reps is outside [0, 10000]; errors of the
+ * automatic plan or of a launch are returned as such. */
+spmm_status_t spmm_bcsr_plan_tuned(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
+                                   int32_t b_row, int32_t b_col, const int32_t *h_block_row_ptr,
+                                   const int32_t *d_block_col_idx, const void *d_blocks,
+                                   spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
+                                   const spmm_plan_options_t *options, const void *d_B, int64_t ldb,
+                                   void *d_C, int64_t ldc, void *stream, int32_t reps,
+                                   spmm_plan_options_t *chosen, size_t *workspace_bytes);
+spmm_status_t spmm_wcsr_plan_tuned(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
+                                   int32_t b_row, int32_t b_col, const int32_t *h_window_row_ptr,
+                                   const int32_t *d_window_col_idx, const void *d_values,
+                                   spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype, int64_t split_cols,
+                                   const spmm_plan_options_t *options, const void *d_B, int64_t ldb,
+                                   void *d_C, int64_t ldc, void *stream, int32_t reps,
+                                   spmm_plan_options_t *chosen, size_t *workspace_bytes);
 
 /* Run: C = A * B (the problem of Section II-C: A sparse m x k, B dense k x N),
  * computed by the kernels of Section III-A..III-C as chosen by the plan, fp32

@@ -149,3 +149,28 @@ def test_allocation_failure_hook_gives_out_of_memory(monkeypatch):
     monkeypatch.setenv("SPMM_TEST_FAIL_ALLOC", "0")
     for fn in calls.values():
         fn()
+
+
+def test_tuned_plan_argument_checks_without_gpu():
+    """The tuned plans check their own arguments before any device work: a null
+    plan pointer or reps outside [0, 10000] is INVALID_ARGUMENT; without a GPU
+    the automatic plan fails with a HIP error."""
+    import torch
+    ptr = np.array([0, 1], np.int32)
+    sz = ctypes.c_size_t(0)
+    h = ctypes.c_void_p(0)
+    opt = ws.PlanOptions.of(None)
+    args = (16, 64, 64, 16, 16, ptr.ctypes.data, 256, 256, 0, 2, ctypes.byref(opt), 512, 64, 1024, 64,
+            None)
+    assert ws._lib.spmm_bcsr_plan_tuned(None, *args, 0, None, ctypes.byref(sz)) == ws.ERR_INVALID_ARGUMENT
+    assert ws._lib.spmm_bcsr_plan_tuned(ctypes.byref(h), *args, -1, None, ctypes.byref(sz)) \
+        == ws.ERR_INVALID_ARGUMENT
+    assert "reps" in ws._lib.spmm_last_error().decode()
+    wptr = np.array([0, 8], np.int32)
+    wargs = (16, 64, 64, 16, 8, wptr.ctypes.data, 256, 256, 0, 2, 0, ctypes.byref(opt), 512, 64,
+             1024, 64, None)
+    assert ws._lib.spmm_wcsr_plan_tuned(ctypes.byref(h), *wargs, 20000, None, ctypes.byref(sz)) \
+        == ws.ERR_INVALID_ARGUMENT
+    if not torch.cuda.is_available():
+        assert ws._lib.spmm_bcsr_plan_tuned(ctypes.byref(h), *args, 0, None, ctypes.byref(sz)) == ws.ERR_HIP
+        assert not h.value

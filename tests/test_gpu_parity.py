@@ -941,3 +941,101 @@ def test_config4_group_kernel_sampled(ws, which):
     got = run_gpu(ws, p, A=A)
     assert np.isfinite(got).all()
     check(p, got, rows=_block_rows_sample(p, 21 if which == "gate" else 22))
+
+
+# --------------------------------------------------------------------------
+# tuned plans (the tile-width measurement of Section IV-C, Fig. 7, made per problem)
+# --------------------------------------------------------------------------
+
+def _tuned_case(ws, p, options=None, split_cols=0, rows=None):
+    """Tunes a plan on the problem's own B and C, runs it on a NaN-filled C and
+    checks the result against the oracle; the options it reports reproduce the
+    same configuration through the ordinary plan."""
+    _say("gpu case (tuned):", p.name, p.fmt, p.m, p.k, p.N, p.b_row, p.b_col, options)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, split_cols=split_cols, options=options)
+    B = _device_b(p)
+    C = A.new_c()
+    default = A.plan.info()
+    chosen = A.tune(B, C, reps=3, options=options)
+    info = A.plan.info()
+    _say("   default kernel %d tile %d -> tuned %s (kernel %d tile %d, %d timed)" % (
+        default["kernel"], default["tile_cols"], chosen, info["kernel"], info["tile_cols"],
+        info["tuned"]))
+    assert info["tuned"] >= 2
+    assert default["tuned"] == 0
+    C.fill_(float("nan"))
+    A.run(B, C)
+    torch.cuda.synchronize()
+    got = C.float().cpu().numpy().astype(np.float64)
+    check(p, got, rows=rows)
+    if info["split_cols"] in (0, default["split_cols"]):
+        A.replan(chosen)
+        again = A.plan.info()
+        for key in ("kernel", "tile_cols", "waves_n", "waves_k", "cols_per_lane", "ranges_per_xcd"):
+            assert again[key] == info[key], key
+    return info
+
+
+def test_tuned_plan_wcsr(ws):
+    p = synth.random_problem(1500, 2500, 136, 0.02, seed=61, ab_dtype="fp16", c_dtype="fp32",
+                             fmt="wcsr", b_row=16, b_col=8, empty_row_frac=0.1)
+    _tuned_case(ws, p)
+
+
+def test_tuned_plan_wcsr_pinned_fields_stay(ws):
+    p = synth.random_problem(700, 900, 72, 0.03, seed=62, ab_dtype="bf16", c_dtype="bf16",
+                             fmt="wcsr", b_row=16, b_col=8)
+    info = _tuned_case(ws, p, options={"cols_per_lane": 2}, split_cols=64)
+    assert info["cols_per_lane"] == 2 and info["split_cols"] == 64
+
+
+def test_tuned_plan_bcsr64_short_rows(ws):
+    p = _short_rows_problem(1000, 1500, 2048, "bf16", "fp32", seed=63)
+    _tuned_case(ws, p)
+
+
+def test_tuned_plan_bcsr_small_blocks(ws):
+    p = synth.block_problem(500, 400, 264, 32, 16, 0.3, seed=64, ab_dtype="fp16", c_dtype="bf16",
+                            entry_density=0.7)
+    _tuned_case(ws, p)
+
+
+def test_tuned_plan_col_major(ws):
+    """A column-major plan tunes among the kernels that take B^T and C^T."""
+    p = synth.block_problem(256, 320, 512, 64, 64, 0.3, seed=65, ab_dtype="bf16", c_dtype="fp32",
+                            entry_density=0.7)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"col_major": 1})
+    Bt = torch.from_numpy(np.ascontiguousarray(p.B.T).view(np.int16)).cuda()
+    Ct = torch.empty((p.N, p.m), dtype=torch.float32, device="cuda")
+    chosen = A.tune(Bt, Ct, reps=3, options={"col_major": 1})
+    info = A.plan.info()
+    assert chosen.get("col_major") == 1 and info["col_major"] == 1 and info["kernel"] in (1, 2)
+    Ct.fill_(float("nan"))
+    A.run(Bt, Ct)
+    torch.cuda.synchronize()
+    check(p, Ct.T.cpu().numpy().astype(np.float64))
+
+
+def test_tuned_plan_config3_member(ws):
+    """A population member (m = k = 32768 class, banded) at N = 128, tuned."""
+    p = synth.config3_matrix(4, 128)
+    _tuned_case(ws, p, rows=None if p.m <= CFG3_FULL_ROWS else _cfg3_rows(p, 4))
+
+
+def test_tuned_plan_refuses_bad_operands(ws):
+    p = synth.random_problem(200, 300, 64, 0.05, seed=66, ab_dtype="fp16", c_dtype="fp32",
+                             fmt="wcsr", b_row=16, b_col=8)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    B = _device_b(p)
+    with pytest.raises(ValueError, match="C has shape"):
+        A.tune(B, torch.empty((p.m, p.N + 8), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ws.SpmmError):
+        A.tune(B, A.new_c(), reps=-1)
+    # the object keeps a working plan after a refused tuning
+    C = A.new_c()
+    A.run(B, C)
+    torch.cuda.synchronize()
+    check(p, C.float().cpu().numpy().astype(np.float64))

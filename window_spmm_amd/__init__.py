@@ -38,7 +38,7 @@ EXPORTED = [
     "spmm_bcsr_run", "spmm_wcsr_run", "spmm_plan_info", "spmm_plan_destroy",
     "spmm_status_string", "spmm_last_error", "spmm_recommended_ld", "spmm_rcm_order",
     "spmm_csr_permute", "spmm_plan_options_default", "spmm_bcsr_plan_ex", "spmm_wcsr_plan_ex",
-    "spmm_launch_floor", "spmm_wcsr_run_noalloc",
+    "spmm_launch_floor", "spmm_wcsr_run_noalloc", "spmm_bcsr_plan_tuned", "spmm_wcsr_plan_tuned",
 ]
 # bytes of the library's static partial-tile scratch (SPMM_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -49,7 +49,7 @@ class PlanInfo(ctypes.Structure):
                 ("tile_cols", ctypes.c_int32), ("waves_n", ctypes.c_int32),
                 ("waves_k", ctypes.c_int32), ("cols_per_lane", ctypes.c_int32),
                 ("kernel", ctypes.c_int32), ("ranges_per_xcd", ctypes.c_int32),
-                ("col_major", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("col_major", ctypes.c_int32), ("tuned", ctypes.c_int32),
                 ("split_cols", ctypes.c_int64), ("n_tasks", ctypes.c_int64),
                 ("n_merges", ctypes.c_int64), ("n_slots", ctypes.c_int64),
                 ("stored_entries", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
@@ -101,6 +101,12 @@ _sigs = {
                           ctypes.c_int, ctypes.c_int, ctypes.POINTER(PlanOptions), _Psz],
     "spmm_wcsr_plan_ex": [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                           ctypes.c_int, ctypes.c_int, _i64, ctypes.POINTER(PlanOptions), _Psz],
+    "spmm_bcsr_plan_tuned": [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(PlanOptions), _vp, _i64,
+                             _vp, _i64, _vp, _i32, ctypes.POINTER(PlanOptions), _Psz],
+    "spmm_wcsr_plan_tuned": [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                             ctypes.c_int, ctypes.c_int, _i64, ctypes.POINTER(PlanOptions), _vp,
+                             _i64, _vp, _i64, _vp, _i32, ctypes.POINTER(PlanOptions), _Psz],
     "spmm_bcsr_run": [_vp, _vp, _i64, _vp, _i64, _vp, _vp],
     "spmm_wcsr_run": [_vp, _vp, _i64, _vp, _i64, _vp, _vp],
     "spmm_wcsr_run_noalloc": [_vp, _vp, _i64, _vp, _i64, _vp],
@@ -379,6 +385,53 @@ def wcsr_plan(m, k, N, b_row, b_col, h_window_row_ptr, d_window_col_idx, d_value
     return Plan(h, "wcsr", ws.value, (d_window_col_idx, d_values), prob)
 
 
+def _options_dict(o: PlanOptions) -> dict:
+    """The fields of `o` that are not automatic."""
+    return {name: getattr(o, name) for name, auto in PlanOptions.AUTO.items()
+            if getattr(o, name) != auto}
+
+
+def bcsr_plan_tuned(m, k, N, b_row, b_col, h_block_row_ptr, d_block_col_idx, d_blocks, B, C,
+                    ab_dtype="bf16", c_dtype="fp32", options=None, stream=None, reps=0):
+    """spmm_bcsr_plan_tuned: times the candidate configurations on B and C
+    (C is overwritten) and returns (plan, options it was made with)."""
+    rp = _host(h_block_row_ptr, np.int32)
+    prob = _plan_checks("bcsr", m, k, N, b_row, b_col, rp, d_block_col_idx, d_blocks, ab_dtype,
+                        c_dtype, options)
+    _run_checks(Plan(None, "bcsr", 0, (), prob), B, C, None, check_workspace=False)
+    h = ctypes.c_void_p(0)
+    ws = ctypes.c_size_t(0)
+    opt, chosen = PlanOptions.of(options), PlanOptions.of(None)
+    _check(_lib.spmm_bcsr_plan_tuned(ctypes.byref(h), m, k, N, b_row, b_col, _hp(rp),
+                                     _dp(d_block_col_idx), _dp(d_blocks), DTYPES[ab_dtype],
+                                     DTYPES[c_dtype], ctypes.byref(opt), _dp(B), _ld(B), _dp(C),
+                                     _ld(C), _stream_handle(stream), int(reps),
+                                     ctypes.byref(chosen), ctypes.byref(ws)),
+           "spmm_bcsr_plan_tuned")
+    return Plan(h, "bcsr", ws.value, (d_block_col_idx, d_blocks), prob), _options_dict(chosen)
+
+
+def wcsr_plan_tuned(m, k, N, b_row, b_col, h_window_row_ptr, d_window_col_idx, d_values, B, C,
+                    ab_dtype="fp16", c_dtype="fp32", split_cols=0, options=None, stream=None,
+                    reps=0):
+    """spmm_wcsr_plan_tuned: as bcsr_plan_tuned for WCSR (split_cols = 0 also
+    times sub-task sizes)."""
+    rp = _host(h_window_row_ptr, np.int32)
+    prob = _plan_checks("wcsr", m, k, N, b_row, b_col, rp, d_window_col_idx, d_values, ab_dtype,
+                        c_dtype, options)
+    _run_checks(Plan(None, "wcsr", 0, (), prob), B, C, None, check_workspace=False)
+    h = ctypes.c_void_p(0)
+    ws = ctypes.c_size_t(0)
+    opt, chosen = PlanOptions.of(options), PlanOptions.of(None)
+    _check(_lib.spmm_wcsr_plan_tuned(ctypes.byref(h), m, k, N, b_row, b_col, _hp(rp),
+                                     _dp(d_window_col_idx), _dp(d_values), DTYPES[ab_dtype],
+                                     DTYPES[c_dtype], int(split_cols), ctypes.byref(opt), _dp(B),
+                                     _ld(B), _dp(C), _ld(C), _stream_handle(stream), int(reps),
+                                     ctypes.byref(chosen), ctypes.byref(ws)),
+           "spmm_wcsr_plan_tuned")
+    return Plan(h, "wcsr", ws.value, (d_window_col_idx, d_values), prob), _options_dict(chosen)
+
+
 def _stream_handle(stream):
     if stream is None:
         import torch
@@ -516,6 +569,28 @@ class DeviceSparse:
                                      device=self.device) if nbytes else None
         self._ws_stream = None
         return self
+
+    def tune(self, B, C, stream=None, reps=0, options=None):
+        """Replaces the plan by a tuned one (spmm_*_plan_tuned, timed on B and C;
+        C is overwritten) and makes its workspace.  Returns the options the
+        tuned plan was made with."""
+        import torch
+        if self.fmt == "bcsr":
+            plan, chosen = bcsr_plan_tuned(self.m, self.k, self.N, self.b_row, self.b_col,
+                                           self.h_ptr, self.d_idx, self.d_vals, B, C,
+                                           self.ab_dtype, self.c_dtype, options, stream, reps)
+        else:
+            plan, chosen = wcsr_plan_tuned(self.m, self.k, self.N, self.b_row, self.b_col,
+                                           self.h_ptr, self.d_idx, self.d_vals, B, C,
+                                           self.ab_dtype, self.c_dtype, self.split_cols,
+                                           options, stream, reps)
+        self.plan.destroy()
+        self.plan = plan
+        nbytes = self.plan.workspace_bytes
+        self.workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32,
+                                     device=self.device) if nbytes else None
+        self._ws_stream = None
+        return chosen
 
     @property
     def stored_entries(self) -> int:

@@ -45,6 +45,7 @@ struct spmm_plan_s {
     int64_t tile_cols, n_col_tiles;
     size_t workspace;
     int device;
+    int n_tuned;                // configurations timed to choose this plan (0: not tuned)
 };
 
 namespace wspmm {
@@ -250,8 +251,7 @@ spmm_status_t check_run(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int
     // 32-bit store offsets must stay past the end of C^T without wrapping)
     if (cm && (uint64_t)(pl->N + 1024) * (uint64_t)ldc * esz >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "C^T ((N + 1024) * ldc * element bytes) must be below 4 GiB - 256");
-    if ((pl->kernel >= 0 && pl->kernel <= 3) &&
-        (uint64_t)pl->b_row * (uint64_t)ldc * (pl->ct == SPMM_FP32 ? 4u : 2u) >= kMaxBBytes)
+    if ((uint64_t)pl->b_row * (uint64_t)ldc * (pl->ct == SPMM_FP32 ? 4u : 2u) >= kMaxBBytes)
         return fail(SPMM_ERR_UNSUPPORTED, "b_row rows of C (b_row * ldc * element bytes) must be below 4 GiB");
     if (pl->workspace > 0 && (!ws || ((uintptr_t)ws & 15)))
         return fail(SPMM_ERR_INVALID_ARGUMENT, "plan needs a 16-byte aligned workspace of %zu bytes",
@@ -1038,6 +1038,356 @@ extern "C" spmm_status_t spmm_wcsr_run(spmm_plan_t plan, const void *d_B, int64_
 }
 
 // ---------------------------------------------------------------------------
+// Tuned plans.  The plan's own rules pick one configuration per problem from
+// its shape; the paper instead measures throughput against the tile width and
+// keeps the best one (Section IV-C, Fig. 7).  These entry points make that
+// measurement on the caller's operands: every configuration the caller's
+// options leave open is planned and timed on the caller's stream, and the
+// fastest plan is kept.
+namespace wspmm {
+namespace {
+
+// A candidate keeps every field the caller pinned; a candidate that pins a
+// field to another value than the caller's is dropped.
+bool merge_pinned(const spmm_plan_options_t &base, spmm_plan_options_t &o)
+{
+    auto field = [](int32_t b, int32_t &c, int32_t automatic) {
+        if (b == automatic)
+            return true;
+        if (c == automatic)
+            c = b;
+        return c == b;
+    };
+    return field(base.kernel, o.kernel, -1) && field(base.cols_per_lane, o.cols_per_lane, 0) &&
+           field(base.waves_n, o.waves_n, 0) && field(base.waves_k, o.waves_k, 0) &&
+           field(base.distribution, o.distribution, -1) && field(base.row_order, o.row_order, -1) &&
+           field(base.order, o.order, -1) && field(base.ranges_per_xcd, o.ranges_per_xcd, 0) &&
+           field(base.col_major, o.col_major, 0);
+}
+
+// The configurations to time after the automatic one: the 64 x 64 block
+// kernels' variants (BCSR with 64 x 64 blocks), then the generic kernel's tile
+// shapes (columns per lane x waves across the tile x waves along the packed
+// columns, with both ways of handing out tasks).  Configurations a kernel
+// cannot run are refused by the plan and skipped.
+std::vector<spmm_plan_options_t> tune_candidates(const spmm_plan_options_t &base, bool bcsr,
+                                                 int32_t b_row, int32_t b_col)
+{
+    std::vector<spmm_plan_options_t> out;
+    auto add = [&](spmm_plan_options_t o) {
+        if (!merge_pinned(base, o))
+            return;
+        for (const auto &x : out)
+            if (std::memcmp(&x, &o, sizeof(o)) == 0)
+                return;
+        out.push_back(o);
+    };
+    spmm_plan_options_t o;
+    if (bcsr && b_row == 64 && b_col == 64) {
+        for (int wn : {2, 4})
+            for (int ord : {0, 1}) {
+                spmm_plan_options_default(&o);
+                o.kernel = 1; o.waves_n = wn; o.order = ord;
+                add(o);
+            }
+        for (int cpl : {8, 4})
+            for (int h : {1, 2, 4, 8, 16}) {
+                spmm_plan_options_default(&o);
+                o.kernel = 2; o.cols_per_lane = cpl; o.ranges_per_xcd = h;
+                add(o);
+            }
+        for (int kern : {3, 4})
+            for (int h : {1, 2, 4, 8, 16, 32}) {
+                spmm_plan_options_default(&o);
+                o.kernel = kern; o.ranges_per_xcd = h;
+                add(o);
+            }
+    }
+    static const int kWaves[6][2] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {2, 2}, {4, 1}};
+    for (int V : {2, 4, 8}) {
+        if (V == 8 && b_row >= 32)
+            continue;
+        for (const auto &w : kWaves)
+            for (int dist : {0, 1}) {
+                spmm_plan_options_default(&o);
+                o.kernel = 0; o.cols_per_lane = V; o.waves_n = w[0]; o.waves_k = w[1];
+                o.distribution = dist;
+                add(o);
+            }
+    }
+    return out;
+}
+
+// Device memory and events of one tuning call, released on every return path.
+struct TuneState {
+    void *ws = nullptr;
+    size_t ws_cap = 0;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    ~TuneState()
+    {
+        if (ws) (void)hipFree(ws);
+        if (e0) (void)hipEventDestroy(e0);
+        if (e1) (void)hipEventDestroy(e1);
+    }
+    // a workspace of at least n bytes (grows, never shrinks)
+    spmm_status_t reserve(size_t n)
+    {
+        if (n <= ws_cap)
+            return SPMM_OK;
+        if (ws) (void)hipFree(ws);
+        ws = nullptr;
+        ws_cap = 0;
+        if (test_fail_alloc() || hipMalloc(&ws, n) != hipSuccess) {
+            ws = nullptr;
+            return fail(SPMM_ERR_OUT_OF_MEMORY, "tuning workspace of %zu bytes", n);
+        }
+        ws_cap = n;
+        return SPMM_OK;
+    }
+};
+
+// Mean time (us) of one run of `pl`: two untimed runs, then `reps` runs
+// between two events on the stream.
+spmm_status_t time_runs(spmm_plan_t pl, const void *B, int64_t ldb, void *C, int64_t ldc,
+                        TuneState &ts, void *stream, int reps, double *us)
+{
+    spmm_status_t s = ts.reserve(pl->workspace);
+    if (s != SPMM_OK)
+        return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    for (int i = 0; i < 2; ++i)
+        if ((s = run_plan(pl, pl->fmt, B, ldb, C, ldc, ts.ws, stream)) != SPMM_OK)
+            return s;
+    hipError_t e = hipEventRecord(ts.e0, st);
+    for (int i = 0; e == hipSuccess && i < reps; ++i)
+        if ((s = run_plan(pl, pl->fmt, B, ldb, C, ldc, ts.ws, stream)) != SPMM_OK)
+            return s;
+    if (e == hipSuccess)
+        e = hipEventRecord(ts.e1, st);
+    if (e == hipSuccess)
+        e = hipEventSynchronize(ts.e1);
+    float ms = 0.f;
+    if (e == hipSuccess)
+        e = hipEventElapsedTime(&ms, ts.e0, ts.e1);
+    if (e != hipSuccess)
+        return hip_fail(e, "timing a candidate plan");
+    *us = (double)ms * 1e3 / reps;
+    return SPMM_OK;
+}
+
+using PlanMaker = std::function<spmm_status_t(const spmm_plan_options_t &, int64_t, spmm_plan_t *)>;
+
+// A candidate replaces the incumbent only when it is this much faster, so that
+// timing noise does not trade the automatic plan for an equal one.
+constexpr double kTuneMargin = 0.02;
+// Candidates kept after the first timing, and rounds of the final comparison.
+constexpr int kTuneFinalists = 3;
+constexpr int kTuneRounds = 3;
+
+struct Timed {
+    spmm_plan_t plan;
+    spmm_plan_options_t opt;
+    double us;
+};
+
+// One selection stage: every candidate (options, split size) is planned and
+// timed once; the fastest kTuneFinalists are then timed again kTuneRounds
+// times, interleaved with the incumbent, and the one with the lowest median
+// replaces the incumbent if it is kTuneMargin faster.  Candidates no kernel
+// can run (UNSUPPORTED or INVALID_ARGUMENT from the plan) and candidates whose
+// workspace cannot be allocated are skipped; other errors end the stage.
+spmm_status_t select_plan(const PlanMaker &make,
+                          const std::vector<std::pair<spmm_plan_options_t, int64_t>> &cands,
+                          const void *B, int64_t ldb, void *C, int64_t ldc, TuneState &ts,
+                          void *stream, int n, Timed &inc, int *timed)
+{
+    std::vector<Timed> top;  // sorted by time, at most kTuneFinalists
+    auto release = [&]() {
+        for (auto &t : top)
+            free_plan(t.plan);
+        top.clear();
+    };
+    for (const auto &cand : cands) {
+        spmm_plan_t c = nullptr;
+        spmm_status_t r = make(cand.first, cand.second, &c);
+        if (r == SPMM_ERR_UNSUPPORTED || r == SPMM_ERR_INVALID_ARGUMENT)
+            continue;
+        if (r != SPMM_OK) {
+            release();
+            return r;
+        }
+        double us = 0.0;
+        r = time_runs(c, B, ldb, C, ldc, ts, stream, n, &us);
+        if (r != SPMM_OK) {
+            free_plan(c);
+            if (r == SPMM_ERR_OUT_OF_MEMORY)  // its workspace does not fit: not a candidate
+                continue;
+            release();
+            return r;
+        }
+        ++*timed;
+        top.push_back({c, cand.first, us});
+        std::sort(top.begin(), top.end(), [](const Timed &a, const Timed &b) { return a.us < b.us; });
+        if ((int)top.size() > kTuneFinalists) {
+            free_plan(top.back().plan);
+            top.pop_back();
+        }
+    }
+    if (top.empty())
+        return SPMM_OK;
+    // final rounds: incumbent and finalists in turn, median of the rounds
+    std::vector<std::vector<double>> t(top.size() + 1);
+    for (int round = 0; round < kTuneRounds; ++round)
+        for (size_t i = 0; i <= top.size(); ++i) {
+            double us = 0.0;
+            spmm_status_t r = time_runs(i == 0 ? inc.plan : top[i - 1].plan, B, ldb, C, ldc, ts,
+                                        stream, n, &us);
+            if (r != SPMM_OK) {
+                release();
+                return r;
+            }
+            t[i].push_back(us);
+        }
+    auto median = [](std::vector<double> v) {
+        std::sort(v.begin(), v.end());
+        return v[v.size() / 2];
+    };
+    inc.us = median(t[0]);
+    size_t best = 0;
+    double best_us = inc.us * (1.0 - kTuneMargin);
+    for (size_t i = 1; i <= top.size(); ++i) {
+        const double us = median(t[i]);
+        if (us < best_us) {
+            best = i;
+            best_us = us;
+        }
+    }
+    if (best > 0) {
+        free_plan(inc.plan);
+        inc = top[best - 1];
+        inc.us = best_us;
+        top[best - 1].plan = nullptr;
+    }
+    for (auto &x : top)
+        if (x.plan)
+            free_plan(x.plan);
+    top.clear();
+    return SPMM_OK;
+}
+
+spmm_status_t tune_plan(int fmt, int32_t b_row, int32_t b_col, const PlanMaker &make,
+                        const spmm_plan_options_t *options, int64_t split_cols, const void *B,
+                        int64_t ldb, void *C, int64_t ldc, void *stream, int32_t reps,
+                        spmm_plan_options_t *chosen, spmm_plan_t *plan, size_t *workspace_bytes)
+{
+    if (reps < 0 || reps > 10000)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "reps must be in [0, 10000]");
+    spmm_plan_options_t base;
+    spmm_plan_options_default(&base);
+    if (options)
+        base = *options;
+    Timed inc{nullptr, base, 0.0};
+    spmm_status_t s = make(base, split_cols, &inc.plan);
+    if (s != SPMM_OK)
+        return s;
+    // the operands must suit the plan before anything is launched (a stand-in
+    // workspace address: the tuner brings its own)
+    if ((s = check_run(inc.plan, B, ldb, C, ldc, inc.plan->workspace ? (void *)16 : nullptr)) !=
+        SPMM_OK) {
+        free_plan(inc.plan);
+        return s;
+    }
+    auto done = [&](spmm_status_t st, int timed) {
+        if (st != SPMM_OK) {
+            free_plan(inc.plan);
+            return st;
+        }
+        inc.plan->n_tuned = timed;
+        *plan = inc.plan;
+        *workspace_bytes = inc.plan->workspace;
+        if (chosen)
+            *chosen = inc.opt;
+        return ok();
+    };
+    if (inc.plan->m == 0 || inc.plan->N == 0 || inc.plan->n_items == 0)
+        return done(SPMM_OK, 0);
+    TuneState ts;
+    hipError_t e = hipEventCreate(&ts.e0);
+    if (e == hipSuccess)
+        e = hipEventCreate(&ts.e1);
+    if (e != hipSuccess)
+        return done(hip_fail(e, "event creation"), 0);
+    // reps: enough runs for about 2 ms of timed work, from a 3-run probe
+    if ((s = time_runs(inc.plan, B, ldb, C, ldc, ts, stream, 3, &inc.us)) != SPMM_OK)
+        return done(s, 0);
+    const int n = reps > 0 ? reps
+                           : (int)std::min(100.0, std::max(3.0, 2000.0 / std::max(inc.us, 1.0)));
+    int timed = 1;
+    std::vector<std::pair<spmm_plan_options_t, int64_t>> cands;
+    for (const auto &o : tune_candidates(base, fmt == 0, b_row, b_col))
+        cands.emplace_back(o, split_cols);
+    if ((s = select_plan(make, cands, B, ldb, C, ldc, ts, stream, n, inc, &timed)) != SPMM_OK)
+        return done(s, timed);
+    // WCSR with an automatic split size: the sub-task size as a second stage,
+    // with the configuration the first stage kept
+    if (fmt == 1 && split_cols == 0 && inc.plan->kernel == 0) {
+        cands.clear();
+        for (int64_t T : {128, 512, 2048, 8192})
+            cands.emplace_back(inc.opt, T);
+        if ((s = select_plan(make, cands, B, ldb, C, ldc, ts, stream, n, inc, &timed)) != SPMM_OK)
+            return done(s, timed);
+    }
+    return done(SPMM_OK, timed);
+}
+
+}  // namespace
+}  // namespace wspmm
+
+extern "C" spmm_status_t spmm_bcsr_plan_tuned(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
+                                              int32_t b_row, int32_t b_col,
+                                              const int32_t *h_block_row_ptr,
+                                              const int32_t *d_block_col_idx, const void *d_blocks,
+                                              spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
+                                              const spmm_plan_options_t *options, const void *d_B,
+                                              int64_t ldb, void *d_C, int64_t ldc, void *stream,
+                                              int32_t reps, spmm_plan_options_t *chosen,
+                                              size_t *workspace_bytes)
+{
+    if (!plan || !workspace_bytes)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "null plan or workspace_bytes pointer");
+    *plan = nullptr;
+    size_t ws = 0;
+    const PlanMaker make = [&](const spmm_plan_options_t &o, int64_t, spmm_plan_t *out) {
+        return spmm_bcsr_plan_ex(out, m, k, N, b_row, b_col, h_block_row_ptr, d_block_col_idx,
+                                 d_blocks, ab_dtype, c_dtype, &o, &ws);
+    };
+    return tune_plan(0, b_row, b_col, make, options, 0, d_B, ldb, d_C, ldc, stream, reps, chosen,
+                     plan, workspace_bytes);
+}
+
+extern "C" spmm_status_t spmm_wcsr_plan_tuned(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N,
+                                              int32_t b_row, int32_t b_col,
+                                              const int32_t *h_window_row_ptr,
+                                              const int32_t *d_window_col_idx, const void *d_values,
+                                              spmm_dtype_t ab_dtype, spmm_dtype_t c_dtype,
+                                              int64_t split_cols, const spmm_plan_options_t *options,
+                                              const void *d_B, int64_t ldb, void *d_C, int64_t ldc,
+                                              void *stream, int32_t reps,
+                                              spmm_plan_options_t *chosen, size_t *workspace_bytes)
+{
+    if (!plan || !workspace_bytes)
+        return fail(SPMM_ERR_INVALID_ARGUMENT, "null plan or workspace_bytes pointer");
+    *plan = nullptr;
+    size_t ws = 0;
+    const PlanMaker make = [&](const spmm_plan_options_t &o, int64_t T, spmm_plan_t *out) {
+        return spmm_wcsr_plan_ex(out, m, k, N, b_row, b_col, h_window_row_ptr, d_window_col_idx,
+                                 d_values, ab_dtype, c_dtype, T, &o, &ws);
+    };
+    return tune_plan(1, b_row, b_col, make, options, split_cols, d_B, ldb, d_C, ldc, stream, reps,
+                     chosen, plan, workspace_bytes);
+}
+
+// ---------------------------------------------------------------------------
 // The run that allocates nothing: the fp32 partial tiles of split windows go
 // into this file's static device array instead of a caller-supplied
 // workspace.  Each GPU the library runs on holds its own copy of the array
@@ -1119,6 +1469,7 @@ extern "C" spmm_status_t spmm_plan_info(spmm_plan_t pl, spmm_plan_info_t *info)
     info->n_slots = pl->n_slots;
     info->stored_entries = pl->stored_entries;
     info->workspace_bytes = pl->workspace;
+    info->tuned = pl->n_tuned;
     return ok();
 }
 
