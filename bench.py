@@ -15,9 +15,10 @@ BCSR, 2: the WCSR matrix alone, 3: one WCSR population member, 5: block-sparse
 P*V).  Prints one JSON line.
 
 Timing: `value`, `ms_per_step` and `roofline` use cold-cache time, each launch
-preceded by a 1 GiB fill (more than the 256 MB MALL and the L2s together), the
-fills' own time subtracted; warm time (launches back to back, the paper's
-protocol) is reported next to it.  ``--warm-only`` skips the cold pass.
+preceded by a read of a 1 GiB buffer (more than the 256 MB MALL and the L2s
+together), the reads' own time subtracted; warm time (launches back to back,
+the paper's protocol) is reported next to it.  ``--warm-only`` skips the cold
+pass.
 """
 
 from __future__ import annotations
@@ -85,13 +86,20 @@ def algorithmic(p, A):
             "bytes_alg": float(bytes_alg), "b_rows_referenced": brows}
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "window_spmm_amd", "csrc", "kernels.hip")
+# the sources of the default plans' kernels (the tile, LDS-A, sweep and merge
+# kernels) and the headers they include
+KERNEL_SOURCES = [os.path.join(ROOT, "window_spmm_amd", "csrc", f)
+                  for f in ("kernels.hip", "kernels.h", "device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """One hash over the kernel sources: a traffic record counts only while it matches."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload_key: str):
@@ -355,23 +363,25 @@ def timed_pair(A, B, C, steps, warmup, cold=True):
     """Warm and cold per-launch time (s) of one SpMM.
 
     Warm: after `warmup` launches, one HIP event pair on the launch stream
-    around `steps` back-to-back launches.  Cold: `steps` steps of (1 GiB fill,
-    launch), the fill writing more than the MALL and every L2 hold, so each
-    launch starts with its inputs in HBM only; the region of `steps` fills
-    alone is timed the same way and subtracted.  Every region is bracketed by
-    torch.cuda.synchronize() on both sides.  Returns (warm, cold or None, the
-    regions' raw times in ms)."""
+    around `steps` back-to-back launches.  Cold: `steps` steps of (sum of a
+    1 GiB buffer, launch): the sum reads more than the MALL and every L2 hold,
+    so each launch starts with its inputs in HBM only, and it leaves no dirty
+    lines whose write-back would overlap the launch (a fill would); the region
+    of `steps` sums alone is timed the same way and subtracted.  Every region
+    is bracketed by torch.cuda.synchronize() on both sides.  Returns (warm,
+    cold or None, the regions' raw times in ms)."""
     import torch
     t_warm, wall_warm = time_runs(A, B, C, steps, warmup)
     region = {"warm_ms": t_warm * steps * 1e3, "warm_wall_ms": wall_warm * steps * 1e3}
     if not cold:
         return t_warm, None, region
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=C.device)
-    t_pair, _ = time_calls(lambda st: (flush.fill_(1.0), A.run(B, C, st)), steps, 2)
-    t_fill, _ = time_calls(lambda st: flush.fill_(1.0), steps, 2)
-    del flush
-    region.update({"fill_and_run_ms": t_pair * steps * 1e3, "fill_only_ms": t_fill * steps * 1e3})
-    return t_warm, max(t_pair - t_fill, 1e-9), region
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=C.device)
+    sink = torch.empty((), dtype=torch.float32, device=C.device)
+    t_pair, _ = time_calls(lambda st: (torch.sum(flush, dim=0, out=sink), A.run(B, C, st)), steps, 2)
+    t_read, _ = time_calls(lambda st: torch.sum(flush, dim=0, out=sink), steps, 2)
+    del flush, sink
+    region.update({"flush_and_run_ms": t_pair * steps * 1e3, "flush_only_ms": t_read * steps * 1e3})
+    return t_warm, max(t_pair - t_read, 1e-9), region
 
 
 def roofline_of(p, alg, t, info, key):

@@ -602,8 +602,12 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
 {
     constexpr int R = 64, BC = 64, MT = 4, V = 8, DW = 4;
     constexpr int NT = NW * 64;                    // threads per work-group
-    constexpr int STRIDE = BC * 2 + 16;            // padded LDS row: conflict-free b128 reads
-    constexpr int ABUF = R * STRIDE;               // bytes of one A buffer
+    // A buffers in MFMA fragment order: the 16 bytes lane l = 16g + i reads for
+    // (k half h, row slice mt) -- row 16mt + i, k = 32h + 8g .. +7 -- sit at
+    // ((h * 4 + mt) * 64 + l) * 16, so that every LDS write and every fragment
+    // read is one contiguous 1 KB run (no bank conflicts; padded rows read as
+    // 16 rows x 16 bytes took 3.2 conflict cycles per LDS instruction)
+    constexpr int ABUF = R * BC * 2;               // bytes of one A buffer
     constexpr int CPT = R * BC / 8 / NT;           // 16-byte chunks per thread per block
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * ABUF];
 
@@ -640,17 +644,20 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
     auto load_a = [&](int q, u32x4_t (&r)[CPT]) {
 #pragma unroll
         for (int t = 0; t < CPT; ++t) {
+            // chunk c in fragment order: (h, mt) = ((c / 64) / MT, (c / 64) % MT),
+            // lane l = c % 64 = 16g + i: row 16mt + i, k = 32h + 8g .. +7
             const int c = threadIdx.x + t * NT;
+            const int l = c & 63, hm = c >> 6;
+            const int row = 16 * (hm % MT) + (l & 15), cc = 4 * (hm / MT) + (l >> 4);
             r[t] = __builtin_amdgcn_raw_buffer_load_b128(
-                rA, (int)(((uint32_t)q * R * BC + (uint32_t)c * 8) * 2), 0, kNT);
+                rA, (int)(((uint32_t)q * R * BC + (uint32_t)row * BC + (uint32_t)cc * 8) * 2), 0, kNT);
         }
     };
     auto store_a = [&](int buf, const u32x4_t (&r)[CPT]) {
 #pragma unroll
         for (int t = 0; t < CPT; ++t) {
             const int c = threadIdx.x + t * NT;
-            *reinterpret_cast<u32x4_t *>(lds_a + buf * ABUF + (c >> 3) * STRIDE + (c & 7) * 16) =
-                r[t];
+            *reinterpret_cast<u32x4_t *>(lds_a + buf * ABUF + c * 16) = r[t];
         }
     };
     // Block column of block q (work-group uniform, so a scalar load); -1 past the end.
@@ -682,8 +689,8 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
         u32x4_t af[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            af[mt] = *reinterpret_cast<const u32x4_t *>(lds_a + buf * ABUF + (mt * 16 + li) * STRIDE +
-                                                       (half * 32 + 8 * g) * 2);
+            af[mt] = *reinterpret_cast<const u32x4_t *>(lds_a + buf * ABUF +
+                                                       ((half * MT + mt) * 64 + lane) * 16);
 #pragma unroll
         for (int c = 0; c < V; ++c) {
             u32x4_t bf;
@@ -774,7 +781,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
     constexpr int R = 64, BC = 64, MT = 4, V = CM ? 4 : VR;
     constexpr int DW = CM ? 4 : V * ESZ / 4;       // dwords of one B row segment per lane
     constexpr int NT = NW * 64;
-    constexpr int STRIDE = BC * ESZ + 16;          // padded LDS row: conflict-free reads
+    // Padded LDS rows, filled with row-major loads.  The fragment reads take
+    // about 3.6 bank-conflict cycles per LDS instruction; the conflict-free
+    // fragment order of bcsr64_lds_kernel, whose A loads are then strided, made
+    // this kernel 5 % slower (its A is loaded at every work-group's start, on
+    // the critical path; the LDS itself is not)
+    constexpr int STRIDE = BC * ESZ + 16;
     constexpr int ABUF = R * STRIDE;               // bytes of one block in LDS
     constexpr int CPR = BC * ESZ / 16;             // 16-byte chunks per block row
     constexpr int CPB = R * CPR;                   // 16-byte chunks per block
