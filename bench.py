@@ -113,7 +113,7 @@ def measured_traffic(workload_key: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    w = rec.get("workloads", {}).get(workload_key)
+    w = rec.get("workloads", {}).get(workload_key) if workload_key else None
     if not w or w.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     cp = rec["copy"]
@@ -611,8 +611,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--tuned", action="store_true",
-                    help="with --population: also tune each run's plan (spmm_wcsr_plan_tuned) "
-                         "and report it beside the default plan")
+                    help="time a tuned plan (spmm_*_plan_tuned) instead of the default one; "
+                         "with --population: tune each run's plan and report it beside the "
+                         "default plan")
     ap.add_argument("--warm-only", action="store_true",
                     help="no cold-cache pass: value and roofline from warm launches")
     ap.add_argument("--no-peaks", action="store_true",
@@ -688,6 +689,13 @@ def main():
     if args.sweep:
         run_sweep(p, A, B, C, alg, workload, {"col_major": 1} if args.col_major else None)
         return
+    tuned_opts = None
+    if args.tuned:
+        # the plan chosen by timing (spmm_*_plan_tuned on this B and C) instead of
+        # the plan's rules; the options it returns are reported in config
+        print("bench: tuning the plan", file=sys.stderr, flush=True)
+        tuned_opts = A.tune(B, C, options=opts or None)
+        info = A.plan.info()
 
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
     t_warm, t_cold, region = timed_pair(A, B, C, args.steps, args.warmup, not args.warm_only)
@@ -696,6 +704,8 @@ def main():
     key = "config%d" % args.config + ("_" + args.which if args.config == 4 else "") + \
           ("_m%d_n%d" % (args.member, args.n3) if args.config == 3 else "") + \
           ("_colmajor" if args.col_major else "") + ("_fp8" if args.fp8 else "")
+    if opts or args.tuned or args.n4 != 65536:
+        key = None   # the traffic records hold the default plans of the named workloads
     roof = roofline_of(p, alg, t_kernel, info, key)
     peak_mfma = PEAK_MFMA_TFLOPS_FP8 if p.ab_dtype == "fp8" else PEAK_MFMA_TFLOPS
     t_roof_mfma = alg["flops_stored"] / (peak_mfma * 1e12)
@@ -718,6 +728,8 @@ def main():
         "data": "synthetic (seeded; no dataset)",
         "config": {"workload": workload, "format": p.fmt, "m": p.m, "k": p.k, "N": p.N,
                    "options": opts,
+                   "tuned": None if tuned_opts is None else {"options": tuned_opts,
+                                                             "configurations_timed": info["tuned"]},
                    "ldb": int(B.stride(0)), "ldc": int(C.stride(0)),
                    "b_row": p.b_row, "b_col": p.b_col, "nnz": p.nnz,
                    "stored_entries": A.stored_entries, "c_dtype": p.c_dtype,

@@ -196,7 +196,8 @@ spmm_status_t spmm_csr_permute(int64_t n, const int32_t *h_row_ptr, const int32_
  * problem (see each kernel) is UNSUPPORTED. */
 typedef struct {
     int32_t kernel;          /* -1 auto; 0 generic tile kernel (any format and shape);
-                                1 BCSR 64x64 with LDS-shared A (b_row = b_col = 64, N >= 256);
+                                1 BCSR 64x64 with LDS-shared A (b_row = b_col = 64; N >= 256,
+                                  or any N with waves_n = 1);
                                 2 BCSR 64x64 A-stationary sweep (b_row = b_col = 64,
                                   N >= 4096, at most 8 blocks in every block row);
                                 3 BCSR 64x64 with each block row's A in the registers of
@@ -213,7 +214,8 @@ typedef struct {
                                 the default) or 4 (256-column tiles; FP16/BF16 only, and
                                 the only choice with col_major) */
     int32_t waves_n;         /* 0 auto; kernel 0: 1, 2 or 4 waves across the tile's
-                                columns; kernel 1: 2 or 4 */
+                                columns; kernel 1: 1, 2 or 4 waves of 128 columns (1 only
+                                when pinned: one wave per block row and tile) */
     int32_t waves_k;         /* 0 auto; kernel 0: 1, 2 or 4 waves splitting the packed
                                 columns, waves_n * waves_k <= 4 */
     int32_t distribution;    /* -1 auto; kernel 0: 0 planned per-work-group task lists,

@@ -586,7 +586,8 @@ def test_bcsr_wide_blocks_split_block_row(ws, br, bc):
     check(p, run_gpu(ws, p, A=A))
 
 
-@pytest.mark.parametrize("opts", [{"kernel": 1, "waves_n": 2}, {"kernel": 1, "waves_n": 4},
+@pytest.mark.parametrize("opts", [{"kernel": 1, "waves_n": 1}, {"kernel": 1, "waves_n": 2},
+                                  {"kernel": 1, "waves_n": 4},
                                   {"kernel": 1, "order": 1}, {"kernel": 0},
                                   {"kernel": 0, "waves_n": 1, "waves_k": 4},
                                   {"kernel": 0, "cols_per_lane": 2, "waves_n": 4}],
@@ -656,6 +657,7 @@ COL_MAJOR_CASES = [
     # m, k, N, block density, ab, c, options
     (1000, 520, 1288, 0.3, "bf16", "bf16", {"kernel": 1, "waves_n": 4}),
     (1000, 520, 1288, 0.3, "fp16", "fp32", {"kernel": 1, "waves_n": 2}),
+    (520, 640, 200, 0.3, "bf16", "fp32", {"kernel": 1, "waves_n": 1}),
     (1280, 640, 4104, 0.25, "bf16", "bf16", {"kernel": 2, "ranges_per_xcd": 1}),
     (704, 576, 8200, 0.3, "bf16", "fp16", {"kernel": 2, "ranges_per_xcd": 2}),
     (640, 512, 4096, 0.95, "fp16", "fp32", {"kernel": 2}),
@@ -1039,3 +1041,39 @@ def test_tuned_plan_refuses_bad_operands(ws):
     A.run(B, C)
     torch.cuda.synchronize()
     check(p, C.float().cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("case", [(1000, 1500, 128, "bf16", "fp32"), (333, 700, 72, "fp16", "bf16"),
+                                  (64, 64, 8, "bf16", "fp16"), (520, 4000, 264, "bf16", "fp32")],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_bcsr64_lds_kernel_one_wave_narrow_n(ws, case):
+    """The LDS-shared-A kernel with one wave of 128 columns per work-group (plan
+    option waves_n = 1), the only form it takes below N = 256: narrow and ragged
+    N (one partial column tile), ragged m and k, every output type."""
+    m, k, N, ab, ct = case
+    p = synth.block_problem(m, k, N, 64, 64, 0.3, seed=m + N, ab_dtype=ab, c_dtype=ct)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"kernel": 1, "waves_n": 1})
+    info = A.plan.info()
+    assert info["kernel"] == 1 and info["waves_n"] == 1 and info["tile_cols"] == 128
+    check(p, run_gpu(ws, p, A=A))
+
+
+def test_bcsr64_lds_kernel_one_wave_refused_unpinned(ws):
+    """Below N = 256 kernel 1 runs only when one wave is asked for."""
+    p = synth.block_problem(200, 300, 128, 64, 64, 0.3, seed=3, ab_dtype="bf16", c_dtype="fp32")
+    with pytest.raises(ws.SpmmError) as e:
+        ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"kernel": 1})
+    assert e.value.code == ws.ERR_UNSUPPORTED
+
+
+def test_config5_lds_kernel_one_wave_sampled(ws):
+    """Config 5 (the block-sparse P*V workload, N = 128) on the one-wave LDS-A
+    kernel, sampled rows."""
+    p = synth.config5()
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"kernel": 1, "waves_n": 1})
+    got = run_gpu(ws, p, A=A)
+    check(p, got, rows=_block_rows_sample(p, 5))
+

@@ -809,7 +809,9 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
     // are what make each XCD's work-groups sweep the same B tiles together, so
     // it needs every block row to fit twice per CU.
     const int64_t tiles512 = ceil_div(N, 512);
-    const bool lds_ok = b64 && N >= 256;
+    // kernel 1: 128-column tiles per wave, 2 or 4 waves (N >= 256), or one wave
+    // per work-group when pinned (any N)
+    const bool lds_ok = b64 && (N >= 256 || (opt.kernel == 1 && opt.waves_n == 1));
     // kernel 2 runs 8 columns per lane (512-column tiles), or 4 with col_major
     // or when the options ask for them (256-column tiles, 16-bit inputs)
     const int sweep_v = opt.col_major || opt.cols_per_lane == 4 ? 4 : 8;
@@ -924,9 +926,9 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         pl->n_ranges = 8 * h;
         pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
     } else if (pl->kernel == 1) {
-        if (opt.waves_n != 0 && opt.waves_n != 2 && opt.waves_n != 4) {
+        if (opt.waves_n == 0 && N < 256) {
             free_plan(pl);
-            return fail(SPMM_ERR_UNSUPPORTED, "kernel 1 runs 2 or 4 waves across N");
+            return fail(SPMM_ERR_UNSUPPORTED, "kernel 1 below N = 256 runs with waves_n = 1 only");
         }
         const int nw = opt.waves_n > 0 ? opt.waves_n : 4;
         pl->n_items = nbr;
@@ -1084,7 +1086,7 @@ std::vector<spmm_plan_options_t> tune_candidates(const spmm_plan_options_t &base
     };
     spmm_plan_options_t o;
     if (bcsr && b_row == 64 && b_col == 64) {
-        for (int wn : {2, 4})
+        for (int wn : {1, 2, 4})
             for (int ord : {0, 1}) {
                 spmm_plan_options_default(&o);
                 o.kernel = 1; o.waves_n = wn; o.order = ord;

@@ -1143,9 +1143,13 @@ static void launch_lds_nw(int ab, const TileParams &p, hipStream_t stream)
 hipError_t launch_bcsr64_lds(int ab, const TileParams &p, hipStream_t stream)
 {
     if (p.col_major)
-        p.waves_n == 2 ? launch_lds_nw<2, true>(ab, p, stream) : launch_lds_nw<4, true>(ab, p, stream);
+        p.waves_n == 1   ? launch_lds_nw<1, true>(ab, p, stream)
+        : p.waves_n == 2 ? launch_lds_nw<2, true>(ab, p, stream)
+                         : launch_lds_nw<4, true>(ab, p, stream);
     else
-        p.waves_n == 2 ? launch_lds_nw<2, false>(ab, p, stream) : launch_lds_nw<4, false>(ab, p, stream);
+        p.waves_n == 1   ? launch_lds_nw<1, false>(ab, p, stream)
+        : p.waves_n == 2 ? launch_lds_nw<2, false>(ab, p, stream)
+                         : launch_lds_nw<4, false>(ab, p, stream);
     return hipGetLastError();
 }
 
