@@ -1077,3 +1077,74 @@ def test_config5_lds_kernel_one_wave_sampled(ws):
     got = run_gpu(ws, p, A=A)
     check(p, got, rows=_block_rows_sample(p, 5))
 
+
+
+# --------------------------------------------------------------------------
+# the largest B the kernels' 32-bit buffer offsets address
+# --------------------------------------------------------------------------
+
+# At N = 65536 (leading dimension 65600) the largest k with k * ldb * 2 below
+# 2^32 - 256 that is a multiple of 64: B is 4.29 GB.
+K_AT_LIMIT = 32704
+
+
+@pytest.mark.parametrize("fmt,opts", [("bcsr", {}), ("bcsr", {"kernel": 1}), ("bcsr", {"kernel": 0}),
+                                      ("bcsr", {"kernel": 3}), ("wcsr", {})],
+                         ids=lambda x: x if isinstance(x, str) else ("k%s" % x.get("kernel", "auto")))
+def test_b_at_the_32bit_offset_limit(ws, fmt, opts):
+    """B of 4.29 GB, the last rows of which sit just below the 2^32 - 256 byte
+    limit of the kernels' buffer offsets: A has blocks in the first, a middle and
+    the last block columns, so the gathers reach B's last row at every column of
+    N = 65536.  The result is compared with the oracle on the B rows A uses."""
+    N, k, m = 65536, K_AT_LIMIT, 128
+    ldb = ws.recommended_ld(N, 2)
+    assert k * ldb * 2 < 2 ** 32 - 256 <= (k + 64) * ldb * 2
+    nbc = k // 64
+    blocks = [[0, nbc // 2, nbc - 1], [1, nbc - 2, nbc - 1]]
+    g = np.random.default_rng(17)
+    rows, cols = [], []
+    for br, js in enumerate(blocks):
+        for r in range(64 * br, 64 * br + 64):
+            for J in js:
+                rows.append(np.full(64, r))
+                cols.append(np.arange(J * 64, J * 64 + 64))
+    rows, cols = np.concatenate(rows), np.concatenate(cols)
+    row_ptr = np.zeros(m + 1, np.int64)
+    np.add.at(row_ptr, rows + 1, 1)
+    row_ptr = np.cumsum(row_ptr).astype(np.int32)
+    v = g.normal(0.0, 1.0, cols.size)
+    v[v == 0] = 1.0
+    vals = synth.bf16_bits(v)
+    _say("gpu case: B at the offset limit", fmt, opts, "k", k, "ldb", ldb)
+    # B on the device, drawn there in row chunks
+    Bfull = torch.empty((k, ldb), dtype=torch.int16, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    for r0 in range(0, k, 4096):
+        r1 = min(k, r0 + 4096)
+        Bfull[r0:r1, :N] = torch.randn((r1 - r0, N), generator=gen, device="cuda",
+                                        dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+    B = Bfull[:, :N]
+    b_row, b_col = (64, 64) if fmt == "bcsr" else (16, 8)
+    A = ws.DeviceSparse(fmt, m, k, N, row_ptr, cols.astype(np.int32), vals, b_row, b_col, "bf16",
+                        "fp32", options=opts or None)
+    if opts.get("kernel") is not None:
+        assert A.plan.info()["kernel"] == opts["kernel"]
+    C = torch.full((m, ws.recommended_ld(N, 4)), float("nan"), dtype=torch.float32, device="cuda")
+    A.run(B, C[:, :N])
+    torch.cuda.synchronize()
+    # the oracle on a compact B holding only the rows A uses
+    used = np.unique(cols // 64)
+    Bc = B[torch.from_numpy(np.concatenate([np.arange(J * 64, J * 64 + 64) for J in used])).cuda()]
+    Bc = Bc.cpu().numpy().view(np.uint16)
+    pos = {int(J): i for i, J in enumerate(used)}
+    cols_c = np.array([pos[int(c) // 64] * 64 + int(c) % 64 for c in cols], np.int32)
+    out_rows = np.array([0, 1, 63, 64, 100, 127])
+    ref, bound = oracle.spmm(m, used.size * 64, N, rows.astype(np.int32), cols_c, vals, Bc, "bf16",
+                             out_rows=out_rows)
+    got = C[:, :N].cpu().numpy().astype(np.float64)[out_rows]
+    ok, worst, at = oracle.within_tolerance(got, ref, bound, TOL, out_dtype="fp32")
+    _say("   worst |dC|/Bound = %.3g at %s" % (worst, at))
+    assert ok, (at, worst)
+    assert not np.isnan(C[:, :N].cpu().numpy()).any()
+    del Bfull, B, C, A
+    torch.cuda.empty_cache()
