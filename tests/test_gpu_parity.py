@@ -1148,3 +1148,50 @@ def test_b_at_the_32bit_offset_limit(ws, fmt, opts):
     assert not np.isnan(C[:, :N].cpu().numpy()).any()
     del Bfull, B, C, A
     torch.cuda.empty_cache()
+
+
+# The widest N the kernels take: ldb < 2^23 elements (B row numbers and the
+# leading dimension share 24-bit multiplies), N = 2^23 - 8.
+N_AT_LIMIT = (1 << 23) - 8
+
+
+@pytest.mark.parametrize("fmt,opts", [("bcsr", {}), ("bcsr", {"kernel": 1}), ("bcsr", {"kernel": 0}),
+                                      ("wcsr", {})],
+                         ids=lambda x: x if isinstance(x, str) else ("k%s" % x.get("kernel", "auto")))
+def test_n_at_the_ldb_limit(ws, fmt, opts):
+    """N = 2^23 - 8 columns (B 3.4 GB, C 4.4 GB): thousands of column tiles and
+    ranges, the last tile ragged.  The product is separable by columns, so the
+    first and the last 8192 columns are compared with the oracle on those
+    columns of B."""
+    m, k = 130, 200
+    N = N_AT_LIMIT
+    ldb = ws.recommended_ld(N, 2)
+    assert ldb < (1 << 23) and k * ldb * 2 < 2 ** 32 - 256
+    b_row, b_col = (64, 64) if fmt == "bcsr" else (16, 8)
+    p0 = synth.random_problem(m, k, 8, 0.1, seed=41, ab_dtype="bf16", c_dtype="fp32", fmt=fmt,
+                              b_row=b_row, b_col=b_col, empty_row_frac=0.1)
+    _say("gpu case: N at the ldb limit", fmt, opts, "N", N)
+    Bfull = torch.empty((k, ldb), dtype=torch.int16, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    for r in range(k):
+        Bfull[r, :N] = torch.randn(N, generator=gen, device="cuda", dtype=torch.float32) \
+            .to(torch.bfloat16).view(torch.int16)
+    B = Bfull[:, :N]
+    A = ws.DeviceSparse(fmt, m, k, N, p0.row_ptr, p0.col_idx, p0.vals, b_row, b_col, "bf16", "fp32",
+                        options=opts or None)
+    if opts.get("kernel") is not None:
+        assert A.plan.info()["kernel"] == opts["kernel"]
+    C = torch.empty((m, ws.recommended_ld(N, 4)), dtype=torch.float32, device="cuda")[:, :N]
+    C.fill_(float("nan"))
+    A.run(B, C)
+    torch.cuda.synchronize()
+    for c0 in (0, N - 8192):
+        Bs = B[:, c0:c0 + 8192].contiguous().cpu().numpy().view(np.uint16)
+        ref, bound = oracle.spmm(m, k, 8192, p0.coo_rows(), p0.col_idx, p0.vals, Bs, "bf16")
+        got = C[:, c0:c0 + 8192].cpu().numpy().astype(np.float64)
+        ok, worst, at = oracle.within_tolerance(got, ref, bound, TOL, out_dtype="fp32")
+        _say("   columns %d..: worst |dC|/Bound = %.3g at %s" % (c0, worst, at))
+        assert ok, (c0, at, worst)
+    assert not torch.isnan(C).any().item()
+    del Bfull, B, C, A
+    torch.cuda.empty_cache()
