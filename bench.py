@@ -181,7 +181,7 @@ def sweep_candidates(p):
     packed columns) with both ways of handing out tasks."""
     cands = []
     if p.fmt == "bcsr" and p.b_row == 64 and p.b_col == 64:
-        cands += [{"kernel": 1, "waves_n": wn, "order": o} for wn in (2, 4) for o in (0, 1)]
+        cands += [{"kernel": 1, "waves_n": wn, "order": o} for wn in (1, 2, 4, 8) for o in (0, 1)]
         cands += [{"kernel": 2, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16)]
         cands += [{"kernel": 2, "cols_per_lane": 4, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16)]
         cands += [{"kernel": 3, "ranges_per_xcd": h} for h in (1, 2, 4, 8, 16, 32)]

@@ -587,7 +587,7 @@ def test_bcsr_wide_blocks_split_block_row(ws, br, bc):
 
 
 @pytest.mark.parametrize("opts", [{"kernel": 1, "waves_n": 1}, {"kernel": 1, "waves_n": 2},
-                                  {"kernel": 1, "waves_n": 4},
+                                  {"kernel": 1, "waves_n": 4}, {"kernel": 1, "waves_n": 8},
                                   {"kernel": 1, "order": 1}, {"kernel": 0},
                                   {"kernel": 0, "waves_n": 1, "waves_k": 4},
                                   {"kernel": 0, "cols_per_lane": 2, "waves_n": 4}],

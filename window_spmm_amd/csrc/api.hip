@@ -63,10 +63,13 @@ spmm_status_t check_options(const spmm_plan_options_t &o, bool bcsr)
                     o.kernel);
     if (o.cols_per_lane != 0 && o.cols_per_lane != 2 && o.cols_per_lane != 4 && o.cols_per_lane != 8)
         return fail(SPMM_ERR_INVALID_ARGUMENT, "options.cols_per_lane must be 0, 2, 4 or 8");
-    if (o.waves_n < 0 || o.waves_n > 4 || o.waves_n == 3 || o.waves_k < 0 || o.waves_k > 4 ||
-        o.waves_k == 3 || std::max(1, o.waves_n) * std::max(1, o.waves_k) > 4)
+    // waves_n 8: the LDS-A kernel's 1024-column tiles (kernel 1 pinned, row-major)
+    const bool lds8 = o.kernel == 1 && o.waves_n == 8 && o.waves_k == 0 && !o.col_major;
+    if (!lds8 && (o.waves_n < 0 || o.waves_n > 4 || o.waves_n == 3 || o.waves_k < 0 || o.waves_k > 4 ||
+                  o.waves_k == 3 || std::max(1, o.waves_n) * std::max(1, o.waves_k) > 4))
         return fail(SPMM_ERR_INVALID_ARGUMENT,
-                    "options.waves_n and waves_k must be 0, 1, 2 or 4 with a product of at most 4");
+                    "options.waves_n and waves_k must be 0, 1, 2 or 4 with a product of at most 4 "
+                    "(waves_n 8 only with kernel 1, row-major)");
     if (o.distribution < -1 || o.distribution > 1 || o.row_order < -1 || o.row_order > 1 ||
         o.order < -1 || o.order > 1)
         return fail(SPMM_ERR_INVALID_ARGUMENT, "options.distribution, row_order and order must be -1, 0 or 1");
@@ -930,7 +933,10 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
             free_plan(pl);
             return fail(SPMM_ERR_UNSUPPORTED, "kernel 1 below N = 256 runs with waves_n = 1 only");
         }
-        const int nw = opt.waves_n > 0 ? opt.waves_n : 4;
+        // 1024-column tiles (8 waves sharing each A block) at wide row-major N:
+        // measured on down_proj (N = 65536) 1616-1619 against 1661-1665 us with
+        // 512-column tiles (half the A loads and barriers per column)
+        const int nw = opt.waves_n > 0 ? opt.waves_n : (N >= 8192 && !opt.col_major ? 8 : 4);
         pl->n_items = nbr;
         pl->V = 8;
         pl->waves_n = nw;
@@ -1086,7 +1092,7 @@ std::vector<spmm_plan_options_t> tune_candidates(const spmm_plan_options_t &base
     };
     spmm_plan_options_t o;
     if (bcsr && b_row == 64 && b_col == 64) {
-        for (int wn : {1, 2, 4})
+        for (int wn : {1, 2, 4, 8})
             for (int ord : {0, 1}) {
                 spmm_plan_options_default(&o);
                 o.kernel = 1; o.waves_n = wn; o.order = ord;

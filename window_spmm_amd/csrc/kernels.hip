@@ -1149,6 +1149,7 @@ hipError_t launch_bcsr64_lds(int ab, const TileParams &p, hipStream_t stream)
     else
         p.waves_n == 1   ? launch_lds_nw<1, false>(ab, p, stream)
         : p.waves_n == 2 ? launch_lds_nw<2, false>(ab, p, stream)
+        : p.waves_n == 8 ? launch_lds_nw<8, false>(ab, p, stream)
                          : launch_lds_nw<4, false>(ab, p, stream);
     return hipGetLastError();
 }
