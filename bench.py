@@ -87,14 +87,16 @@ def algorithmic(p, A):
 
 
 # the sources of the default plans' kernels (the tile, LDS-A, sweep and merge
-# kernels) and the headers they include
+# kernels), the headers they include, and the planner that picks their launch
+# shapes
 KERNEL_SOURCES = [os.path.join(ROOT, "window_spmm_amd", "csrc", f)
-                  for f in ("kernels.hip", "kernels.h", "device.h")]
+                  for f in ("kernels.hip", "kernels.h", "device.h", "api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_sha256() -> str:
-    """One hash over the kernel sources: a traffic record counts only while it matches."""
+    """One hash over the kernel and planner sources: a traffic record counts only
+    while it matches."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
         with open(path, "rb") as f:
@@ -261,8 +263,9 @@ def run_ffn_table():
     product of the same shape through torch.mm (hipBLASLt).  Latency averaged
     over 100 runs after 10 warm-up runs, as in the paper.  At N = 1K each sparse
     result is checked against torch.mm of its densified weight (fp32).  Each
-    measurement starts after a 2 s pause (the GPU's clocks drop after long
-    full-power runs such as the dense GEMM), sparse cases before the dense one."""
+    measurement is preceded by at least 100 ms of the same launches (at least
+    10), so that it starts at the clock the load holds rather than at an idle
+    one; sparse cases before the dense one."""
     import torch
     import synth
     import window_spmm_amd as ws
@@ -270,11 +273,14 @@ def run_ffn_table():
     m, k = 18944, 3584
     sparsities = (0.80, 0.90, 0.95, 0.99)
 
-    def timed(fn, warm=10, n=100):
+    def timed(fn, warm=10, n=100, warm_ms=100.0):
         torch.cuda.synchronize()
-        time.sleep(2.0)
-        for _ in range(warm):
+        t0, done = time.perf_counter(), 0
+        while done < warm or (time.perf_counter() - t0) * 1e3 < warm_ms:
             fn()
+            done += 1
+            if done % 10 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()

@@ -302,8 +302,8 @@ spmm_status_t spmm_wcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t
  * variants, the generic kernel's columns per lane, wave splits and task
  * distribution; for WCSR with split_cols = 0 also sub-task sizes 128, 512, 2048
  * and 8192), times each on `stream` (two untimed runs, then `reps` runs between
- * two events; reps = 0: about 2 ms of runs, at least 3 and at most 100), then
- * times the three fastest three more times each, interleaved with the automatic
+ * two events; reps = 0: about 4 ms of runs, at least 5 and at most 100), then
+ * times the four fastest three more times each, interleaved with the automatic
  * plan, and returns the one with the lowest median if it is at least 2 % faster
  * than the automatic plan's median (else the automatic plan; the sub-task sizes
  * are a second such stage after the first).  Candidates no kernel can run are

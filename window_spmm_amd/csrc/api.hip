@@ -918,13 +918,20 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         pl->n_col_tiles = ceil_div(N, pl->tile_cols);
         pl->workspace = 0;
         pl->order = 0;
-        // Ranges of two column tiles: on the FFN shapes (N = 65536, 128 tiles)
-        // ranges of 1, 2, 4, 8 and 16 tiles measured 1540, 1430, 1660, 1730 and
-        // 1770 us (gate), 1530, 1410, 1580, 1620 and 1760 us (up); longer
-        // ranges amortise the A load over more tiles but let the work-groups of
-        // an XCD drift apart, so that fewer of them share each B tile in L2.
-        const int64_t h = opt.ranges_per_xcd > 0
-                              ? opt.ranges_per_xcd
+        // Range length.  Longer ranges amortise the A load over more tiles but
+        // let the work-groups of an XCD drift apart, so that fewer of them share
+        // each B tile in L2.  Measured (interleaved runs on one box, the gate_proj
+        // shape at 90 % block sparsity): at N = 65536 (128 tiles) ranges of one
+        // tile ran 1287-1319 us cold against 1357-1361 us for two (up_proj
+        // 1290-1310 against 1338-1345 us; 95 % sparsity 901-906 against
+        // 947-954 us; N = 131072 2657-2660 against 2734-2736 us), but with one
+        // block per block row (99 %) two tiles stay better (688-693 against
+        // 742-744 us); at N = 16384 and 32768 (32 and 64 tiles) ranges of two
+        // to four tiles are best (367-378 us against 440 and 569 us for four
+        // and one; 614-619 us for four against 650-672 for two).
+        const int64_t h = opt.ranges_per_xcd > 0 ? opt.ranges_per_xcd
+                          : pl->n_col_tiles >= 128 && max_blocks >= 3
+                              ? std::min<int64_t>(64, pl->n_col_tiles / 8)
                               : std::max<int64_t>(1, std::min<int64_t>(64, pl->n_col_tiles / 16));
         pl->n_ranges = 8 * h;
         pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
@@ -933,10 +940,14 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
             free_plan(pl);
             return fail(SPMM_ERR_UNSUPPORTED, "kernel 1 below N = 256 runs with waves_n = 1 only");
         }
-        // 1024-column tiles (8 waves sharing each A block) at wide row-major N:
-        // measured on down_proj (N = 65536) 1616-1619 against 1661-1665 us with
-        // 512-column tiles (half the A loads and barriers per column)
-        const int nw = opt.waves_n > 0 ? opt.waves_n : (N >= 8192 && !opt.col_major ? 8 : 4);
+        // 1024-column tiles (8 waves sharing each A block) at wide row-major N
+        // and long block rows: measured on down_proj (N = 65536, 30 blocks per
+        // block row) 1616-1619 against 1661-1665 us with 512-column tiles (half
+        // the A loads and barriers per column); on the gate_proj shape at 80 %
+        // block sparsity (11 blocks per block row) 2388-2398 against 2361-2363 us
+        const double mean_blocks = (double)h_block_row_ptr[nbr] / (double)std::max<int64_t>(1, nbr);
+        const int nw = opt.waves_n > 0 ? opt.waves_n
+                       : (N >= 8192 && !opt.col_major && mean_blocks >= 16.0) ? 8 : 4;
         pl->n_items = nbr;
         pl->V = 8;
         pl->waves_n = nw;
@@ -1189,7 +1200,7 @@ using PlanMaker = std::function<spmm_status_t(const spmm_plan_options_t &, int64
 // timing noise does not trade the automatic plan for an equal one.
 constexpr double kTuneMargin = 0.02;
 // Candidates kept after the first timing, and rounds of the final comparison.
-constexpr int kTuneFinalists = 3;
+constexpr int kTuneFinalists = 4;
 constexpr int kTuneRounds = 3;
 
 struct Timed {
@@ -1325,11 +1336,12 @@ spmm_status_t tune_plan(int fmt, int32_t b_row, int32_t b_col, const PlanMaker &
         e = hipEventCreate(&ts.e1);
     if (e != hipSuccess)
         return done(hip_fail(e, "event creation"), 0);
-    // reps: enough runs for about 2 ms of timed work, from a 3-run probe
+    // reps: enough runs for about 4 ms of timed work (at least 5), from a
+    // 3-run probe: candidates of one kernel differ by a few per cent
     if ((s = time_runs(inc.plan, B, ldb, C, ldc, ts, stream, 3, &inc.us)) != SPMM_OK)
         return done(s, 0);
     const int n = reps > 0 ? reps
-                           : (int)std::min(100.0, std::max(3.0, 2000.0 / std::max(inc.us, 1.0)));
+                           : (int)std::min(100.0, std::max(5.0, 4000.0 / std::max(inc.us, 1.0)));
     int timed = 1;
     std::vector<std::pair<spmm_plan_options_t, int64_t>> cands;
     for (const auto &o : tune_candidates(base, fmt == 0, b_row, b_col))
