@@ -376,11 +376,14 @@ spmm_status_t spmm_wcsr_run_noalloc(spmm_plan_t plan, const void *d_B, int64_t l
 spmm_status_t spmm_plan_info(spmm_plan_t plan, spmm_plan_info_t *info);
 
 /* Leading dimension (elements) to allocate for a dense operand with N columns of
- * elem_bytes-byte elements: N rounded up to 8, plus 64 (128 for 1-byte elements)
- * when the row pitch would be a multiple of 4 KiB.  With power-of-two pitches the rows that one column
- * tile gathers from B all fall into the same L2 sets; the pad spreads them.
- * Any ldb/ldc >= N that is a multiple of 8 is valid; this only affects speed.
- * Returns N unchanged for N <= 0 or elem_bytes <= 0. */
+ * elem_bytes-byte elements: N rounded up to 8; when that row pitch is a multiple
+ * of 4 KiB, plus 2 KiB of elements (1024 for 2-byte, 2048 for 1-byte, 512 for
+ * 4-byte elements) if the pitch is 16 KiB or more, else plus 64 elements (128
+ * for 1-byte elements).  With a 4 KiB-multiple pitch, the rows that one column
+ * tile reads all fall into the same L2 sets; from 16 KiB on, a pitch half a page
+ * past the multiple also makes a run's time independent of where B and C were
+ * allocated.  Any ldb/ldc >= N that is a multiple of 8 is valid; this only
+ * affects speed.  Returns N unchanged for N <= 0 or elem_bytes <= 0. */
 int64_t spmm_recommended_ld(int64_t N, int32_t elem_bytes);
 
 /* Launch floor: enqueues one empty kernel (one work-group of 64 threads) on

@@ -90,10 +90,18 @@ def test_launch_floor_without_gpu_reports_hip_error():
 
 
 def test_recommended_ld():
-    # pitches that are a multiple of 4 KiB get 64 extra elements; others are kept
-    assert ws.recommended_ld(65536, 2) == 65600
-    assert ws.recommended_ld(65536, 4) == 65600
+    # pitches that are a multiple of 4 KiB get 2 KiB more from 16 KiB on, one
+    # 128-byte line (64 elements, 128 for 1-byte data) below; others are kept
+    assert ws.recommended_ld(65536, 2) == 66560
+    assert ws.recommended_ld(65536, 4) == 66048
+    assert ws.recommended_ld(65536, 1) == 67584
+    assert ws.recommended_ld(8192, 2) == 9216
+    assert ws.recommended_ld(16384, 1) == 18432
+    assert ws.recommended_ld(4096, 2) == 4160
+    assert ws.recommended_ld(4096, 1) == 4224
+    assert ws.recommended_ld(1024, 4) == 1088
     assert ws.recommended_ld(2048, 2) == 2112
+    assert ws.recommended_ld(16000, 2) == 16000
     assert ws.recommended_ld(128, 2) == 128
     assert ws.recommended_ld(1000, 2) == 1000
     assert ws.recommended_ld(1001, 2) == 1008

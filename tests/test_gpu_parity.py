@@ -1083,9 +1083,9 @@ def test_config5_lds_kernel_one_wave_sampled(ws):
 # the largest B the kernels' 32-bit buffer offsets address
 # --------------------------------------------------------------------------
 
-# At N = 65536 (leading dimension 65600) the largest k with k * ldb * 2 below
+# At N = 65536 (leading dimension 66560) the largest k with k * ldb * 2 below
 # 2^32 - 256 that is a multiple of 64: B is 4.29 GB.
-K_AT_LIMIT = 32704
+K_AT_LIMIT = 32256
 
 
 @pytest.mark.parametrize("fmt,opts", [("bcsr", {}), ("bcsr", {"kernel": 1}), ("bcsr", {"kernel": 0}),

@@ -1519,8 +1519,16 @@ extern "C" int64_t spmm_recommended_ld(int64_t N, int32_t elem_bytes)
     if (N <= 0 || elem_bytes <= 0)
         return N;
     const int64_t ld = ceil_div(N, 8) * 8;
-    // Row pitches that are a multiple of 4 KiB put the rows of a column slice into
-    // the same L2 sets; 64 extra elements (128 for 1-byte data, so one 128-byte
-    // line for 8- and 16-bit data) spread them.
-    return (ld * elem_bytes) % 4096 == 0 ? ld + (elem_bytes == 1 ? 128 : 64) : ld;
+    if ((ld * elem_bytes) % 4096 != 0)
+        return ld;
+    // A row pitch that is a multiple of 4 KiB puts the rows of a column slice
+    // into the same L2 sets.  From 16 KiB on, the pitch gets half a 4 KiB page
+    // more: rows then alternate between the two halves of a page, and the time
+    // of a run no longer depends on where in memory B and C sit (with one
+    // 128-byte line more, the same run varied up to 2x between allocations).
+    // Shorter pitches get the one line (64 elements, 128 for 1-byte data), at
+    // a smaller cost in memory.
+    if (ld * elem_bytes >= 16384)
+        return ld + ceil_div(ceil_div(2048, elem_bytes), 8) * 8;
+    return ld + (elem_bytes == 1 ? 128 : 64);
 }
