@@ -920,6 +920,81 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         pl->order = 0;
         // Range length.  Longer ranges amortise the A load over more tiles but
         // let the work-groups of an XCD drift apart, so that fewer of them share
+        // each B tile in L2; one-tile ranges keep every resident work-group of
+        // an XCD on one B slice and re-read A (from L2 and the memory-side
+        // cache) once per tile, which pays when A is short and B is wide.
+        // Measured on the gate_proj shape (row-major, 6 ranges-per-XCD settings
+        // timed interleaved, medians, one box; 1 / 3 / 6 / 8 blocks per block
+        // row, N = 8K to 64K, i.e. 16 to 128 tiles):
+        //  - about four tiles per range (N / 16384 ranges per XCD) is best or
+        //    within 3 % at 1 and 8 blocks, and at 3 and 6 blocks up to 64 and
+        //    32 tiles (e.g. 6 blocks, N = 32768: 606 us against 643 us with two
+        //    tiles and 656 us with one);
+        //  - at 7-8 blocks, past 64 tiles, two ranges per XCD stay best (N =
+        //    65536: 1515 us against 1752 us with four tiles, 1598 with one);
+        //  - one-tile ranges win at 3-6 blocks from 96 tiles on (6 blocks, N =
+        //    65536: 1300 us against 1525 with four tiles; 3 blocks: 885 against
+        //    1077) and at 3 blocks from 48 tiles on (N = 32768: 445 against 467).
+        // Column-major plans (256-column tiles) keep the one-tile rule from 128
+        // tiles and 3 blocks, and N / 4096 ranges per XCD below, the rule they
+        // were measured with.
+        const double mean_blocks = (double)h_block_row_ptr[nbr] / (double)std::max<int64_t>(1, nbr);
+        const int64_t tiles = pl->n_col_tiles;
+        int64_t h;
+        if (opt.ranges_per_xcd > 0) {
+            h = opt.ranges_per_xcd;
+        } else if (opt.col_major) {
+            h = tiles >= 128 && max_blocks >= 3 ? std::min<int64_t>(64, tiles / 8)
+                                                : std::max<int64_t>(1, std::min<int64_t>(64, tiles / 16));
+        } else {
+            const bool one_tile = mean_blocks >= 2.5 && ((mean_blocks <= 6.5 && tiles >= 96) ||
+                                                         (mean_blocks <= 3.5 && tiles >= 48));
+            h = one_tile ? std::min<int64_t>(64, ceil_div(tiles, 8))
+                         : std::max<int64_t>(1, std::min<int64_t>(mean_blocks > 6.5 ? 2 : 64, tiles / 32));
+        }
+        pl->n_ranges = 8 * h;
+        pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
+    } else if (pl->kernel == 3) {
+        if (opt.cols_per_lane != 0 && opt.cols_per_lane != 8) {
+            free_plan(pl);
+            return fail(SPMM_ERR_UNSUPPORTED, "kernel 3 runs 8 columns per lane");
+        }
+        pl->n_items = nbr;
+        pl->V = 8;
+        pl->waves_n = 1;
+        pl->waves_k = 2;
+        pl->tile_cols = 128;
+        pl->n_col_tiles = ceil_div(N, 128);
+        pl->workspace = 0;
+        pl->order = 0;
+        // ranges of eight 128-column strips by default (a block row's A is
+        // loaded once per range)
+        const int64_t h = opt.ranges_per_xcd > 0
+                              ? opt.ranges_per_xcd
+                              : std::max<int64_t>(1, std::min<int64_t>(64, pl->n_col_tiles / 64));
+        pl->n_ranges = 8 * h;
+        pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
+    } else if (pl->kernel == 2) {
+        // column-major: 4 columns per lane (a whole block of B^T per ring stage)
+        if (opt.cols_per_lane != 0 && opt.cols_per_lane != sweep_v) {
+            free_plan(pl);
+            return fail(SPMM_ERR_UNSUPPORTED, "kernel 2 runs 8 or 4 columns per lane (4 with "
+                                              "col_major, 8 with FP8_E4M3)");
+        }
+        if (ab_dtype == SPMM_FP8_E4M3 && sweep_v != 8) {
+            free_plan(pl);
+            return fail(SPMM_ERR_UNSUPPORTED, "kernel 2 runs FP8_E4M3 with 8 columns per lane");
+        }
+        pl->n_items = nbr;
+        pl->V = sweep_v;
+        pl->waves_n = 4;
+        pl->waves_k = 1;
+        pl->tile_cols = 64 * sweep_v;
+        pl->n_col_tiles = ceil_div(N, pl->tile_cols);
+        pl->workspace = 0;
+        pl->order = 0;
+        // Range length.  Longer ranges amortise the A load over more tiles but
+        // let the work-groups of an XCD drift apart, so that fewer of them share
         // each B tile in L2.  Measured (interleaved runs on one box, the gate_proj
         // shape at 90 % block sparsity): at N = 65536 (128 tiles) ranges of one
         // tile ran 1287-1319 us cold against 1357-1361 us for two (up_proj
