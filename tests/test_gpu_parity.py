@@ -520,6 +520,40 @@ def test_config4_down_sampled(ws):
     check(p, got, rows=rows)
 
 
+RANGE_RULE_CASES = [
+    # block density (blocks per block row of 56), N, ranges per XCD the plan takes
+    (0.05, 24576, 6),    # 3 blocks, 48 tiles: one-tile ranges, 6 ranges per XCD
+    (0.05, 40000, 10),   # 3 blocks, 79 tiles (the last 64 columns wide): one-tile, one empty range
+    (0.14, 65536, 2),    # 8 blocks, 128 tiles: two ranges per XCD (8 tiles each)
+    (0.02, 65536, 4),    # 1 block, 128 tiles: four ranges per XCD (4 tiles each)
+    (0.10, 16384, 1),    # 6 blocks, 32 tiles: one range per XCD (4 tiles each)
+]
+
+
+@pytest.mark.parametrize("case", RANGE_RULE_CASES, ids=lambda c: "d%g-N%d" % c[:2])
+def test_sweep_kernel_range_rule_shapes(ws, case):
+    """The gate_proj shape (18944 x 3584, 64x64 blocks) at the block counts and
+    widths where the sweep kernel's automatic range length changes: the plan
+    takes the range count of the rule, and the product (B and C rows allocated
+    with the recommended leading dimension, as the benchmark does) matches the
+    oracle on sampled rows across all N columns."""
+    dens, N, H = case
+    p = synth.config4("gate", N=N, density=dens)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype)
+    info = A.plan.info()
+    assert info["kernel"] == 2 and info["ranges_per_xcd"] == H, info
+    _say("gpu case: range rule", dens, N, info)
+    B = A.device_b(p.B, padded=True)
+    C = A.new_c(padded=True)
+    C.fill_(float("nan"))
+    A.run(B, C)
+    torch.cuda.synchronize()
+    got = C.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    check(p, got, rows=_block_rows_sample(p, int(N) + 7, n_random=16))
+
+
 @pytest.mark.parametrize("width", [1, 9])
 def test_config5_sampled(ws, width):
     """Config 5 (block-sparse attention probabilities times V): the literal
