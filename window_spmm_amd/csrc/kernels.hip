@@ -692,8 +692,12 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
             const int c = threadIdx.x + t * NT;
             const int l = c & 63, hm = c >> 6;
             const int row = 16 * (hm % MT) + (l & 15), cc = 4 * (hm / MT) + (l >> 4);
+            // plain loads: A is read again for every column tile and is small
+            // enough to stay in the memory-side cache; non-temporal loads, which
+            // do not keep it there, made down_proj 8 % slower (1605 against
+            // 1472-1481 us)
             r[t] = __builtin_amdgcn_raw_buffer_load_b128(
-                rA, (int)(((uint32_t)q * R * BC + (uint32_t)row * BC + (uint32_t)cc * 8) * 2), 0, kNT);
+                rA, (int)(((uint32_t)q * R * BC + (uint32_t)row * BC + (uint32_t)cc * 8) * 2), 0, 0);
         }
     };
     auto store_a = [&](int buf, const u32x4_t (&r)[CPT]) {
@@ -854,7 +858,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
     const int nblk = p.row_ptr[item + 1] - (int)blk0;  // <= kSweepMaxBlocks (the plan checks)
     const int64_t row0 = (int64_t)item * R;
 
-    // the block row's A blocks -> LDS: every load in flight before the first store
+    // the block row's A blocks -> LDS: every load in flight before the first store.
+    // Plain loads: every column range reads A again, and A (a few to a few tens
+    // of MB) stays in the memory-side cache between them; with non-temporal
+    // loads gate_proj ran 7 % slower (1408-1425 against 1309-1319 us). A costs
+    // about 400 us of the launch either way (1015-1020 us with its loads
+    // skipped, timing only).
     {
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(
             reinterpret_cast<const uint8_t *>(p.A) + blk0 * R * BC * ESZ, (uint32_t)(nblk * R * BC * ESZ));
@@ -863,7 +872,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
 #pragma unroll
         for (int t = 0; t < MAXC; ++t) {
             const int c = threadIdx.x + t * NT;
-            v[t] = __builtin_amdgcn_raw_buffer_load_b128(rA, c < nchunks ? c * 16 : (int)kOOB, 0, kNT);
+            v[t] = __builtin_amdgcn_raw_buffer_load_b128(rA, c < nchunks ? c * 16 : (int)kOOB, 0, 0);
         }
 #pragma unroll
         for (int t = 0; t < MAXC; ++t) {
