@@ -69,12 +69,17 @@ hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stre
 hipError_t launch_bcsr64_lds(int ab_dtype, const TileParams &p, hipStream_t stream);
 // Most blocks in a block row that the sweep kernel holds in LDS.
 constexpr int kSweepMaxBlocks = 8;
+// Bytes of LDS per wave with which the sweep kernel regroups column-major B^T
+// lines into MFMA operands (16 rows of 128 bytes; with 8 blocks of A a
+// work-group then takes 80 KB, two per CU).
+constexpr int kSweepCmScratch = 2048;
 // BCSR with 64x64 blocks, A-stationary: n_items block rows x n_ranges column
 // ranges of range_tiles tiles of p.tile_cols = 64 * (columns per lane) columns
 // (512 or 256; 256 with col_major), 4 waves, every block of a block row in LDS
 // (max_blocks <= kSweepMaxBlocks).
 hipError_t launch_bcsr64_sweep(int ab_dtype, int max_blocks, const TileParams &p, hipStream_t stream);
-size_t sweep_lds_bytes(int max_blocks, int ab_dtype);
+// Dynamic LDS of one sweep work-group: the CM scratch, then the A blocks.
+size_t sweep_lds_bytes(int max_blocks, int ab_dtype, bool col_major);
 // Work-groups of the sweep kernel resident per CU (0 if the query fails).
 int sweep_blocks_per_cu(int ab_dtype, int max_blocks, bool col_major, int cols_per_lane);
 // Most blocks in a block row that the pair kernel holds in registers.

@@ -838,12 +838,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
     constexpr int CPR = BC * ESZ / 16;             // 16-byte chunks per block row
     constexpr int CPB = R * CPR;                   // 16-byte chunks per block
     constexpr int MAXC = kSweepMaxBlocks * CPB / NT;  // chunks per thread, fullest row
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds_a[];
+    // CM: a per-wave scratch of 16 B^T rows x 128 bytes in front of the A blocks
+    constexpr int SCR = CM ? kSweepCmScratch : 0;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    uint8_t *const lds_a = lds_dyn + NW * SCR;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;
     const int li = lane & 15;
+    uint8_t *const scr = lds_dyn + wave * SCR;
 
     const uint32_t xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
     const uint32_t h = local / (uint32_t)p.n_items;
@@ -913,18 +917,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
         const bool jv = (t < ntiles) & (q < nblk) & (J < nbc);
         const uint32_t r0 = (jv ? J : 0u) * BC + (uint32_t)half * 32 + 8 * g;
         if constexpr (CM) {
-            // the whole block: B^T rows n = col_first + t*tile_cols + 16c, 32 bytes
-            // from k = J*64 + 16g (both halves of a 128-byte line arrive together);
-            // st.b[2c + hh] feeds half hh (`half` is unused)
-            const uint32_t k0 = (jv ? J : 0u) * BC + 16 * g;
-            const uint32_t base =
-                ((uint32_t)col_first + (uint32_t)t * (uint32_t)p.tile_cols) * ldb2 + k0 * 2;
+            // the whole block as whole 128-byte lines: load e brings B^T rows
+            // n_wave + 8e .. +7 (row n_wave + 8e + lane/8, the 16 bytes of k =
+            // J*64 + 8*(lane%8) .. +7), eight rows per instruction instead of
+            // sixteen half lines; compute_cm regroups them (`half` is unused)
+            const uint32_t n0 = (uint32_t)(col_first - li) + (uint32_t)t * (uint32_t)p.tile_cols +
+                                (uint32_t)(lane >> 3);
+            const uint32_t kq = (jv ? J : 0u) * BC + 8 * (uint32_t)(lane & 7);
 #pragma unroll
-            for (int c = 0; c < V; ++c)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    buf_load<DW>(rB, (jv & (k0 + 8 * hh < k32)) ? base + (uint32_t)(16 * c) * ldb2 + 16 * hh : kOOB,
-                                 st.b[2 * c + hh]);
+            for (int e = 0; e < 8; ++e)
+                buf_load<DW>(rB, (jv & (kq < k32)) ? (n0 + 8 * e) * ldb2 + kq * 2 : kOOB, st.b[e]);
         } else {
             const uint32_t base = r0 * ldb2 + (uint32_t)col_first * ESZ + (uint32_t)t * tile_bytes;
 #pragma unroll
@@ -947,30 +949,56 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
                 for (int mt = 0; mt < MT; ++mt)
                     acc[mt][c] = mfma16x16x32_fp8(af[mt], bf[c], acc[mt][c]);
         } else {
+        // row-major (column-major blocks go through compute_cm): lane group g of
+        // half `half` holds k = 32*half + 8g .. +7
         u32x4_t af[MT];
-        // CM: lane group g, half `half` holds k = 16g + 8*half .. +7 (row-major:
-        // 32*half + 8g .. +7); A is read with the same permutation of k
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             af[mt] = *reinterpret_cast<const u32x4_t *>(
-                lds_a + q * ABUF + (mt * 16 + li) * STRIDE +
-                (CM ? 16 * g + 8 * half : half * 32 + 8 * g) * 2);
+                lds_a + q * ABUF + (mt * 16 + li) * STRIDE + (half * 32 + 8 * g) * 2);
 #pragma unroll
         for (int c = 0; c < V; ++c) {
             u32x4_t bf;
-            if constexpr (CM) {
-                const int e = 2 * c + half;
-                bf = u32x4_t{st.b[e][0], st.b[e][1], st.b[e][2], st.b[e][3]};
-            } else {
-                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq)
-                    bf[qq] = __builtin_amdgcn_perm(st.b[2 * qq + 1][c >> 1], st.b[2 * qq][c >> 1], sel);
-            }
+            for (int qq = 0; qq < 4; ++qq)
+                bf[qq] = __builtin_amdgcn_perm(st.b[2 * qq + 1][c >> 1], st.b[2 * qq][c >> 1], sel);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 acc[mt][c] = mfma16x16x32<AB>(af[mt], bf, acc[mt][c]);
         }
+        }
+    };
+    // CM, one whole block: the eight loaded lines pass through the wave's
+    // scratch 16 rows (one column group c) at a time, written with the 16-byte
+    // chunk x of row r at slot x ^ (r % 8), so that the eight lanes of a read
+    // phase hit eight different slots, and come back as MFMA operands: lane
+    // (g, i) of half h reads chunk 4h + g of row i.  The scratch is private to
+    // the wave and LDS instructions of a wave complete in order: no barrier.
+    auto compute_cm = [&](const BStage<DW> &st, int q) {
+        u32x4_t af[2][MT];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                af[hh][mt] = *reinterpret_cast<const u32x4_t *>(
+                    lds_a + q * ABUF + (mt * 16 + li) * STRIDE + (hh * 32 + 8 * g) * 2);
+#pragma unroll
+        for (int c = 0; c < V; ++c) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                *reinterpret_cast<u32x4_t *>(scr + (8 * e + (lane >> 3)) * 128 +
+                                             (((lane & 7) ^ (lane >> 3)) * 16)) =
+                    u32x4_t{st.b[2 * c + e][0], st.b[2 * c + e][1], st.b[2 * c + e][2],
+                            st.b[2 * c + e][3]};
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const u32x4_t bf = *reinterpret_cast<const u32x4_t *>(
+                    scr + li * 128 + (((4 * hh + g) ^ (li & 7)) * 16));
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][c] = mfma16x16x32<AB>(af[hh][mt], bf, acc[mt][c]);
+            }
         }
     };
     // stores tile t (one branch on C's type per tile)
@@ -1013,16 +1041,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
             for (int q = 0; q < nblk; q += 2) {
                 issue_b(t, q + 1, 0, st1);
                 __builtin_amdgcn_sched_barrier(0);
-                compute(st0, q, 0);
-                compute(st0, q, 1);
+                compute_cm(st0, q);
                 __builtin_amdgcn_sched_barrier(0);
                 const bool last = q + 2 >= nblk;
                 issue_b(last ? t + 1 : t, last ? 0 : q + 2, 0, st0);
                 __builtin_amdgcn_sched_barrier(0);
-                if (q + 1 < nblk) {
-                    compute(st1, q + 1, 0);
-                    compute(st1, q + 1, 1);
-                }
+                if (q + 1 < nblk)
+                    compute_cm(st1, q + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
             store_tile(t);
@@ -1163,9 +1188,10 @@ hipError_t launch_bcsr64_lds(int ab, const TileParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-size_t sweep_lds_bytes(int max_blocks, int ab)
+size_t sweep_lds_bytes(int max_blocks, int ab, bool col_major)
 {
-    return (size_t)max_blocks * 64 * (64 * (ab == SPMM_FP8_E4M3 ? 1 : 2) + 16);
+    return (size_t)(col_major ? 4 * kSweepCmScratch : 0) +
+           (size_t)max_blocks * 64 * (64 * (ab == SPMM_FP8_E4M3 ? 1 : 2) + 16);
 }
 
 static const void *sweep_fn(int ab, bool cm, int v)
@@ -1188,14 +1214,14 @@ hipError_t launch_bcsr64_sweep(int ab, int max_blocks, const TileParams &p, hipS
     void *args[] = {&arg};
     return hipLaunchKernel(sweep_fn(ab, p.col_major != 0, p.tile_cols / 64),
                            dim3((unsigned)(p.n_items * p.n_ranges)), dim3(256), args,
-                           sweep_lds_bytes(max_blocks, ab), stream);
+                           sweep_lds_bytes(max_blocks, ab, p.col_major != 0), stream);
 }
 
 int sweep_blocks_per_cu(int ab, int max_blocks, bool col_major, int v)
 {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sweep_fn(ab, col_major, v), 256,
-                                                     sweep_lds_bytes(max_blocks, ab)) != hipSuccess)
+                                                     sweep_lds_bytes(max_blocks, ab, col_major)) != hipSuccess)
         return 0;
     return n;
 }
