@@ -214,10 +214,10 @@ typedef struct {
                                 the default) or 4 (256-column tiles; FP16/BF16 only, and
                                 the only choice with col_major) */
     int32_t waves_n;         /* 0 auto; kernel 0: 1, 2 or 4 waves across the tile's
-                                columns; kernel 1: 1, 2, 4 or 8 waves of 128 columns (1
-                                only when pinned: one wave per block row and tile; 8 only
-                                when pinned with kernel 1 and row-major, or chosen by the
-                                plan at N >= 8192) */
+                                columns; kernel 1: 1, 2, 4 or 8 waves of 128 columns (64
+                                with col_major) (1 only when pinned: one wave per block
+                                row and tile; 8 only when pinned with kernel 1, or chosen
+                                by the plan at N >= 8192) */
     int32_t waves_k;         /* 0 auto; kernel 0: 1, 2 or 4 waves splitting the packed
                                 columns, waves_n * waves_k <= 4 */
     int32_t distribution;    /* -1 auto; kernel 0: 0 planned per-work-group task lists,

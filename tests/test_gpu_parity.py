@@ -692,6 +692,8 @@ COL_MAJOR_CASES = [
     (1000, 520, 1288, 0.3, "bf16", "bf16", {"kernel": 1, "waves_n": 4}),
     (1000, 520, 1288, 0.3, "fp16", "fp32", {"kernel": 1, "waves_n": 2}),
     (520, 640, 200, 0.3, "bf16", "fp32", {"kernel": 1, "waves_n": 1}),
+    (1000, 520, 1288, 0.3, "bf16", "bf16", {"kernel": 1, "waves_n": 8}),
+    (712, 1096, 4104, 0.45, "fp16", "fp32", {"kernel": 1, "waves_n": 8}),
     (1280, 640, 4104, 0.25, "bf16", "bf16", {"kernel": 2, "ranges_per_xcd": 1}),
     (704, 576, 8200, 0.3, "bf16", "fp16", {"kernel": 2, "ranges_per_xcd": 2}),
     (640, 512, 4096, 0.95, "fp16", "fp32", {"kernel": 2}),

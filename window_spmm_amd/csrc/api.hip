@@ -63,13 +63,13 @@ spmm_status_t check_options(const spmm_plan_options_t &o, bool bcsr)
                     o.kernel);
     if (o.cols_per_lane != 0 && o.cols_per_lane != 2 && o.cols_per_lane != 4 && o.cols_per_lane != 8)
         return fail(SPMM_ERR_INVALID_ARGUMENT, "options.cols_per_lane must be 0, 2, 4 or 8");
-    // waves_n 8: the LDS-A kernel's 1024-column tiles (kernel 1 pinned, row-major)
-    const bool lds8 = o.kernel == 1 && o.waves_n == 8 && o.waves_k == 0 && !o.col_major;
+    // waves_n 8: the LDS-A kernel's 8-wave tiles (kernel 1 pinned)
+    const bool lds8 = o.kernel == 1 && o.waves_n == 8 && o.waves_k == 0;
     if (!lds8 && (o.waves_n < 0 || o.waves_n > 4 || o.waves_n == 3 || o.waves_k < 0 || o.waves_k > 4 ||
                   o.waves_k == 3 || std::max(1, o.waves_n) * std::max(1, o.waves_k) > 4))
         return fail(SPMM_ERR_INVALID_ARGUMENT,
                     "options.waves_n and waves_k must be 0, 1, 2 or 4 with a product of at most 4 "
-                    "(waves_n 8 only with kernel 1, row-major)");
+                    "(waves_n 8 only with kernel 1)");
     if (o.distribution < -1 || o.distribution > 1 || o.row_order < -1 || o.row_order > 1 ||
         o.order < -1 || o.order > 1)
         return fail(SPMM_ERR_INVALID_ARGUMENT, "options.distribution, row_order and order must be -1, 0 or 1");
@@ -1020,14 +1020,17 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         // block row) 1616-1619 against 1661-1665 us with 512-column tiles (half
         // the A loads and barriers per column); on the gate_proj shape at 80 %
         // block sparsity (11 blocks per block row) 2388-2398 against 2361-2363 us
+        // Column-major: 4 columns per lane (a whole block of B^T lines per
+        // stage), 8 waves from N = 8192, so that a tile is 512 columns wide.
         const double mean_blocks = (double)h_block_row_ptr[nbr] / (double)std::max<int64_t>(1, nbr);
         const int nw = opt.waves_n > 0 ? opt.waves_n
-                       : (N >= 8192 && !opt.col_major && mean_blocks >= 16.0) ? 8 : 4;
+                       : opt.col_major ? (N >= 8192 ? 8 : 4)
+                       : (N >= 8192 && mean_blocks >= 16.0) ? 8 : 4;
         pl->n_items = nbr;
-        pl->V = 8;
+        pl->V = opt.col_major ? 4 : 8;
         pl->waves_n = nw;
         pl->waves_k = 1;
-        pl->tile_cols = 128 * nw;
+        pl->tile_cols = 16 * pl->V * nw;
         pl->n_col_tiles = ceil_div(N, pl->tile_cols);
         pl->workspace = 0;
         pl->order = opt.order > 0 ? 1 : 0;

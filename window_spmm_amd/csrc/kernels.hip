@@ -631,19 +631,19 @@ __global__ __launch_bounds__(256, 2) void spmm_tile_kernel(TileParams p)
     finish(prev, true);
 }
 
-// BCSR with 64 x 64 blocks and a wide column tile (NW waves x 128 columns).
+// BCSR with 64 x 64 blocks and a wide column tile (NW waves x 16V columns).
 // Same MFMA mapping and B pipeline as spmm_tile_kernel, but the A block is
-// shared: the work-group loads each 64 x 64 block once (non-temporal, it is
-// streamed) into one of two padded LDS buffers, and every wave reads its A
-// fragments from there.  Block-column indices are work-group uniform and come
-// through scalar loads.  One LDS barrier per block.  CM: column-major B and C
-// (B^T and C^T row-major): each lane's 16-byte load of a B^T row already is
-// its MFMA B operand, no register transpose.
+// shared: the work-group loads each 64 x 64 block once into one of two LDS
+// buffers (MFMA fragment order), and every wave reads its A fragments from
+// there.  Block-column indices are work-group uniform and come through scalar
+// loads.  One LDS barrier per block.  CM: column-major B and C (B^T and C^T
+// row-major), 4 columns per lane: a whole block of B^T lines per stage,
+// regrouped through a per-wave LDS scratch as in bcsr64_sweep_kernel.
 template <int AB, int NW, bool CM>
 __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
                                                              const int32_t *__restrict__ block_cols)
 {
-    constexpr int R = 64, BC = 64, MT = 4, V = 8, DW = 4;
+    constexpr int R = 64, BC = 64, MT = 4, V = CM ? 4 : 8, DW = 4;
     constexpr int NT = NW * 64;                    // threads per work-group
     // A buffers in MFMA fragment order: the 16 bytes lane l = 16g + i reads for
     // (k half h, row slice mt) -- row 16mt + i, k = 32h + 8g .. +7 -- sit at
@@ -653,6 +653,7 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
     constexpr int ABUF = R * BC * 2;               // bytes of one A buffer
     constexpr int CPT = R * BC / 8 / NT;           // 16-byte chunks per thread per block
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * ABUF];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scr[CM ? NW * kSweepCmScratch : 16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -718,13 +719,17 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
     // a multiple of 8: a lane's eight values are all inside B or all past it)
     auto issue_b = [&](int s, uint32_t J, BStage<DW> &st) {
         const bool jv = J < nbc;
-        const uint32_t r0 = (jv ? J : 0u) * BC + (uint32_t)(s & 1) * 32 + 8 * g;
         if constexpr (CM) {
-            const uint32_t base = (uint32_t)li * ldb2 + r0 * 2;
+            // the whole block of the wave's 64 B^T rows as 8 whole 128-byte
+            // lines per load: load e brings rows 8e .. 8e+7 (row 8e + lane/8,
+            // the 16 bytes of k = J*64 + 8*(lane%8) .. +7); `s` is unused
+            const uint32_t kq = (jv ? J : 0u) * BC + 8 * (uint32_t)(lane & 7);
+            const uint32_t base = (uint32_t)(lane >> 3) * ldb2 + kq * 2;
 #pragma unroll
-            for (int c = 0; c < V; ++c)
-                buf_load<DW>(rB, (jv & (r0 < k32)) ? base + (uint32_t)(16 * c) * ldb2 : kOOB, st.b[c]);
+            for (int e = 0; e < 8; ++e)
+                buf_load<DW>(rB, (jv & (kq < k32)) ? base + (uint32_t)(8 * e) * ldb2 : kOOB, st.b[e]);
         } else {
+            const uint32_t r0 = (jv ? J : 0u) * BC + (uint32_t)(s & 1) * 32 + 8 * g;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t r = r0 + j;
@@ -741,21 +746,76 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
 #pragma unroll
         for (int c = 0; c < V; ++c) {
             u32x4_t bf;
-            if constexpr (CM) {
-                bf = u32x4_t{st.b[c][0], st.b[c][1], st.b[c][2], st.b[c][3]};
-            } else {
-                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    bf[q] = __builtin_amdgcn_perm(st.b[2 * q + 1][c >> 1], st.b[2 * q][c >> 1], sel);
-            }
+            for (int q = 0; q < 4; ++q)
+                bf[q] = __builtin_amdgcn_perm(st.b[2 * q + 1][c >> 1], st.b[2 * q][c >> 1], sel);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 acc[mt][c] = mfma16x16x32<AB>(af[mt], bf, acc[mt][c]);
         }
     };
+    // CM, one whole block from buffer `buf`: the lines of column group c (16
+    // rows) pass through the wave's scratch, chunk x of row r at slot
+    // x ^ (r % 8), and lane (g, i) of half h reads chunk 4h + g of row i (no
+    // bank conflicts within an 8-lane read phase; the scratch is the wave's
+    // own and its LDS instructions complete in order)
+    uint8_t *const scr = lds_scr + (CM ? wave * kSweepCmScratch : 0);
+    auto compute_cm = [&](const BStage<DW> &st, int buf) {
+        u32x4_t af[2][MT];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                af[hh][mt] = *reinterpret_cast<const u32x4_t *>(lds_a + buf * ABUF +
+                                                               ((hh * MT + mt) * 64 + lane) * 16);
+#pragma unroll
+        for (int c = 0; c < V; ++c) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                *reinterpret_cast<u32x4_t *>(scr + (8 * e + (lane >> 3)) * 128 +
+                                             (((lane & 7) ^ (lane >> 3)) * 16)) =
+                    u32x4_t{st.b[2 * c + e][0], st.b[2 * c + e][1], st.b[2 * c + e][2],
+                            st.b[2 * c + e][3]};
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const u32x4_t bf = *reinterpret_cast<const u32x4_t *>(
+                    scr + li * 128 + (((4 * hh + g) ^ (li & 7)) * 16));
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][c] = mfma16x16x32<AB>(af[hh][mt], bf, acc[mt][c]);
+            }
+        }
+    };
 
-    if (nblk > 0) {
+    if (CM && nblk > 0) {
+        // two blocks per iteration: st0 and A buffer 0 hold block q, st1 and
+        // buffer 1 block q + 1 (past the row's end: zeros, not computed); every
+        // path issues the same loads, which keeps the wait counts exact
+        u32x4_t areg[CPT];
+        BStage<DW> st0, st1;
+        load_a(0, areg);
+        issue_b(0, block_col(0), st0);
+        store_a(0, areg);
+        lds_barrier();
+        for (int q = 0; q < nblk; q += 2) {
+            issue_b(0, block_col(q + 1), st1);
+            load_a(q + 1 < nblk ? q + 1 : q, areg);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_cm(st0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            store_a(1, areg);
+            lds_barrier();
+            issue_b(0, block_col(q + 2), st0);
+            load_a(q + 2 < nblk ? q + 2 : q, areg);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q + 1 < nblk)
+                compute_cm(st1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            store_a(0, areg);
+            lds_barrier();
+        }
+    } else if (nblk > 0) {
         u32x4_t areg[CPT];
         BStage<DW> st0, st1;
         uint32_t Jcur = block_col(0);
@@ -1179,6 +1239,7 @@ hipError_t launch_bcsr64_lds(int ab, const TileParams &p, hipStream_t stream)
     if (p.col_major)
         p.waves_n == 1   ? launch_lds_nw<1, true>(ab, p, stream)
         : p.waves_n == 2 ? launch_lds_nw<2, true>(ab, p, stream)
+        : p.waves_n == 8 ? launch_lds_nw<8, true>(ab, p, stream)
                          : launch_lds_nw<4, true>(ab, p, stream);
     else
         p.waves_n == 1   ? launch_lds_nw<1, false>(ab, p, stream)
