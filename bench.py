@@ -94,13 +94,39 @@ KERNEL_SOURCES = [os.path.join(ROOT, "window_spmm_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def code_only(text: str) -> str:
+    """C/C++ source without its comments and blank lines, each line stripped:
+    what a traffic record depends on (a comment edit leaves the code, and so
+    the counters, as they were).  String and character literals are kept."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(l.strip() for l in "".join(out).splitlines() if l.strip())
+
+
 def kernel_source_sha256() -> str:
-    """One hash over the kernel and planner sources: a traffic record counts only
-    while it matches."""
+    """One hash over the code (comments and blank lines left out) of the kernel
+    and planner sources: a traffic record counts only while it matches."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode("utf-8"))
     return h.hexdigest()
 
 

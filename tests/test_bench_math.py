@@ -54,3 +54,15 @@ def test_roofline_time_takes_the_larger_bound():
     assert abs(bench.roofline_time(p, alg) - 2e-3) < 1e-12
     alg = {"flops_stored": 5e11, "bytes_alg": 8e9}
     assert abs(bench.roofline_time(p, alg) - 1e-3) < 1e-12
+
+
+def test_traffic_key_ignores_comments_but_not_code():
+    # the key of a traffic record follows the code: comments, blank lines and
+    # indentation do not count, literals that look like comments do
+    src = 'int f(int x) {\n    return x + 1; // one\n}\n'
+    assert bench.code_only(src) == bench.code_only('/* doc */\nint f(int x) {\n\n  return x + 1;\n}')
+    assert bench.code_only(src) != bench.code_only(src.replace("x + 1", "x + 2"))
+    lit = 'const char *s = "a // b /* c */"; char q = \'/\';'
+    assert bench.code_only(lit) == lit
+    assert bench.code_only('a /* x */ b') == 'a   b'
+    assert len(bench.kernel_source_sha256()) == 64

@@ -714,9 +714,9 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
         const uint32_t J = (uint32_t)block_cols[at];
         return q < nblk ? J : 0xFFFFFFFFu;
     };
-    // k' step s of block column J (half s%2): row-major, B rows J*64 + 32*(s%2) +
-    // 8g + j; CM, columns 16c + i of B^T rows from k = J*64 + 32*(s%2) + 8g (k is
-    // a multiple of 8: a lane's eight values are all inside B or all past it)
+    // Row-major: k' step s of block column J (half s%2), B rows J*64 + 32*(s%2) +
+    // 8g + j.  CM: the whole block (k is a multiple of 8: a lane's eight values
+    // are all inside B^T's row or all past it).
     auto issue_b = [&](int s, uint32_t J, BStage<DW> &st) {
         const bool jv = J < nbc;
         if constexpr (CM) {
@@ -737,6 +737,7 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
             }
         }
     };
+    // row-major half-block (column-major blocks go through compute_cm)
     auto compute = [&](const BStage<DW> &st, int buf, int half) {
         u32x4_t af[MT];
 #pragma unroll
