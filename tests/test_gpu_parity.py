@@ -726,6 +726,36 @@ def test_bcsr64_col_major(ws, case):
     check(p, np.ascontiguousarray(got[:, :m].T))
 
 
+@pytest.mark.parametrize("which", ["gate", "down"])
+def test_config4_col_major_sampled(ws, which):
+    """Config 4's gate and down weights at the full N = 65536 with column-major
+    B and C (B^T 65536 x k, C^T 65536 x m, rows allocated with the recommended
+    leading dimension), the launch configuration `bench.py --col-major` times:
+    every element of C^T written, sampled rows of C (each across all 65536
+    columns) against the oracle."""
+    p = synth.config4(which)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, options={"col_major": 1})
+    info = A.plan.info()
+    _say("gpu case: config 4 column-major", which, info)
+    assert info["col_major"] == 1 and info["kernel"] == (2 if which == "gate" else 1)
+    ldb, ldc = ws.recommended_ld(p.k, 2), ws.recommended_ld(p.m, 2)
+    bt = np.zeros((p.N, ldb), dtype=np.uint16)
+    bt[:, :p.k] = p.B.T
+    Bt = torch.from_numpy(bt.view(np.int16)).cuda()[:, :p.k]
+    del bt
+    Ct = torch.full((p.N, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")[:, :p.m]
+    A.run(Bt, Ct)
+    torch.cuda.synchronize()
+    assert not torch.isnan(Ct).any().item()
+    rows = _block_rows_sample(p, 7 if which == "gate" else 8)
+    got = np.full((p.m, p.N), np.nan)
+    got[rows] = Ct[:, torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64).T
+    check(p, got, rows=rows)
+    del A, Bt, Ct
+    torch.cuda.empty_cache()
+
+
 def test_col_major_rejected_where_unsupported(ws):
     p = synth.block_problem(200, 150, 72, 32, 16, 0.3, seed=1, ab_dtype="bf16", c_dtype="fp32")
     with pytest.raises(ws.SpmmError, match="UNSUPPORTED"):
