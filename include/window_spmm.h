@@ -217,7 +217,9 @@ typedef struct {
                                 columns; kernel 1: 1, 2, 4 or 8 waves of 128 columns (64
                                 with col_major) (1 only when pinned: one wave per block
                                 row and tile; 8 only when pinned with kernel 1, or chosen
-                                by the plan at N >= 8192) */
+                                by the plan at N >= 8192); kernel 2 with col_major: 8
+                                (pinned) for 8 waves of 64 columns, 512-column tiles,
+                                instead of 4 (256-column tiles, the default) */
     int32_t waves_k;         /* 0 auto; kernel 0: 1, 2 or 4 waves splitting the packed
                                 columns, waves_n * waves_k <= 4 */
     int32_t distribution;    /* -1 auto; kernel 0: 0 planned per-work-group task lists,

@@ -697,6 +697,9 @@ COL_MAJOR_CASES = [
     (1280, 640, 4104, 0.25, "bf16", "bf16", {"kernel": 2, "ranges_per_xcd": 1}),
     (704, 576, 8200, 0.3, "bf16", "fp16", {"kernel": 2, "ranges_per_xcd": 2}),
     (640, 512, 4096, 0.95, "fp16", "fp32", {"kernel": 2}),
+    (1280, 640, 4104, 0.25, "bf16", "bf16", {"kernel": 2, "waves_n": 8, "ranges_per_xcd": 1}),
+    (704, 576, 8200, 0.3, "fp16", "fp32", {"kernel": 2, "waves_n": 8}),
+    (640, 512, 4096, 0.95, "bf16", "fp16", {"kernel": 2, "waves_n": 8}),
 ]
 
 

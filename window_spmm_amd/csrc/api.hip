@@ -63,13 +63,15 @@ spmm_status_t check_options(const spmm_plan_options_t &o, bool bcsr)
                     o.kernel);
     if (o.cols_per_lane != 0 && o.cols_per_lane != 2 && o.cols_per_lane != 4 && o.cols_per_lane != 8)
         return fail(SPMM_ERR_INVALID_ARGUMENT, "options.cols_per_lane must be 0, 2, 4 or 8");
-    // waves_n 8: the LDS-A kernel's 8-wave tiles (kernel 1 pinned)
-    const bool lds8 = o.kernel == 1 && o.waves_n == 8 && o.waves_k == 0;
+    // waves_n 8: the LDS-A kernel's 8-wave tiles (kernel 1 pinned), or the sweep
+    // kernel's column-major 8-wave tiles (kernel 2 pinned, col_major)
+    const bool lds8 = (o.kernel == 1 || (o.kernel == 2 && o.col_major == 1)) && o.waves_n == 8 &&
+                      o.waves_k == 0;
     if (!lds8 && (o.waves_n < 0 || o.waves_n > 4 || o.waves_n == 3 || o.waves_k < 0 || o.waves_k > 4 ||
                   o.waves_k == 3 || std::max(1, o.waves_n) * std::max(1, o.waves_k) > 4))
         return fail(SPMM_ERR_INVALID_ARGUMENT,
                     "options.waves_n and waves_k must be 0, 1, 2 or 4 with a product of at most 4 "
-                    "(waves_n 8 only with kernel 1)");
+                    "(waves_n 8 only with kernel 1, or kernel 2 with col_major)");
     if (o.distribution < -1 || o.distribution > 1 || o.row_order < -1 || o.row_order > 1 ||
         o.order < -1 || o.order > 1)
         return fail(SPMM_ERR_INVALID_ARGUMENT, "options.distribution, row_order and order must be -1, 0 or 1");
@@ -818,9 +820,12 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
     // kernel 2 runs 8 columns per lane (512-column tiles), or 4 with col_major
     // or when the options ask for them (256-column tiles, 16-bit inputs)
     const int sweep_v = opt.col_major || opt.cols_per_lane == 4 ? 4 : 8;
+    // column-major: 4 waves (256-column tiles, two work-groups per CU) or, as an
+    // option, 8 waves (512-column tiles, one work-group per CU)
+    const int sweep_nw = opt.col_major && opt.waves_n == 8 ? 8 : 4;
     const bool sweep_fits = b64 && max_blocks <= kSweepMaxBlocks && tiles512 >= 8 &&
-                            sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks),
-                                                opt.col_major != 0, sweep_v) >= 2;
+                            sweep_blocks_per_cu(ab_dtype, std::max(1, max_blocks), opt.col_major != 0,
+                                                sweep_v, sweep_nw) >= (sweep_nw == 8 ? 1 : 2);
     const bool sweep_auto = sweep_fits && tiles512 >= 16;
     // Kernel 3 holds a block row's A in the registers of two waves: at most
     // kPairMaxBlocks blocks per block row, 16-bit inputs, row-major operands,
@@ -912,9 +917,9 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         }
         pl->n_items = nbr;
         pl->V = sweep_v;
-        pl->waves_n = 4;
+        pl->waves_n = sweep_nw;
         pl->waves_k = 1;
-        pl->tile_cols = 64 * sweep_v;
+        pl->tile_cols = 16 * sweep_v * sweep_nw;
         pl->n_col_tiles = ceil_div(N, pl->tile_cols);
         pl->workspace = 0;
         pl->order = 0;
@@ -987,9 +992,9 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         }
         pl->n_items = nbr;
         pl->V = sweep_v;
-        pl->waves_n = 4;
+        pl->waves_n = sweep_nw;
         pl->waves_k = 1;
-        pl->tile_cols = 64 * sweep_v;
+        pl->tile_cols = 16 * sweep_v * sweep_nw;
         pl->n_col_tiles = ceil_div(N, pl->tile_cols);
         pl->workspace = 0;
         pl->order = 0;
@@ -1191,6 +1196,12 @@ std::vector<spmm_plan_options_t> tune_candidates(const spmm_plan_options_t &base
             for (int h : {1, 2, 4, 8, 16}) {
                 spmm_plan_options_default(&o);
                 o.kernel = 2; o.cols_per_lane = cpl; o.ranges_per_xcd = h;
+                add(o);
+            }
+        if (base.col_major == 1)   // the sweep kernel's 8-wave column-major tiles
+            for (int h : {1, 2, 4, 8, 16}) {
+                spmm_plan_options_default(&o);
+                o.kernel = 2; o.waves_n = 8; o.ranges_per_xcd = h;
                 add(o);
             }
         for (int kern : {3, 4})

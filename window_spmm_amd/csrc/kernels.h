@@ -74,14 +74,16 @@ constexpr int kSweepMaxBlocks = 8;
 // work-group then takes 80 KB, two per CU).
 constexpr int kSweepCmScratch = 2048;
 // BCSR with 64x64 blocks, A-stationary: n_items block rows x n_ranges column
-// ranges of range_tiles tiles of p.tile_cols = 64 * (columns per lane) columns
-// (512 or 256; 256 with col_major), 4 waves, every block of a block row in LDS
+// ranges of range_tiles tiles of p.tile_cols = 16 * (columns per lane) * waves columns
+// (512 or 256; 256 with col_major and 4 waves), 4 waves (8 with col_major and
+// p.waves_n = 8: 512-column tiles), every block of a block row in LDS
 // (max_blocks <= kSweepMaxBlocks).
 hipError_t launch_bcsr64_sweep(int ab_dtype, int max_blocks, const TileParams &p, hipStream_t stream);
-// Dynamic LDS of one sweep work-group: the CM scratch, then the A blocks.
-size_t sweep_lds_bytes(int max_blocks, int ab_dtype, bool col_major);
-// Work-groups of the sweep kernel resident per CU (0 if the query fails).
-int sweep_blocks_per_cu(int ab_dtype, int max_blocks, bool col_major, int cols_per_lane);
+// Dynamic LDS of one sweep work-group of `waves` waves: the CM scratch, then the A blocks.
+size_t sweep_lds_bytes(int max_blocks, int ab_dtype, bool col_major, int waves);
+// Work-groups of the sweep kernel resident per CU (0 if the query fails); waves
+// per work-group 4, or 8 (column-major only, p.waves_n = 8).
+int sweep_blocks_per_cu(int ab_dtype, int max_blocks, bool col_major, int cols_per_lane, int waves);
 // Most blocks in a block row that the pair kernel holds in registers.
 constexpr int kPairMaxBlocks = 6;
 // BCSR with 64x64 blocks, A in the registers of a wave pair: n_items block rows x

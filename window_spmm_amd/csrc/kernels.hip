@@ -878,7 +878,7 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
 // and C, as in bcsr64_lds_kernel.  VR: row-major columns per lane (8, or 4 for
 // 256-column tiles, whose B column slices take half the L2).
 template <int AB, int NW, bool CM, int VR>
-__global__ __launch_bounds__(NW * 64, 2) void bcsr64_sweep_kernel(TileParams p)
+__global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bcsr64_sweep_kernel(TileParams p)
 {
     // CM: 4 columns per lane, so that a whole block of B^T (both halves) fits
     // one ring stage.  F8: one-byte codes (8 columns per lane = 2 dwords per row)
@@ -1250,16 +1250,19 @@ hipError_t launch_bcsr64_lds(int ab, const TileParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-size_t sweep_lds_bytes(int max_blocks, int ab, bool col_major)
+size_t sweep_lds_bytes(int max_blocks, int ab, bool col_major, int waves)
 {
-    return (size_t)(col_major ? 4 * kSweepCmScratch : 0) +
+    return (size_t)(col_major ? waves * kSweepCmScratch : 0) +
            (size_t)max_blocks * 64 * (64 * (ab == SPMM_FP8_E4M3 ? 1 : 2) + 16);
 }
 
-static const void *sweep_fn(int ab, bool cm, int v)
+static const void *sweep_fn(int ab, bool cm, int v, int waves)
 {
     if (ab == SPMM_FP8_E4M3)
         return reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP8_E4M3, 4, false, 8>);
+    if (cm && waves == 8)
+        return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 8, true, 8>)
+                               : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 8, true, 8>);
     if (cm)
         return ab == SPMM_FP16 ? reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_FP16, 4, true, 8>)
                                : reinterpret_cast<const void *>(bcsr64_sweep_kernel<SPMM_BF16, 4, true, 8>);
@@ -1274,16 +1277,17 @@ hipError_t launch_bcsr64_sweep(int ab, int max_blocks, const TileParams &p, hipS
 {
     TileParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel(sweep_fn(ab, p.col_major != 0, p.tile_cols / 64),
-                           dim3((unsigned)(p.n_items * p.n_ranges)), dim3(256), args,
-                           sweep_lds_bytes(max_blocks, ab, p.col_major != 0), stream);
+    const int waves = p.waves_n == 8 ? 8 : 4;
+    return hipLaunchKernel(sweep_fn(ab, p.col_major != 0, p.tile_cols / (16 * waves), waves),
+                           dim3((unsigned)(p.n_items * p.n_ranges)), dim3(64 * waves), args,
+                           sweep_lds_bytes(max_blocks, ab, p.col_major != 0, waves), stream);
 }
 
-int sweep_blocks_per_cu(int ab, int max_blocks, bool col_major, int v)
+int sweep_blocks_per_cu(int ab, int max_blocks, bool col_major, int v, int waves)
 {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sweep_fn(ab, col_major, v), 256,
-                                                     sweep_lds_bytes(max_blocks, ab, col_major)) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sweep_fn(ab, col_major, v, waves), 64 * waves,
+                                                     sweep_lds_bytes(max_blocks, ab, col_major, waves)) != hipSuccess)
         return 0;
     return n;
 }
