@@ -940,79 +940,21 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         //  - one-tile ranges win at 3-6 blocks from 96 tiles on (6 blocks, N =
         //    65536: 1300 us against 1525 with four tiles; 3 blocks: 885 against
         //    1077) and at 3 blocks from 48 tiles on (N = 32768: 445 against 467).
-        // Column-major plans (256-column tiles) keep the one-tile rule from 128
-        // tiles and 3 blocks, and N / 4096 ranges per XCD below, the rule they
-        // were measured with.
+        // Column-major plans (256-column tiles) count the rule in 512-column
+        // units, so that a range spans the columns a row-major range would: on
+        // gate_proj two 256-column tiles per range ran 1398-1440 us cold against
+        // 1533-1573 us for one (and 1436-1441 us for four).
         const double mean_blocks = (double)h_block_row_ptr[nbr] / (double)std::max<int64_t>(1, nbr);
-        const int64_t tiles = pl->n_col_tiles;
+        const int64_t tiles = opt.col_major ? ceil_div(N, (int64_t)512) : pl->n_col_tiles;
         int64_t h;
         if (opt.ranges_per_xcd > 0) {
             h = opt.ranges_per_xcd;
-        } else if (opt.col_major) {
-            h = tiles >= 128 && max_blocks >= 3 ? std::min<int64_t>(64, tiles / 8)
-                                                : std::max<int64_t>(1, std::min<int64_t>(64, tiles / 16));
         } else {
             const bool one_tile = mean_blocks >= 2.5 && ((mean_blocks <= 6.5 && tiles >= 96) ||
                                                          (mean_blocks <= 3.5 && tiles >= 48));
             h = one_tile ? std::min<int64_t>(64, ceil_div(tiles, 8))
                          : std::max<int64_t>(1, std::min<int64_t>(mean_blocks > 6.5 ? 2 : 64, tiles / 32));
         }
-        pl->n_ranges = 8 * h;
-        pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
-    } else if (pl->kernel == 3) {
-        if (opt.cols_per_lane != 0 && opt.cols_per_lane != 8) {
-            free_plan(pl);
-            return fail(SPMM_ERR_UNSUPPORTED, "kernel 3 runs 8 columns per lane");
-        }
-        pl->n_items = nbr;
-        pl->V = 8;
-        pl->waves_n = 1;
-        pl->waves_k = 2;
-        pl->tile_cols = 128;
-        pl->n_col_tiles = ceil_div(N, 128);
-        pl->workspace = 0;
-        pl->order = 0;
-        // ranges of eight 128-column strips by default (a block row's A is
-        // loaded once per range)
-        const int64_t h = opt.ranges_per_xcd > 0
-                              ? opt.ranges_per_xcd
-                              : std::max<int64_t>(1, std::min<int64_t>(64, pl->n_col_tiles / 64));
-        pl->n_ranges = 8 * h;
-        pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
-    } else if (pl->kernel == 2) {
-        // column-major: 4 columns per lane (a whole block of B^T per ring stage)
-        if (opt.cols_per_lane != 0 && opt.cols_per_lane != sweep_v) {
-            free_plan(pl);
-            return fail(SPMM_ERR_UNSUPPORTED, "kernel 2 runs 8 or 4 columns per lane (4 with "
-                                              "col_major, 8 with FP8_E4M3)");
-        }
-        if (ab_dtype == SPMM_FP8_E4M3 && sweep_v != 8) {
-            free_plan(pl);
-            return fail(SPMM_ERR_UNSUPPORTED, "kernel 2 runs FP8_E4M3 with 8 columns per lane");
-        }
-        pl->n_items = nbr;
-        pl->V = sweep_v;
-        pl->waves_n = sweep_nw;
-        pl->waves_k = 1;
-        pl->tile_cols = 16 * sweep_v * sweep_nw;
-        pl->n_col_tiles = ceil_div(N, pl->tile_cols);
-        pl->workspace = 0;
-        pl->order = 0;
-        // Range length.  Longer ranges amortise the A load over more tiles but
-        // let the work-groups of an XCD drift apart, so that fewer of them share
-        // each B tile in L2.  Measured (interleaved runs on one box, the gate_proj
-        // shape at 90 % block sparsity): at N = 65536 (128 tiles) ranges of one
-        // tile ran 1287-1319 us cold against 1357-1361 us for two (up_proj
-        // 1290-1310 against 1338-1345 us; 95 % sparsity 901-906 against
-        // 947-954 us; N = 131072 2657-2660 against 2734-2736 us), but with one
-        // block per block row (99 %) two tiles stay better (688-693 against
-        // 742-744 us); at N = 16384 and 32768 (32 and 64 tiles) ranges of two
-        // to four tiles are best (367-378 us against 440 and 569 us for four
-        // and one; 614-619 us for four against 650-672 for two).
-        const int64_t h = opt.ranges_per_xcd > 0 ? opt.ranges_per_xcd
-                          : pl->n_col_tiles >= 128 && max_blocks >= 3
-                              ? std::min<int64_t>(64, pl->n_col_tiles / 8)
-                              : std::max<int64_t>(1, std::min<int64_t>(64, pl->n_col_tiles / 16));
         pl->n_ranges = 8 * h;
         pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
     } else if (pl->kernel == 1) {
