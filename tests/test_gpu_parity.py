@@ -1219,6 +1219,65 @@ def test_b_at_the_32bit_offset_limit(ws, fmt, opts):
     torch.cuda.empty_cache()
 
 
+# Column-major: B^T rows of k = 3584 (7168 bytes, the recommended leading
+# dimension), the largest N, a multiple of 8, with N * 7168 below 2^32 - 256:
+# B^T is 4.29 GB.
+N_CM_AT_LIMIT = 599184
+
+
+@pytest.mark.parametrize("kernel", [2, 1])
+def test_col_major_b_at_the_32bit_offset_limit(ws, kernel):
+    """Column-major B^T of 4.29 GB whose last rows sit just below the 2^32 - 256
+    byte limit of the kernels' buffer offsets (the whole-line B^T loads address
+    rows as row x pitch in 32 bits): A has blocks in the first, a middle and the
+    last block columns; sampled columns of C, the last ones among them, are
+    compared with the oracle on those columns of B."""
+    m, k, N = 128, 3584, N_CM_AT_LIMIT
+    ldb = ws.recommended_ld(k, 2)
+    assert ldb == k and N * ldb * 2 < 2 ** 32 - 256 <= (N + 8) * ldb * 2
+    nbc = k // 64
+    blocks = [[0, nbc // 2, nbc - 1], [1, nbc - 2, nbc - 1]]
+    rows, cols = [], []
+    for br, js in enumerate(blocks):
+        for r in range(64 * br, 64 * br + 64):
+            for J in js:
+                rows.append(np.full(64, r))
+                cols.append(np.arange(J * 64, J * 64 + 64))
+    rows, cols = np.concatenate(rows), np.concatenate(cols)
+    row_ptr = np.zeros(m + 1, np.int64)
+    np.add.at(row_ptr, rows + 1, 1)
+    row_ptr = np.cumsum(row_ptr).astype(np.int32)
+    v = np.random.default_rng(23).normal(0.0, 1.0, cols.size)
+    v[v == 0] = 1.0
+    vals = synth.bf16_bits(v)
+    _say("gpu case: column-major B^T at the offset limit, kernel", kernel, "N", N)
+    Bt = torch.empty((N, ldb), dtype=torch.int16, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    for n0 in range(0, N, 65536):
+        n1 = min(N, n0 + 65536)
+        Bt[n0:n1] = torch.randn((n1 - n0, k), generator=gen, device="cuda",
+                                dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+    A = ws.DeviceSparse("bcsr", m, k, N, row_ptr, cols.astype(np.int32), vals, 64, 64, "bf16",
+                        "fp32", options={"kernel": kernel, "col_major": 1})
+    assert A.plan.info()["kernel"] == kernel and A.plan.info()["col_major"] == 1
+    Ct = torch.full((N, ws.recommended_ld(m, 4)), float("nan"), dtype=torch.float32,
+                    device="cuda")[:, :m]
+    A.run(Bt, Ct)
+    torch.cuda.synchronize()
+    assert not torch.isnan(Ct).any().item()
+    sample = np.unique(np.concatenate([np.arange(8), np.arange(N - 72, N),
+                                       np.random.default_rng(3).choice(N, 56, replace=False)]))
+    Bs = Bt[torch.from_numpy(sample).cuda()].cpu().numpy().view(np.uint16).T.copy()
+    ref, bound = oracle.spmm(m, k, sample.size, rows.astype(np.int32), cols.astype(np.int32),
+                             vals, Bs, "bf16")
+    got = Ct[torch.from_numpy(sample).cuda()].cpu().numpy().astype(np.float64).T
+    ok, worst, at = oracle.within_tolerance(got, ref, bound, TOL, out_dtype="fp32")
+    _say("   worst |dC|/Bound = %.3g at %s" % (worst, at))
+    assert ok, (at, worst)
+    del Bt, Ct, A
+    torch.cuda.empty_cache()
+
+
 # The widest N the kernels take: ldb < 2^23 elements (B row numbers and the
 # leading dimension share 24-bit multiplies), N = 2^23 - 8.
 N_AT_LIMIT = (1 << 23) - 8
