@@ -196,8 +196,9 @@ spmm_status_t spmm_csr_permute(int64_t n, const int32_t *h_row_ptr, const int32_
  * problem (see each kernel) is UNSUPPORTED. */
 typedef struct {
     int32_t kernel;          /* -1 auto; 0 generic tile kernel (any format and shape);
-                                1 BCSR 64x64 with LDS-shared A (b_row = b_col = 64; N >= 256,
-                                  or any N with waves_n = 1);
+                                1 BCSR 64x64 with LDS-shared A (b_row = b_col = 64; below
+                                  N = 256 one wave per work-group, the plan's own choice
+                                  from N = 128 with 16-bit row-major operands);
                                 2 BCSR 64x64 A-stationary sweep (b_row = b_col = 64,
                                   N >= 4096, at most 8 blocks in every block row);
                                 3 BCSR 64x64 with each block row's A in the registers of

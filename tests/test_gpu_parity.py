@@ -1128,21 +1128,34 @@ def test_bcsr64_lds_kernel_one_wave_narrow_n(ws, case):
     check(p, run_gpu(ws, p, A=A))
 
 
-def test_bcsr64_lds_kernel_one_wave_refused_unpinned(ws):
-    """Below N = 256 kernel 1 runs only when one wave is asked for."""
+def test_bcsr64_lds_kernel_one_wave_below_256(ws):
+    """Below N = 256 kernel 1 runs one wave per work-group: the plan's own
+    choice for 64x64 blocks from N = 128 (the generic kernel below), the form a
+    pinned kernel 1 takes without waves_n, and more waves are refused."""
     p = synth.block_problem(200, 300, 128, 64, 64, 0.3, seed=3, ab_dtype="bf16", c_dtype="fp32")
+    for opts in (None, {"kernel": 1}):
+        A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                            p.ab_dtype, p.c_dtype, options=opts)
+        info = A.plan.info()
+        assert info["kernel"] == 1 and info["waves_n"] == 1 and info["tile_cols"] == 128, info
+        check(p, run_gpu(ws, p, A=A))
     with pytest.raises(ws.SpmmError) as e:
         ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
-                        p.ab_dtype, p.c_dtype, options={"kernel": 1})
+                        p.ab_dtype, p.c_dtype, options={"kernel": 1, "waves_n": 2})
     assert e.value.code == ws.ERR_UNSUPPORTED
+    q = synth.block_problem(200, 300, 72, 64, 64, 0.3, seed=4, ab_dtype="bf16", c_dtype="fp32")
+    A = ws.DeviceSparse(q.fmt, q.m, q.k, q.N, q.row_ptr, q.col_idx, q.vals, q.b_row, q.b_col,
+                        q.ab_dtype, q.c_dtype)
+    assert A.plan.info()["kernel"] == 0
 
 
-def test_config5_lds_kernel_one_wave_sampled(ws):
-    """Config 5 (the block-sparse P*V workload, N = 128) on the one-wave LDS-A
-    kernel, sampled rows."""
+def test_config5_generic_kernel_sampled(ws):
+    """Config 5 (the block-sparse P*V workload, N = 128, whose automatic plan is
+    the one-wave LDS-A kernel) on the generic tile kernel, sampled rows."""
     p = synth.config5()
     A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
-                        p.ab_dtype, p.c_dtype, options={"kernel": 1, "waves_n": 1})
+                        p.ab_dtype, p.c_dtype, options={"kernel": 0})
+    assert A.plan.info()["kernel"] == 0
     got = run_gpu(ws, p, A=A)
     check(p, got, rows=_block_rows_sample(p, 5))
 

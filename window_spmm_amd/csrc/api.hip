@@ -815,8 +815,14 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
     // it needs every block row to fit twice per CU.
     const int64_t tiles512 = ceil_div(N, 512);
     // kernel 1: 128-column tiles per wave, 2 or 4 waves (N >= 256), or one wave
-    // per work-group when pinned (any N)
-    const bool lds_ok = b64 && (N >= 256 || (opt.kernel == 1 && opt.waves_n == 1));
+    // per work-group below N = 256: pinned at any N, and the plan's own choice
+    // from N = 128 (16-bit, row-major).  Measured on the P*V workload (65536^2,
+    // N = 128, interleaved rounds): 30.9-34.9 us cold and 30.0-30.4 us warm
+    // against 34.9-38.6 / 33.2-33.8 us for the generic kernel's best shape (with
+    // 9-block-wide lines 180.4 against 193.2 us cold).
+    const bool lds_narrow = opt.kernel == -1 && opt.waves_n <= 1 && N >= 128 && !opt.col_major &&
+                            ab_dtype != SPMM_FP8_E4M3;
+    const bool lds_ok = b64 && (N >= 256 || (opt.kernel == 1 && opt.waves_n <= 1) || lds_narrow);
     // kernel 2 runs 8 columns per lane (512-column tiles), or 4 with col_major
     // or when the options ask for them (256-column tiles, 16-bit inputs)
     const int sweep_v = opt.col_major || opt.cols_per_lane == 4 ? 4 : 8;
@@ -958,7 +964,7 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         pl->n_ranges = 8 * h;
         pl->range_tiles = ceil_div(pl->n_col_tiles, pl->n_ranges);
     } else if (pl->kernel == 1) {
-        if (opt.waves_n == 0 && N < 256) {
+        if (opt.waves_n > 1 && N < 256) {
             free_plan(pl);
             return fail(SPMM_ERR_UNSUPPORTED, "kernel 1 below N = 256 runs with waves_n = 1 only");
         }
@@ -971,6 +977,7 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         // stage), 8 waves from N = 8192, so that a tile is 512 columns wide.
         const double mean_blocks = (double)h_block_row_ptr[nbr] / (double)std::max<int64_t>(1, nbr);
         const int nw = opt.waves_n > 0 ? opt.waves_n
+                       : N < 256 ? 1
                        : opt.col_major ? (N >= 8192 ? 8 : 4)
                        : (N >= 8192 && mean_blocks >= 16.0) ? 8 : 4;
         pl->n_items = nbr;
@@ -980,7 +987,10 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         pl->tile_cols = 16 * pl->V * nw;
         pl->n_col_tiles = ceil_div(N, pl->tile_cols);
         pl->workspace = 0;
-        pl->order = opt.order > 0 ? 1 : 0;
+        // one-wave work-groups below N = 256 in launch order (P*V: 30.2-30.4
+        // against 37.9 us warm, 30.9-33.9 against 43.6-44.5 us cold, with
+        // contiguous ranges per XCD)
+        pl->order = opt.order >= 0 ? opt.order : N < 256 ? 1 : 0;
     } else {
         const auto start = [&](int64_t w) { return (int64_t)h_block_row_ptr[w] * b_col; };
         int shift = 0;
