@@ -216,9 +216,10 @@ typedef struct {
                                 the only choice with col_major) */
     int32_t waves_n;         /* 0 auto; kernel 0: 1, 2 or 4 waves across the tile's
                                 columns; kernel 1: 1, 2, 4 or 8 waves of 128 columns (64
-                                with col_major) (1 only when pinned: one wave per block
-                                row and tile; 8 only when pinned with kernel 1, or chosen
-                                by the plan at N >= 8192); kernel 2 with col_major: 8
+                                with col_major) (1: one wave per block row and tile, the
+                                only form below N = 256 and the plan's choice there; 8 only
+                                when pinned with kernel 1, or chosen by the plan at
+                                N >= 8192); kernel 2 with col_major: 8
                                 (pinned) for 8 waves of 64 columns, 512-column tiles,
                                 instead of 4 (256-column tiles, the default) */
     int32_t waves_k;         /* 0 auto; kernel 0: 1, 2 or 4 waves splitting the packed
@@ -228,7 +229,8 @@ typedef struct {
     int32_t row_order;       /* -1 auto; kernel 0 with distribution 1: 0 longest task
                                 first, 1 row order with a contiguous range per XCD */
     int32_t order;           /* -1 auto; kernel 1: 0 column-tile major with a contiguous
-                                range per XCD, 1 launch order */
+                                range per XCD (auto from N = 256), 1 launch order (auto
+                                below N = 256) */
     int32_t ranges_per_xcd;  /* 0 auto; kernels 2, 3 and 4: column ranges per XCD, 1 to 64 */
     int32_t col_major;       /* 0: B is k x N and C is m x N, row-major (the default);
                                 1: column-major, the layout of activations stored token by
