@@ -169,9 +169,11 @@ spmm_status_t spmm_csr_permute(int64_t n, const int32_t *h_row_ptr, const int32_
  * configuration for (format, b_row, b_col, N, dtypes), copies the small
  * metadata it needs to plan-owned device memory (block/window row pointer,
  * WCSR task and merge tables) and records the device pointers it is given.
- * Those device arrays (column indices, values) are read by every run and must
- * stay valid and unchanged until spmm_plan_destroy.  A plan is immutable, so
- * runs on different streams may overlap if each has its own workspace and C.
+ * Those device arrays (column indices, and the BCSR values) are read by every
+ * run and must stay valid and unchanged until spmm_plan_destroy.  A WCSR plan
+ * copies the values into plan-owned memory instead (see spmm_wcsr_plan), so
+ * its runs do not read d_values.  A plan is immutable, so runs on different
+ * streams may overlap if each has its own workspace and C.
  *
  * Supported: b_row in {16, 32, 64}; b_col a multiple of 8 (BCSR: a power of two
  * in [8, 256]);
@@ -284,7 +286,13 @@ spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t
  * [0, k) (the -1 pads included) reads B as zero.  split_cols: sub-task size T
  * (positive multiple of 32, at most 8192), or 0 to let the plan choose.
  * UNSUPPORTED if a window tile (b_row * width * 2 bytes) reaches 2^32 - 256.
- * Synchronisation as for spmm_bcsr_plan. */
+ * The plan copies d_values into plan-owned device memory in the order the
+ * kernel's matrix instructions consume them (each window's width rounded up to
+ * a multiple of 32 with zeros: b_row * P' * 2 bytes, P' <= P + 24 per window;
+ * every A load of a run is then one contiguous 1 KB run); the copy runs on the
+ * null stream and the plan waits for it.  Writes to d_values after the plan
+ * call reach runs only through a new plan.  OUT_OF_MEMORY if the copy cannot
+ * be allocated.  Synchronisation otherwise as for spmm_bcsr_plan. */
 spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
                              int32_t b_col, const int32_t *h_window_row_ptr,
                              const int32_t *d_window_col_idx, const void *d_values,

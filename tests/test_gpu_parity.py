@@ -112,6 +112,23 @@ def test_wcsr_small(ws, case):
     check(p, run_gpu(ws, p, split_cols=T))
 
 
+@pytest.mark.parametrize("br,bc", [(16, 8), (32, 16), (64, 8)])
+def test_wcsr_plan_keeps_its_own_copy_of_the_values(ws, br, bc):
+    """A WCSR plan copies the window values into its own fragment-order
+    buffer at plan time (widths rounded up to 32 columns with zeros): after
+    the caller's value array is overwritten with NaN codes, runs of the plan
+    still give the product of the values it was made with, split windows and
+    every tile height included."""
+    p = synth.random_problem(700, 2500, 136, 0.04, seed=br + bc, ab_dtype="fp16", c_dtype="fp32",
+                             fmt="wcsr", b_row=br, b_col=bc, empty_row_frac=0.1)
+    A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                        p.ab_dtype, p.c_dtype, split_cols=64)
+    assert A.plan.info()["n_merges"] > 0
+    A.d_vals.fill_(0x7E00)  # fp16 quiet NaN
+    torch.cuda.synchronize()
+    check(p, run_gpu(ws, p, A=A))
+
+
 # --------------------------------------------------------------------------
 # exactness, special matrices, edge cases
 # --------------------------------------------------------------------------

@@ -18,8 +18,12 @@ struct spmm_plan_s {
     int64_t m, k, N;
     int32_t b_row, b_col;
     int ab, ct;
-    const uint16_t *A;
+    const uint16_t *A;          // BCSR: the caller's blocks; WCSR: d_apack
     const int32_t *col_idx;
+    uint16_t *d_apack;          // WCSR: plan-owned copy of the values in the tile kernel's
+                                // fragment order (launch_wcsr_pack)
+    const std::vector<int32_t> *h_pstart;  // WCSR, while planning: first packed entry / b_row
+                                           // of each window in d_apack
     int32_t *d_row_ptr;         // plan-owned copy of the block / window row pointer
     int32_t *d_tasks;           // work-item descriptors, 8 ints each (TileParams::tasks)
     int32_t *d_lists;           // per-work-group ranges of d_tasks (TileParams::lists)
@@ -226,6 +230,7 @@ void free_plan(spmm_plan_s *pl)
     if (pl->d_lists) (void)hipFree(pl->d_lists);
     if (pl->d_merges) (void)hipFree(pl->d_merges);
     if (pl->d_groups) (void)hipFree(pl->d_groups);
+    if (pl->d_apack) (void)hipFree(pl->d_apack);
     delete pl;
 }
 
@@ -502,6 +507,7 @@ spmm_status_t make_tasks(spmm_plan_s *pl, int64_t n_rows, const std::function<in
             if (pl->fmt == 1) {
                 d[4] = (int32_t)start(src[0]);
                 d[5] = (int32_t)(start(src[0] + 1) - start(src[0]));
+                d[7] = pl->h_pstart ? (*pl->h_pstart)[src[0]] : 0;
             }
             d[6] = (int32_t)(item / nt);  // column tile
         }
@@ -718,6 +724,33 @@ spmm_status_t plan_groups(spmm_plan_s *pl, int64_t nbr, const int32_t *h_ptr, co
     } catch (const std::bad_alloc &) {
         return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
     }
+}
+
+// Copies a WCSR plan's values into the tile kernel's A layout (plan-owned,
+// b_row * packed entries) on the null stream and waits for the copy.
+spmm_status_t pack_values(spmm_plan_s *pl, int64_t nw, const std::vector<int32_t> &pstart, int64_t packed)
+{
+    if (packed == 0)
+        return SPMM_OK;  // no entries: the kernel loads no A
+    int32_t *d_pstart = nullptr;
+    spmm_status_t s = upload(pstart.data(), nw + 1, &d_pstart);
+    if (s != SPMM_OK)
+        return s;
+    hipError_t e = hipMalloc(&pl->d_apack, (size_t)pl->b_row * (size_t)packed * sizeof(uint16_t));
+    if (e != hipSuccess) {
+        pl->d_apack = nullptr;
+        (void)hipFree(d_pstart);
+        return e == hipErrorOutOfMemory ? fail(SPMM_ERR_OUT_OF_MEMORY, "hipMalloc of the packed values")
+                                        : hip_fail(e, "hipMalloc of the packed values");
+    }
+    e = launch_wcsr_pack(pl->A, pl->d_row_ptr, d_pstart, nw, pl->b_row, pl->d_apack, nullptr);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(nullptr);
+    (void)hipFree(d_pstart);
+    if (e != hipSuccess)
+        return hip_fail(e, "packing the values");
+    pl->A = pl->d_apack;
+    return SPMM_OK;
 }
 
 spmm_plan_s *new_plan(int fmt, int64_t m, int64_t k, int64_t N, int32_t b_row, int32_t b_col,
@@ -1065,11 +1098,33 @@ extern "C" spmm_status_t spmm_wcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "a window tile (b_row * width * 2 bytes) must be below 4 GiB");
     }
+    // The values in the tile kernel's A layout: window w at entry b_row *
+    // pstart[w], its width rounded up to whole 32-column steps.
+    std::vector<int32_t> pstart;
+    try {
+        pstart.resize((size_t)nw + 1);
+    } catch (const std::bad_alloc &) {
+        free_plan(pl);
+        return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+    int64_t packed = 0;
+    for (int64_t w = 0; w < nw; ++w) {
+        pstart[w] = (int32_t)packed;
+        packed += ceil_div((int64_t)h_window_row_ptr[w + 1] - h_window_row_ptr[w], 32) * 32;
+        if (packed > 0x7fffffff) {
+            free_plan(pl);
+            return fail(SPMM_ERR_UNSUPPORTED, "more than 2^31 - 1 packed columns after rounding windows to 32");
+        }
+    }
+    pstart[nw] = (int32_t)packed;
+    pl->h_pstart = &pstart;
     if ((s = upload(h_window_row_ptr, nw + 1, &pl->d_row_ptr)) != SPMM_OK ||
-        (s = plan_tasks(pl, nw, start, split_cols, 32, 0, n_cu, lds_cu, l2, h_window_row_ptr)) != SPMM_OK) {
+        (s = plan_tasks(pl, nw, start, split_cols, 32, 0, n_cu, lds_cu, l2, h_window_row_ptr)) != SPMM_OK ||
+        (s = pack_values(pl, nw, pstart, packed)) != SPMM_OK) {
         free_plan(pl);
         return s;
     }
+    pl->h_pstart = nullptr;
     if (pl->n_items * (pl->kernel >= 2 ? pl->n_ranges : pl->n_col_tiles) > 0x7fffffff) {
         free_plan(pl);
         return fail(SPMM_ERR_UNSUPPORTED, "too many work-groups");

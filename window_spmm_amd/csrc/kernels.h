@@ -63,6 +63,14 @@ hipError_t launch_tiles(int fmt, int R, int V, int ab_dtype, const TileParams &p
 // `threads` threads and `lds_bytes` of dynamic LDS (0 if the query fails).
 int tiles_blocks_per_cu(int fmt, int R, int V, int ab_dtype, int threads, size_t lds_bytes);
 hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stream);
+// WCSR values -> the generic kernel's A layout.  Window w (packed columns
+// [wptr[w], wptr[w+1]) of R-row tiles, each tile row-major R x W_w) becomes
+// ceil(W_w / 32) steps of R x 32 entries at entry R * pstart[w], each step
+// R / 16 fragments of 1 KB in MFMA operand order: the 16 bytes of lane
+// l = 16g + i of fragment mt hold row 16mt + i, columns 32s + 8g .. +7 (zeros
+// past W_w).  One work-group per window.
+hipError_t launch_wcsr_pack(const uint16_t *values, const int32_t *wptr, const int32_t *pstart,
+                            int64_t n_windows, int R, uint16_t *out, hipStream_t stream);
 // BCSR with 64x64 blocks, waves_n (2 or 4) waves x 128 columns per work-group, A
 // shared through LDS (requires waves_k = 1, V = 8, tile_cols = 128 * waves_n);
 // p.col_major selects column-major B and C.

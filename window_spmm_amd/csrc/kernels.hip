@@ -260,7 +260,8 @@ __device__ __forceinline__ void buf_store_row(__amdgpu_buffer_rsrc_t r, uint32_t
 // Wave-uniform state of one task of the tile kernel (raw fields; buffer
 // resources are rebuilt where they are used).
 struct TaskCtx {
-    const uint16_t *a;   // A values of the task's row tile (BCSR: its first block)
+    const uint16_t *a;   // A values of the task's row tile (BCSR: its first block;
+                         // WCSR: its window in the plan's fragment-order copy)
     uint32_t klen;       // packed columns (0: nothing to load)
     uint32_t begin;      // first packed column (counted from the start of the format)
     uint32_t width;      // WCSR window width (A row pitch); BCSR: b_col
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void spmm_tile_kernel(TileParams p)
             c.a_col0 = 0;
         } else {
             const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)dv, 4);
-            c.a = p.A + (int64_t)R * base;
+            c.a = p.A + (int64_t)R * (uint32_t)__builtin_amdgcn_readlane((int)dv, 7);
             c.width = (uint32_t)__builtin_amdgcn_readlane((int)dv, 5);
             c.a_col0 = c.begin - base;
         }
@@ -410,19 +411,27 @@ __global__ __launch_bounds__(256, 2) void spmm_tile_kernel(TileParams p)
         const uint64_t b_skip = (uint64_t)col0 * 2;
         const __amdgpu_buffer_rsrc_t rB =
             make_rsrc(p.B + col0, (uint32_t)(p.b_bytes > b_skip ? p.b_bytes - b_skip : 0));
-        const uint32_t a_row_stride = c.width * 2u;
+        // BCSR: row-major b_row x b_col blocks.  WCSR: the plan's copy, one
+        // 1 KB fragment per (32-column step, 16 rows): lane l reads bytes
+        // 16l .. 16l+15 of fragment mt of step (a_col0 + kl) / 32 (tasks start
+        // on step boundaries), so every A load is one contiguous 1 KB run
+        // (measured on the 16384^2 WCSR workload against 16 half lines per load
+        // in the row-major window tile: 39.1-39.3 against 41.8-42.0 us warm)
+        const uint32_t a_row_stride = FMT == 0 ? (uint32_t)p.b_col * 2u : 0u;
         const __amdgpu_buffer_rsrc_t rA =
-            make_rsrc(c.a, FMT == 0 ? n_idx_of(c) * (uint32_t)(R * p.b_col * 2) : (uint32_t)R * a_row_stride);
+            make_rsrc(c.a, FMT == 0 ? n_idx_of(c) * (uint32_t)(R * p.b_col * 2)
+                                    : (uint32_t)R * ((c.width + 31u) & ~31u) * 2u);
         // A fragments first, then the B rows: the MFMAs of a stage wait for its
         // last B row, which also covers its A
         const uint32_t q = kl >> p.log2_b_col;            // BCSR: block of the task
         const uint32_t kk = kl & (uint32_t)(p.b_col - 1);  // BCSR: column in the block
         const uint32_t a_off = FMT == 0 ? ((q * R + li) * (uint32_t)p.b_col + kk) * 2u
-                                        : li * a_row_stride + (c.a_col0 + kl) * 2u;
+                                        : ((c.a_col0 + kl) >> 5) * (uint32_t)(R * 64) + (uint32_t)lane * 16u;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             uint32_t w[4];
-            buf_load<4>(rA, ok ? a_off + (uint32_t)(mt * 16) * a_row_stride : kOOB, w);
+            const uint32_t mt_off = FMT == 0 ? (uint32_t)(mt * 16) * a_row_stride : (uint32_t)mt * 1024u;
+            buf_load<4>(rA, ok ? a_off + mt_off : kOOB, w);
             st.a[mt] = u32x4_t{w[0], w[1], w[2], w[3]};
         }
         if constexpr (FMT == 0) {
@@ -1132,6 +1141,42 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bcsr64_sweep_kernel(
         }
         store_tile(t);
     }
+}
+
+// WCSR values into the tile kernel's A layout (see launch_wcsr_pack): one
+// work-group per window, one 16-byte chunk per thread and turn.  Windows are
+// b_col-padded, so the 8 entries of a chunk are all inside the window's width
+// or all past it (zeros).
+__global__ __launch_bounds__(256) void wcsr_pack_kernel(const uint16_t *__restrict__ values,
+                                                        const int32_t *__restrict__ wptr,
+                                                        const int32_t *__restrict__ pstart, int R,
+                                                        uint16_t *__restrict__ out)
+{
+    const int64_t w = blockIdx.x;
+    const uint32_t width = (uint32_t)(wptr[w + 1] - wptr[w]);
+    const uint32_t steps = (width + 31u) / 32u;
+    const uint32_t frags = (uint32_t)R / 16u;
+    const uint32_t chunks = steps * frags * 64u;
+    const __amdgpu_buffer_rsrc_t rV =
+        make_rsrc(values + (int64_t)R * wptr[w], (uint32_t)R * width * 2u);
+    uint16_t *const dst = out + (int64_t)R * pstart[w];
+    for (uint32_t c = threadIdx.x; c < chunks; c += blockDim.x) {
+        const uint32_t l = c & 63u, mt = (c >> 6) % frags, s = (c >> 6) / frags;
+        const uint32_t row = 16u * mt + (l & 15u), col = 32u * s + 8u * (l >> 4);
+        uint32_t v[4];
+        buf_load<4>(rV, col < width ? (row * width + col) * 2u : kOOB, v);
+        *reinterpret_cast<u32x4_t *>(dst + (int64_t)c * 8) = u32x4_t{v[0], v[1], v[2], v[3]};
+    }
+}
+
+hipError_t launch_wcsr_pack(const uint16_t *values, const int32_t *wptr, const int32_t *pstart,
+                            int64_t n_windows, int R, uint16_t *out, hipStream_t stream)
+{
+    if (n_windows <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(wcsr_pack_kernel, dim3((unsigned)n_windows), dim3(256), 0, stream, values, wptr,
+                       pstart, R, out);
+    return hipGetLastError();
 }
 
 // Merge pass: one work-group per (merge record, 32 chunks of 8 tile columns).
