@@ -169,11 +169,14 @@ spmm_status_t spmm_csr_permute(int64_t n, const int32_t *h_row_ptr, const int32_
  * configuration for (format, b_row, b_col, N, dtypes), copies the small
  * metadata it needs to plan-owned device memory (block/window row pointer,
  * WCSR task and merge tables) and records the device pointers it is given.
- * Those device arrays (column indices, and the BCSR values) are read by every
- * run and must stay valid and unchanged until spmm_plan_destroy.  A WCSR plan
- * copies the values into plan-owned memory instead (see spmm_wcsr_plan), so
- * its runs do not read d_values.  A plan is immutable, so runs on different
- * streams may overlap if each has its own workspace and C.
+ * Those device arrays (column indices, and the values) are read by every run
+ * and must stay valid and unchanged until spmm_plan_destroy, except where the
+ * plan copies the values into plan-owned memory (every WCSR plan, and a BCSR
+ * plan on kernel 1 with one wave per work-group and row-major operands; see
+ * spmm_wcsr_plan and spmm_bcsr_plan): its runs then read that copy, and later
+ * writes to the values reach runs only through a new plan.  A plan is
+ * immutable, so runs on different streams may overlap if each has its own
+ * workspace and C.
  *
  * Supported: b_row in {16, 32, 64}; b_col a multiple of 8 (BCSR: a power of two
  * in [8, 256]);
@@ -258,6 +261,11 @@ void spmm_plan_options_default(spmm_plan_options_t *opt);
  * may be split into sub-tasks exactly like WCSR windows (same rule, counted in
  * packed columns = blocks * b_col) and merged in a fixed order; the plan then
  * needs a workspace.  UNSUPPORTED if nnz_blocks * b_col >= 2^31.
+ * On kernel 1 with one wave per work-group and row-major B and C (the plan's
+ * choice for b_row = b_col = 64 and 128 <= N < 256) the plan copies d_blocks
+ * into plan-owned device memory (8 KB per block) in the order the kernel's
+ * matrix instructions consume them (every A load of a run one contiguous 1 KB
+ * run); the copy runs on the null stream and the plan waits for it.
  * Synchronisation: a plan call is blocking.  It allocates and fills its device
  * tables with synchronous copies, and it reads a few device index entries back
  * to the host (synchronous device-to-host copies on the null stream, which
@@ -319,7 +327,9 @@ spmm_status_t spmm_wcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t
  * times the four fastest three more times each, interleaved with the automatic
  * plan, and returns the one with the lowest median if it is at least 2 % faster
  * than the automatic plan's median (else the automatic plan; the sub-task sizes
- * are a second such stage after the first).  Candidates no kernel can run are
+ * are a second such stage after the first).  Candidates no kernel can run,
+ * and candidates whose plan or workspace cannot be allocated beside the plans
+ * held (at most six at a time, each with its tables and any value copy), are
  * skipped.  Arguments as for
  * spmm_*_plan_ex, plus the operands of the runs to time: d_B, ldb, d_C, ldc as
  * for spmm_*_run (the same requirements, checked before anything is launched).

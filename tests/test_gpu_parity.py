@@ -1166,6 +1166,23 @@ def test_bcsr64_lds_kernel_one_wave_below_256(ws):
     assert A.plan.info()["kernel"] == 0
 
 
+def test_bcsr64_one_wave_plan_keeps_its_own_copy_of_the_blocks(ws):
+    """The one-wave row-major form of kernel 1 reads the plan's fragment-order
+    copy of the blocks: after the caller's block array is overwritten with NaN
+    codes, runs still give the product of the blocks the plan was made with
+    (the automatic plan at N = 128 and kernel 1 pinned to one wave at a wide N
+    with a partial last column tile)."""
+    for N, opts in ((128, None), (1288, {"kernel": 1, "waves_n": 1})):
+        p = synth.block_problem(333, 1000, N, 64, 64, 0.3, seed=N, ab_dtype="bf16", c_dtype="fp32")
+        A = ws.DeviceSparse(p.fmt, p.m, p.k, p.N, p.row_ptr, p.col_idx, p.vals, p.b_row, p.b_col,
+                            p.ab_dtype, p.c_dtype, options=opts)
+        info = A.plan.info()
+        assert info["kernel"] == 1 and info["waves_n"] == 1, info
+        A.d_vals.fill_(0x7FC0)  # bf16 quiet NaN
+        torch.cuda.synchronize()
+        check(p, run_gpu(ws, p, A=A))
+
+
 def test_config5_generic_kernel_sampled(ws):
     """Config 5 (the block-sparse P*V workload, N = 128, whose automatic plan is
     the one-wave LDS-A kernel) on the generic tile kernel, sampled rows."""

@@ -20,8 +20,9 @@ struct spmm_plan_s {
     int ab, ct;
     const uint16_t *A;          // BCSR: the caller's blocks; WCSR: d_apack
     const int32_t *col_idx;
-    uint16_t *d_apack;          // WCSR: plan-owned copy of the values in the tile kernel's
-                                // fragment order (launch_wcsr_pack)
+    uint16_t *d_apack;          // plan-owned copy of the values in fragment order: WCSR
+                                // (launch_wcsr_pack), BCSR on the one-wave row-major
+                                // LDS-A kernel (launch_bcsr64_pack)
     const std::vector<int32_t> *h_pstart;  // WCSR, while planning: first packed entry / b_row
                                            // of each window in d_apack
     int32_t *d_row_ptr;         // plan-owned copy of the block / window row pointer
@@ -753,6 +754,30 @@ spmm_status_t pack_values(spmm_plan_s *pl, int64_t nw, const std::vector<int32_t
     return SPMM_OK;
 }
 
+// Copies a BCSR plan's 64x64 blocks into the fragment order of the one-wave
+// LDS-A kernel (plan-owned, 8 KB per block) on the null stream and waits.
+spmm_status_t pack_blocks(spmm_plan_s *pl, int64_t nnzb)
+{
+    if (nnzb == 0)
+        return SPMM_OK;
+    if (test_fail_alloc())
+        return fail(SPMM_ERR_OUT_OF_MEMORY, "device allocation of the packed blocks refused "
+                    "(SPMM_TEST_FAIL_ALLOC)");
+    hipError_t e = hipMalloc(&pl->d_apack, (size_t)nnzb * 4096 * sizeof(uint16_t));
+    if (e != hipSuccess) {
+        pl->d_apack = nullptr;
+        return e == hipErrorOutOfMemory ? fail(SPMM_ERR_OUT_OF_MEMORY, "hipMalloc of the packed blocks")
+                                        : hip_fail(e, "hipMalloc of the packed blocks");
+    }
+    e = launch_bcsr64_pack(pl->A, nnzb, pl->d_apack, nullptr);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(nullptr);
+    if (e != hipSuccess)
+        return hip_fail(e, "packing the blocks");
+    pl->A = pl->d_apack;
+    return SPMM_OK;
+}
+
 spmm_plan_s *new_plan(int fmt, int64_t m, int64_t k, int64_t N, int32_t b_row, int32_t b_col,
                       spmm_dtype_t ab, spmm_dtype_t ct, const void *d_vals, const int32_t *d_idx,
                       int dev)
@@ -1024,6 +1049,10 @@ extern "C" spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t
         // against 37.9 us warm, 30.9-33.9 against 43.6-44.5 us cold, with
         // contiguous ranges per XCD)
         pl->order = opt.order >= 0 ? opt.order : N < 256 ? 1 : 0;
+        if (nw == 1 && !opt.col_major && (s = pack_blocks(pl, h_block_row_ptr[nbr])) != SPMM_OK) {
+            free_plan(pl);
+            return s;
+        }
     } else {
         const auto start = [&](int64_t w) { return (int64_t)h_block_row_ptr[w] * b_col; };
         int shift = 0;
@@ -1310,7 +1339,8 @@ struct Timed {
 // times, interleaved with the incumbent, and the one with the lowest median
 // replaces the incumbent if it is kTuneMargin faster.  Candidates no kernel
 // can run (UNSUPPORTED or INVALID_ARGUMENT from the plan) and candidates whose
-// workspace cannot be allocated are skipped; other errors end the stage.
+// plan or workspace cannot be allocated are skipped; other errors end the
+// stage.
 spmm_status_t select_plan(const PlanMaker &make,
                           const std::vector<std::pair<spmm_plan_options_t, int64_t>> &cands,
                           const void *B, int64_t ldb, void *C, int64_t ldc, TuneState &ts,
@@ -1325,7 +1355,9 @@ spmm_status_t select_plan(const PlanMaker &make,
     for (const auto &cand : cands) {
         spmm_plan_t c = nullptr;
         spmm_status_t r = make(cand.first, cand.second, &c);
-        if (r == SPMM_ERR_UNSUPPORTED || r == SPMM_ERR_INVALID_ARGUMENT)
+        // (OUT_OF_MEMORY: its tables or value copy do not fit beside the
+        // plans already held -- not a candidate either)
+        if (r == SPMM_ERR_UNSUPPORTED || r == SPMM_ERR_INVALID_ARGUMENT || r == SPMM_ERR_OUT_OF_MEMORY)
             continue;
         if (r != SPMM_OK) {
             release();

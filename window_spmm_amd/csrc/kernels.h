@@ -71,6 +71,11 @@ hipError_t launch_merge(const MergeParams &p, int64_t n_merges, hipStream_t stre
 // past W_w).  One work-group per window.
 hipError_t launch_wcsr_pack(const uint16_t *values, const int32_t *wptr, const int32_t *pstart,
                             int64_t n_windows, int R, uint16_t *out, hipStream_t stream);
+// BCSR 64x64 blocks -> the fragment order of the one-wave row-major form of
+// bcsr64_lds_kernel: block q's 16-byte chunk c = (4h + mt) * 64 + 16g + i
+// (row 16mt + i, columns 32h + 8g .. +7) at byte q * 8192 + 16c.  One
+// work-group per block.
+hipError_t launch_bcsr64_pack(const uint16_t *blocks, int64_t n_blocks, uint16_t *out, hipStream_t stream);
 // BCSR with 64x64 blocks, waves_n (2 or 4) waves x 128 columns per work-group, A
 // shared through LDS (requires waves_k = 1, V = 8, tile_cols = 128 * waves_n);
 // p.col_major selects column-major B and C.

@@ -661,6 +661,7 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
     // 16 rows x 16 bytes took 3.2 conflict cycles per LDS instruction)
     constexpr int ABUF = R * BC * 2;               // bytes of one A buffer
     constexpr int CPT = R * BC / 8 / NT;           // 16-byte chunks per thread per block
+    constexpr bool A_FRAG = NW == 1 && !CM;        // A from the plan's fragment-order copy
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * ABUF];
     __shared__ __attribute__((aligned(16))) uint8_t lds_scr[CM ? NW * kSweepCmScratch : 16];
 
@@ -693,12 +694,15 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
         for (int c = 0; c < V; ++c)
             acc[mt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // cooperative A-block copy: chunk c of a block = row c/8, 8 columns (c%8)*8
+    // cooperative A-block copy in fragment order: chunk c = (h * MT + mt) * 64 + l,
+    // lane l = 16g + i: row 16mt + i, k = 32h + 8g .. +7.  The one-wave
+    // row-major form reads the plan's copy, already in that order (each load
+    // one contiguous 1 KB run; measured on the 65536^2 P*V workload: 29.5-29.8
+    // against 30.3-30.6 us warm); the others read the caller's row-major blocks
+    // (16 rows of 64 bytes per load; on down_proj the copy gained nothing).
     auto load_a = [&](int q, u32x4_t (&r)[CPT]) {
 #pragma unroll
         for (int t = 0; t < CPT; ++t) {
-            // chunk c in fragment order: (h, mt) = ((c / 64) / MT, (c / 64) % MT),
-            // lane l = c % 64 = 16g + i: row 16mt + i, k = 32h + 8g .. +7
             const int c = threadIdx.x + t * NT;
             const int l = c & 63, hm = c >> 6;
             const int row = 16 * (hm % MT) + (l & 15), cc = 4 * (hm / MT) + (l >> 4);
@@ -706,8 +710,9 @@ __global__ __launch_bounds__(NW * 64) void bcsr64_lds_kernel(TileParams p,
             // enough to stay in the memory-side cache; non-temporal loads, which
             // do not keep it there, made down_proj 8 % slower (1605 against
             // 1472-1481 us)
-            r[t] = __builtin_amdgcn_raw_buffer_load_b128(
-                rA, (int)(((uint32_t)q * R * BC + (uint32_t)row * BC + (uint32_t)cc * 8) * 2), 0, 0);
+            const uint32_t off = A_FRAG ? (uint32_t)q * R * BC * 2 + (uint32_t)c * 16
+                                        : ((uint32_t)q * R * BC + (uint32_t)row * BC + (uint32_t)cc * 8) * 2;
+            r[t] = __builtin_amdgcn_raw_buffer_load_b128(rA, (int)off, 0, 0);
         }
     };
     auto store_a = [&](int buf, const u32x4_t (&r)[CPT]) {
@@ -1167,6 +1172,32 @@ __global__ __launch_bounds__(256) void wcsr_pack_kernel(const uint16_t *__restri
         buf_load<4>(rV, col < width ? (row * width + col) * 2u : kOOB, v);
         *reinterpret_cast<u32x4_t *>(dst + (int64_t)c * 8) = u32x4_t{v[0], v[1], v[2], v[3]};
     }
+}
+
+// BCSR 64x64 blocks into the fragment order (see launch_bcsr64_pack): one
+// work-group per block, two 16-byte chunks per thread.
+__global__ __launch_bounds__(256) void bcsr64_pack_kernel(const uint16_t *__restrict__ blocks,
+                                                          uint16_t *__restrict__ out)
+{
+    const int64_t q = blockIdx.x;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(blocks + q * 4096, 8192u);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const uint32_t c = threadIdx.x + 256u * t;
+        const uint32_t l = c & 63u, hm = c >> 6;
+        const uint32_t row = 16u * (hm % 4u) + (l & 15u), cc = 4u * (hm / 4u) + (l >> 4);
+        uint32_t v[4];
+        buf_load<4>(rA, (row * 64u + cc * 8u) * 2u, v);
+        *reinterpret_cast<u32x4_t *>(out + q * 4096 + (int64_t)c * 8) = u32x4_t{v[0], v[1], v[2], v[3]};
+    }
+}
+
+hipError_t launch_bcsr64_pack(const uint16_t *blocks, int64_t n_blocks, uint16_t *out, hipStream_t stream)
+{
+    if (n_blocks <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(bcsr64_pack_kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream, blocks, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_wcsr_pack(const uint16_t *values, const int32_t *wptr, const int32_t *pstart,
