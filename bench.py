@@ -740,6 +740,7 @@ def main():
 
     key = "config%d" % args.config + ("_" + args.which if args.config == 4 else "") + \
           ("_m%d_n%d" % (args.member, args.n3) if args.config == 3 else "") + \
+          ("_w%d" % args.width if args.config == 5 and args.width != 1 else "") + \
           ("_colmajor" if args.col_major else "") + ("_fp8" if args.fp8 else "")
     if opts or args.tuned or args.n4 != 65536:
         key = None   # the traffic records hold the default plans of the named workloads
