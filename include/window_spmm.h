@@ -265,7 +265,8 @@ void spmm_plan_options_default(spmm_plan_options_t *opt);
  * choice for b_row = b_col = 64 and 128 <= N < 256) the plan copies d_blocks
  * into plan-owned device memory (8 KB per block) in the order the kernel's
  * matrix instructions consume them (every A load of a run one contiguous 1 KB
- * run); the copy runs on the null stream and the plan waits for it.
+ * run); the copy runs on the null stream and the plan waits for it (d_blocks
+ * must be complete when the plan is called).
  * Synchronisation: a plan call is blocking.  It allocates and fills its device
  * tables with synchronous copies, and it reads a few device index entries back
  * to the host (synchronous device-to-host copies on the null stream, which
@@ -298,7 +299,8 @@ spmm_status_t spmm_bcsr_plan_ex(spmm_plan_t *plan, int64_t m, int64_t k, int64_t
  * kernel's matrix instructions consume them (each window's width rounded up to
  * a multiple of 32 with zeros: b_row * P' * 2 bytes, P' <= P + 24 per window;
  * every A load of a run is then one contiguous 1 KB run); the copy runs on the
- * null stream and the plan waits for it.  Writes to d_values after the plan
+ * null stream and the plan waits for it, so d_values must be complete when the
+ * plan is called (writes on a non-blocking stream synchronised first).  Writes to d_values after the plan
  * call reach runs only through a new plan.  OUT_OF_MEMORY if the copy cannot
  * be allocated.  Synchronisation otherwise as for spmm_bcsr_plan. */
 spmm_status_t spmm_wcsr_plan(spmm_plan_t *plan, int64_t m, int64_t k, int64_t N, int32_t b_row,
